@@ -1,0 +1,287 @@
+"""Float64 CPU oracle for the score -> select -> compact -> decode path.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  It shares no code with the HIP
+library or its Python binding and imports nothing from them; the product path
+never calls it.
+
+Every function is the plain definition written out in numpy float64, one
+(sequence, KV head) at a time, with library primitives (a matmul, exp, a
+stable sort, a cumulative sum) as its steps and no blocking or fusion.
+
+What the pages fix and what this module reads into them
+-------------------------------------------------------
+* "A Simple Plug-in for Improving Eviction-Based KV Cache Compression"
+  (VECTOR), section "Enonce du Probleme": importance-based eviction (SnapKV,
+  KeyDiff) scores the cached tokens and permanently drops the low scorers.
+  The pages name SnapKV's query-aware attention score but never write it out;
+  the score taken here is the observation-window attention score: the last W
+  queries of each query head attend (softmax over every cached key of the
+  sequence) and each token's probabilities are summed over the W window rows
+  and over the query heads of its KV head's GQA group.
+* "KVSculpt: KV Cache Compression as Distillation", section 2.B: the
+  log-sum-exp ell of the attention logits is the per-row normaliser this
+  score divides by; ``window_scores`` also returns it.
+* "KVzap: Fast, Adaptive, and Faithful KV Cache Pruning", section 2.3
+  ("Seuillage"): tokens whose score falls below a fixed threshold tau are
+  dropped, so the kept fraction adapts to the input; here a score equal to
+  tau is kept.
+* "KV Cache Transform Coding for Compact Storage in LLM Inference", section
+  3, and the KVzap page, section 1: the edited cache keeps the plain K/V
+  layout that a standard attention kernel reads, so the compacted cache is a
+  dense packed subset of rows in original order, and decode is ordinary
+  softmax attention over it.
+
+Readings where the pages are silent (each also listed in the design notes):
+softmax scale 1/sqrt(d) applied after the dot product; scores summed (not
+averaged) over the GQA group, so they total W*G per KV head; query head j
+belongs to KV head j // G; window row w of a sequence of length n sits at
+position n - W + w, and ``causal=True`` hides tokens after it (default off:
+every window row sees every key); ties in score go to the lower token index
+and -0.0 equals +0.0; ratio budgets keep clamp(floor(r*n + 1/2), 1, n)
+tokens with r widened from fp32; the mass budget keeps the fewest top tokens
+whose summed score reaches f times the head's total; decode is one fresh
+query per query head over the compacted rows only.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+BUDGET_K = 0
+BUDGET_RATIO = 1
+BUDGET_THRESHOLD = 2
+BUDGET_MASS = 3
+
+
+def _f64(x) -> np.ndarray:
+    """Widen a numpy array or CPU torch tensor (fp32/bf16) exactly to float64."""
+    if hasattr(x, "detach"):
+        t = x.detach().cpu()
+        if t.is_floating_point():
+            t = t.double()
+        return t.numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _ints(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    return np.asarray(x, dtype=np.int64)
+
+
+def _ctx(ctx_len, B: int, N_max: int) -> np.ndarray:
+    if ctx_len is None:
+        return np.full(B, N_max, dtype=np.int64)
+    return _ints(ctx_len)
+
+
+def _scale(scale, d: int) -> float:
+    return 1.0 / math.sqrt(d) if scale is None or scale <= 0 else float(np.float32(scale))
+
+
+def window_scores(q_win, k, ctx_len=None, scale=None, causal=False):
+    """Observation-window scores and row log-sum-exps.
+
+    q_win [B][Hq][W][d], k [B][Hkv][N_max][d], ctx_len [B] (None: all N_max).
+    Returns ``(scores, lse)``: scores [B][Hkv][N_max] float64 with entries at
+    t >= ctx_len[b] left at 0, and lse [B][Hq][W] float64 (natural log).
+
+    For row r = (query head j, window row w) of KV head h = j // G:
+      l[r, t]  = scale * <q[r], k[t]>              (t < n; causal hides t > n-W+w)
+      lse[r]   = m + log(sum_t exp(l[r, t] - m)),  m = max_t l[r, t]
+      s[h, t]  = sum_r exp(l[r, t] - lse[r])
+    """
+    q = _f64(q_win)
+    kk = _f64(k)
+    B, Hq, W, d = q.shape
+    _, Hkv, N_max, _ = kk.shape
+    G = Hq // Hkv
+    sc = _scale(scale, d)
+    ctx = _ctx(ctx_len, B, N_max)
+    scores = np.zeros((B, Hkv, N_max), dtype=np.float64)
+    lse = np.zeros((B, Hq, W), dtype=np.float64)
+    for b in range(B):
+        n = int(ctx[b])
+        for h in range(Hkv):
+            rows = q[b, h * G:(h + 1) * G].reshape(G * W, d)
+            logits = sc * (rows @ kk[b, h, :n].T)               # [G*W, n]
+            if causal:
+                w_of_row = np.tile(np.arange(W), G)
+                last = n - W + w_of_row                           # last visible token per row
+                hidden = np.arange(n)[None, :] > last[:, None]
+                logits[hidden] = -np.inf
+            m = logits.max(axis=1, keepdims=True)
+            row_lse = m + np.log(np.exp(logits - m).sum(axis=1, keepdims=True))
+            p = np.exp(logits - row_lse)
+            scores[b, h, :n] = p.sum(axis=0)
+            lse[b, h * G:(h + 1) * G] = row_lse.reshape(G, W)
+    return scores, lse
+
+
+def total_order(s: np.ndarray) -> np.ndarray:
+    """Token indices of one head from first to last: higher score first,
+    equal scores by lower index (-0.0 and +0.0 compare equal)."""
+    s = np.asarray(s, dtype=np.float64)
+    return np.lexsort((np.arange(s.shape[0]), -s))
+
+
+def _round_half_up(x: float) -> int:
+    return int(math.floor(x + 0.5))
+
+
+def _clamp_bounds(n: int, min_ratio: float, max_ratio: float):
+    lo = max(1, _round_half_up(float(np.float32(min_ratio)) * n))
+    hi = min(n, max(1, _round_half_up(float(np.float32(max_ratio)) * n)))
+    return min(lo, hi), hi
+
+
+def budget_count(s, mode: int, *, k=None, ratio=None, tau=None, mass=None,
+                 min_ratio: float = 0.0, max_ratio: float = 1.0) -> int:
+    """Number of tokens one head keeps, from its n scores ``s``.
+
+    BUDGET_K:         clamp(k, 1, n)
+    BUDGET_RATIO:     clamp(floor(r*n + 1/2), 1, n), r the fp32 ratio widened
+    BUDGET_THRESHOLD: #{t : s_t >= tau}, tau fp32, then clamped to
+                      [max(1, round(min_ratio*n)), round(max_ratio*n)]
+    BUDGET_MASS:      fewest k >= 1 whose top-k score sum C(k) >= f*C(n)
+                      (f fp32; sums in float64 in the total order), then the
+                      same clamp as the threshold mode
+    """
+    s = np.asarray(s, dtype=np.float64)
+    n = s.shape[0]
+    if n == 0:
+        return 0
+    if mode == BUDGET_K:
+        return int(min(max(int(k), 1), n))
+    if mode == BUDGET_RATIO:
+        r = float(np.float32(ratio))
+        return int(min(max(int(math.floor(r * n + 0.5)), 1), n))
+    lo, hi = _clamp_bounds(n, min_ratio, max_ratio)
+    if mode == BUDGET_THRESHOLD:
+        t = float(np.float32(tau))
+        cnt = int(np.count_nonzero(s >= t))
+        return int(min(max(cnt, lo), hi))
+    if mode == BUDGET_MASS:
+        f = float(np.float32(mass))
+        c = np.cumsum(s[total_order(s)])
+        target = f * c[-1]
+        kk = int(np.searchsorted(c, target, side="left")) + 1
+        kk = min(kk, n)
+        return int(min(max(kk, lo), hi))
+    raise ValueError(f"unknown budget mode {mode}")
+
+
+def select(scores, ctx_len=None, mode=BUDGET_RATIO, **params):
+    """Per-head kept token indices.
+
+    scores [B][Hkv][N_max]; params as ``budget_count`` (``k``/``ratio`` may
+    also be per-head arrays of length B*Hkv).  Returns ``(kept_idx, count)``:
+    kept_idx [B][Hkv][N_max] int32 (first count entries valid, ascending, the
+    rest -1) and count [B*Hkv] int32.  The kept set of a head is the first
+    count tokens of ``total_order``.
+    """
+    s_all = _f64(scores)
+    B, Hkv, N_max = s_all.shape
+    ctx = _ctx(ctx_len, B, N_max)
+    kept = np.full((B, Hkv, N_max), -1, dtype=np.int32)
+    count = np.zeros(B * Hkv, dtype=np.int32)
+    for b in range(B):
+        n = int(ctx[b])
+        for h in range(Hkv):
+            i = b * Hkv + h
+            p = dict(params)
+            for key in ("k", "ratio"):
+                if key in p and p[key] is not None and np.ndim(p[key]) > 0:
+                    p[key] = np.asarray(p[key]).reshape(-1)[i]
+            s = s_all[b, h, :n]
+            kk = budget_count(s, mode, **p)
+            idx = np.sort(total_order(s)[:kk])
+            kept[b, h, :kk] = idx
+            count[i] = kk
+    return kept, count
+
+
+def compact(k, v, kept_idx, count):
+    """Gather the kept rows of every head into one packed cache.
+
+    Heads are laid out (sequence, KV head) row-major; offsets [B*Hkv+1] int64
+    is the exclusive prefix sum of count.  Returns numpy arrays
+    ``(k_c [total][d], v_c [total][d], pos [total] int32, offsets)`` with
+    k_c/v_c in the input's own element type, so equality is bitwise.
+    """
+    if hasattr(k, "detach"):
+        import torch  # only to keep bf16 bytes intact
+        kn = k.detach().cpu().view(torch.int16).numpy() if k.dtype == torch.bfloat16 \
+            else k.detach().cpu().numpy()
+        vn = v.detach().cpu().view(torch.int16).numpy() if v.dtype == torch.bfloat16 \
+            else v.detach().cpu().numpy()
+    else:
+        kn, vn = np.asarray(k), np.asarray(v)
+    idx = _ints(kept_idx)
+    cnt = _ints(count)
+    B, Hkv = kn.shape[0], kn.shape[1]
+    offsets = np.zeros(B * Hkv + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(cnt)
+    kc, vc, pos = [], [], []
+    for b in range(B):
+        for h in range(Hkv):
+            c = int(cnt[b * Hkv + h])
+            sel = idx[b, h, :c]
+            kc.append(kn[b, h, sel])
+            vc.append(vn[b, h, sel])
+            pos.append(sel.astype(np.int32))
+    d = kn.shape[-1]
+    k_c = np.concatenate(kc) if kc else np.zeros((0, d), kn.dtype)
+    v_c = np.concatenate(vc) if vc else np.zeros((0, d), vn.dtype)
+    return k_c, v_c, np.concatenate(pos), offsets
+
+
+def decode(q, k_c, v_c, offsets, Hkv: int, scale=None):
+    """One decode query per query head over the compacted cache.
+
+    q [B][Hq][d]; k_c, v_c [total][d] (float arrays or bf16 tensors);
+    offsets [B*Hkv+1].  For query head j of KV head h = j // G with rows
+    o..o+k-1:  u_i = scale*<q, K_c[o+i]>,  out = sum_i softmax(u)_i V_c[o+i],
+    lse = m + log(sum_i exp(u_i - m)).  Returns (out [B][Hq][d], lse [B][Hq]).
+    """
+    qq = _f64(q)
+    kc = _f64(k_c)
+    vc = _f64(v_c)
+    off = _ints(offsets)
+    B, Hq, d = qq.shape
+    G = Hq // Hkv
+    sc = _scale(scale, d)
+    out = np.zeros((B, Hq, d), dtype=np.float64)
+    lse = np.zeros((B, Hq), dtype=np.float64)
+    for b in range(B):
+        for j in range(Hq):
+            h = j // G
+            lo, hi = int(off[b * Hkv + h]), int(off[b * Hkv + h + 1])
+            u = sc * (kc[lo:hi] @ qq[b, j])
+            m = u.max()
+            e = np.exp(u - m)
+            z = e.sum()
+            out[b, j] = (e @ vc[lo:hi]) / z
+            lse[b, j] = m + math.log(z)
+    return out, lse
+
+
+def attend_full(q, k, v, ctx_len=None, scale=None):
+    """Decode over the whole (uncompressed) cache: the 100%-keep reference."""
+    kk = _f64(k)
+    vv = _f64(v)
+    B, Hkv, N_max, d = kk.shape
+    ctx = _ctx(ctx_len, B, N_max)
+    rows_k, rows_v = [], []
+    offsets = np.zeros(B * Hkv + 1, dtype=np.int64)
+    i = 0
+    for b in range(B):
+        for h in range(Hkv):
+            n = int(ctx[b])
+            rows_k.append(kk[b, h, :n])
+            rows_v.append(vv[b, h, :n])
+            offsets[i + 1] = offsets[i] + n
+            i += 1
+    return decode(q, np.concatenate(rows_k), np.concatenate(rows_v), offsets, Hkv, scale)

@@ -1,0 +1,49 @@
+"""Seeded workload generators: reproducibility and the planted-needle check."""
+import numpy as np
+import torch
+
+from kv_cache_compression_score_amd import workloads as wl
+from oracle import oracle as orc
+
+
+def test_generation_is_reproducible():
+    cfg = wl.CONFIGS["ragged_adaptive"]
+    a = wl.make_layer(cfg, B=2, N_max=4096)
+    b = wl.make_layer(cfg, B=2, N_max=4096)
+    for x, y in [(a.k, b.k), (a.v, b.v), (a.q_win, b.q_win), (a.q_dec, b.q_dec),
+                 (a.ctx_len, b.ctx_len)]:
+        assert torch.equal(x, y)
+    assert a.k.dtype == torch.bfloat16
+    for bb in range(2):
+        n = int(a.ctx_len[bb])
+        assert 2048 <= n <= 4096
+        assert torch.count_nonzero(a.k[bb, :, n:]) == 0
+
+
+def test_layers_have_independent_streams():
+    cfg = wl.CONFIGS["long128k"]
+    a = wl.make_layer(cfg, 0, N_max=256, with_v=False)
+    b = wl.make_layer(cfg, 31, N_max=256, with_v=False)
+    assert not torch.equal(a.k, b.k)
+    assert torch.equal(b.k, wl.make_layer(cfg, 31, N_max=256, with_v=False).k)
+
+
+def test_tiny_is_fp32_gaussian():
+    cfg = wl.CONFIGS["tiny"]
+    t = wl.make_layer(cfg)
+    assert t.k.dtype == torch.float32 and t.k.shape == (1, 4, 1024, 64)
+    assert abs(float(t.k.std()) - 1.0) < 0.02
+
+
+def test_needles_are_retained_by_the_oracle():
+    # The planted keys (3x the mean key norm along the window's mean query
+    # direction) must survive a 10% budget; one sequence at full 32K length.
+    cfg = wl.CONFIGS["needle32k"]
+    lay = wl.make_layer(cfg, B=1)
+    s, _ = orc.window_scores(lay.q_win, lay.k, lay.ctx_len)
+    kept, cnt = orc.select(s, lay.ctx_len, orc.BUDGET_RATIO, ratio=cfg.ratio)
+    assert np.all(cnt == 3277)
+    for h in range(cfg.Hkv):
+        keep = set(kept[0, h, :cnt[h]].tolist())
+        missing = [p for p in lay.needle_pos[0, h].tolist() if p not in keep]
+        assert not missing, f"head {h} lost needles {missing}"

@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Throughput of the score -> select -> compact -> decode path on one GPU.
+
+One step = kv_score + kv_select + kv_compact + kv_decode_attn over one batch
+of the chosen synthetic workload (default: batch 4 at 32K context, 32 query
+/ 8 KV heads, d = 128, W = 64, keep 10%, one decode step), inputs resident
+in HBM before timing starts.  Prints one JSON line:
+
+  value       cached tokens per second over the whole step
+  roofline    the kernel with the most GPU time: algorithmic FLOPs (MFMA
+              kernels) or bytes (HBM kernels) per launch / its mean duration,
+              durations from hipEvents recorded on the library's stream
+  cpu_baseline the float64 oracle on a bounded sample on the host cores
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from kv_cache_compression_score_amd import _lib, api  # noqa: E402
+from kv_cache_compression_score_amd import workloads as wl  # noqa: E402
+
+METRIC = "cached tokens/sec scored+selected+compacted at 32K ctx; decode-attn HBM GB/s"
+PEAK_HBM_GBPS = 8000.0
+PEAK_TFLOPS = {torch.bfloat16: 2500.0, torch.float32: 157.3}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="needle32k", choices=sorted(wl.CONFIGS))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seqs", type=int, default=4,
+                   help="sequences of the batch the oracle baseline processes")
+    return p.parse_args()
+
+
+class Pipeline:
+    def __init__(self, lay: wl.Layer):
+        cfg = lay.cfg
+        self.cfg = cfg
+        d = torch.device("cuda:0")
+        self.q = lay.q_win.to(d)
+        self.k = lay.k.to(d)
+        self.v = lay.v.to(d)
+        self.c = lay.ctx_len.to(d)
+        self.qd = lay.q_dec[0].to(d)
+        B, Hkv, N, D = lay.k.shape
+        if cfg.budget_mode == wl.BUDGET_MASS:
+            self.budget = api.Budget(api.BUDGET_MASS, mass=cfg.ratio, min_ratio=cfg.min_ratio,
+                                     max_ratio=cfg.max_ratio)
+            self.cap = int(math.ceil(B * Hkv * N * cfg.max_ratio))
+        else:
+            self.budget = api.Budget(api.BUDGET_RATIO, ratio_scalar=cfg.ratio)
+            self.cap = B * Hkv * max(1, int(math.floor(float(np.float32(cfg.ratio)) * N + 0.5)))
+        f32 = torch.float32
+        self.scores = torch.empty(B, Hkv, N, device=d, dtype=f32)
+        self.ws_s = torch.empty(api.kv_score_workspace_size(B, cfg.Hq, Hkv, N, cfg.W, D),
+                                device=d, dtype=torch.uint8)
+        self.idx = torch.empty(B, Hkv, N, device=d, dtype=torch.int32)
+        self.cnt = torch.empty(B * Hkv, device=d, dtype=torch.int32)
+        self.comp = (torch.empty(self.cap, D, device=d, dtype=lay.k.dtype),
+                     torch.empty(self.cap, D, device=d, dtype=lay.k.dtype),
+                     torch.empty(self.cap, device=d, dtype=torch.int32),
+                     torch.empty(B * Hkv + 1, device=d, dtype=torch.int64))
+        self.out = torch.empty(B, cfg.Hq, D, device=d, dtype=f32)
+        self.lse = torch.empty(B, cfg.Hq, device=d, dtype=f32)
+        self.ws_d = torch.empty(api.kv_decode_workspace_size(B, cfg.Hq, Hkv, D, self.cap),
+                                device=d, dtype=torch.uint8)
+
+    def step(self):
+        api.kv_score(self.q, self.k, self.c, scores=self.scores, workspace=self.ws_s)
+        api.kv_select(self.scores, self.c, self.budget, kept_idx=self.idx, kept_count=self.cnt)
+        k_c, v_c, _, off = api.kv_compact(self.k, self.v, self.idx, self.cnt, self.cap,
+                                          out=self.comp)
+        api.kv_decode_attn(self.qd, k_c, v_c, off, self.cfg.Hkv, out=self.out, lse=self.lse,
+                           workspace=self.ws_d)
+
+
+def kernel_times(pipe: Pipeline, steps: int):
+    L = _lib.lib()
+    L.kv_timing_enable(1)
+    for _ in range(steps):
+        pipe.step()
+    torch.cuda.synchronize()
+    buf = (_lib.KvKernelTime * 32)()
+    n = L.kv_timing_read(buf, 32)
+    L.kv_timing_enable(0)
+    if n < 0:
+        raise RuntimeError(f"kv_timing_read failed: {n}")
+    return {buf[i].name.decode(): (buf[i].total_ms / buf[i].launches, buf[i].launches)
+            for i in range(n)}
+
+
+def cpu_baseline(lay: wl.Layer, nseq: int):
+    """The float64 oracle, as it stands, on the first nseq sequences."""
+    from oracle import oracle as orc
+    cfg = lay.cfg
+    sl = slice(0, nseq)
+    ctx = lay.ctx_len[sl]
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    t0 = time.perf_counter()
+    s, _ = orc.window_scores(lay.q_win[sl], lay.k[sl], ctx)
+    if cfg.budget_mode == wl.BUDGET_MASS:
+        idx, cnt = orc.select(s, ctx, orc.BUDGET_MASS, mass=cfg.ratio,
+                              min_ratio=cfg.min_ratio, max_ratio=cfg.max_ratio)
+    else:
+        idx, cnt = orc.select(s, ctx, orc.BUDGET_RATIO, ratio=cfg.ratio)
+    k_c, v_c, pos, off = orc.compact(lay.k[sl], lay.v[sl], idx, cnt)
+    kc = torch.from_numpy(k_c).view(lay.k.dtype) if lay.k.dtype == torch.bfloat16 else k_c
+    vc = torch.from_numpy(v_c).view(lay.k.dtype) if lay.k.dtype == torch.bfloat16 else v_c
+    orc.decode(lay.q_dec[0][sl], kc, vc, off, cfg.Hkv)
+    dt = time.perf_counter() - t0
+    tokens = int(ctx.sum())
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"sequences 0..{nseq - 1} of the batch ({tokens} cached tokens, all "
+                      f"{cfg.Hkv} KV heads): float64 score+select+compact+decode, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this path runs on one GPU; every stage is independent "
+                          "per (sequence, KV head), so more GPUs shard heads with no exchange "
+                          "and no multi-GPU run is provided", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    cfg = wl.CONFIGS[args.workload]
+    log(f"bench: generating {cfg.name}")
+    lay = wl.make_layer(cfg)
+    pipe = Pipeline(lay)
+    log(f"bench: {torch.cuda.get_device_name(0)}; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        pipe.step()
+    torch.cuda.synchronize()
+
+    log(f"bench: timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        pipe.step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    kt = kernel_times(pipe, args.steps)
+    log("bench: per-kernel mean ms " + ", ".join(f"{k}={v[0]:.4f}" for k, v in kt.items()))
+
+    B, Hkv, N, D = lay.k.shape
+    G, W = cfg.G, cfg.W
+    esz = lay.k.element_size()
+    ctx = lay.ctx_len.numpy().astype(np.int64)
+    tokens = int(ctx.sum())
+    th = int(Hkv * ctx.sum())                       # token-heads scored
+    kept = int(pipe.cnt.sum().item())
+    flop_pass = 2.0 * G * W * D * th
+    bytes_sel = 4.0 * th + 4.0 * kept + 4.0 * B * Hkv
+    bytes_comp = kept * (4.0 * D * esz + 8.0) + 8.0 * (B * Hkv + 1)
+    bytes_dec = 2.0 * kept * D * esz + B * cfg.Hq * D * (esz + 4.0) + 4.0 * B * cfg.Hq
+    peak_f = PEAK_TFLOPS[lay.k.dtype]
+    work = {"score_rowstats": ("mfma", flop_pass), "score_colsum": ("mfma", flop_pass),
+            "select": ("hbm", bytes_sel), "compact": ("hbm", bytes_comp),
+            "decode_split": ("hbm", bytes_dec)}
+    dom = max(work, key=lambda k: kt.get(k, (0.0,))[0])
+    bound, amount = work[dom]
+    t_dom = kt[dom][0] * 1e-3
+    if bound == "mfma":
+        achieved, peak, unit = amount / t_dom / 1e12, peak_f, "TFLOP/s"
+    else:
+        achieved, peak, unit = amount / t_dom / 1e9, PEAK_HBM_GBPS, "GB/s"
+    t = {k: v[0] * 1e-3 for k, v in kt.items()}
+    t_score = t["score_rowstats"] + t["score_lse"] + t["score_colsum"]
+    t_dec = t["decode_split"] + t["decode_combine"]
+    t_scd = t["select"] + t["compact"] + t_dec
+    res = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if lay.k.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "ctx": int(N), "Hq": cfg.Hq, "Hkv": Hkv,
+                   "d": D, "W": W, "budget": "mass" if cfg.budget_mode == wl.BUDGET_MASS
+                   else f"ratio {cfg.ratio}", "kept_rows": kept},
+        "roofline": {"kernel": dom, "bound": bound, "achieved": achieved, "peak": peak,
+                     "unit": unit, "frac": achieved / peak, "traffic": None},
+        "decode_hbm_gbps": bytes_dec / t_dec / 1e9,
+        "score_stage": {"ms": t_score * 1e3,
+                        "algorithmic_tflops": flop_pass / t_score / 1e12,
+                        "algorithmic_frac": flop_pass / t_score / 1e12 / peak_f,
+                        "executed_frac": 2 * flop_pass / t_score / 1e12 / peak_f},
+        "select_compact_decode": {"ms": t_scd * 1e3,
+                                  "gbps": (bytes_sel + bytes_comp + bytes_dec) / t_scd / 1e9,
+                                  "frac": (bytes_sel + bytes_comp + bytes_dec) / t_scd / 1e9
+                                  / PEAK_HBM_GBPS},
+        "kernels_ms": {k: v[0] for k, v in kt.items()},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: oracle baseline on the host")
+        res["cpu_baseline"] = cpu_baseline(lay, min(args.cpu_seqs, B))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,222 @@
+/*
+ * kvcc.h - C ABI of the MI355X (gfx950) KV-cache scoring / selection /
+ * compaction / decode library (libkvcc.so).
+ *
+ * The four calls are the steps of importance-based eviction as the pages
+ * describe it: score every cached token, keep a budgeted subset per KV head,
+ * and leave a plain dense cache that an ordinary attention kernel reads.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every tensor pointer is DEVICE memory owned by the caller.  The library
+ *   never allocates, frees or retains a pointer beyond the call.  Scratch
+ *   memory comes only from the caller's `workspace`, sized by the matching
+ *   *_workspace_size() function (a pure host function).
+ * - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *   enqueue work on it and never synchronise; buffers must stay alive until
+ *   the stream has passed the call.
+ * - Host-side validation runs before any launch.  On failure the call returns
+ *   a non-zero kv_status and launches nothing.  A launch failure returns
+ *   KV_ERR_LAUNCH.  Faults during execution surface at the caller's next
+ *   synchronisation.
+ * - Tensor pointers must be 16-byte aligned.  Head dimension d is 64 or 128.
+ *   dtype is KV_F32 (fp32) or KV_BF16 (bfloat16) and applies to every
+ *   q / k / v / k_c / v_c tensor of the call; scores, outputs and statistics
+ *   are fp32.
+ * - Query head j belongs to KV head j / G with G = Hq / Hkv (contiguous
+ *   groups); Hq must be a multiple of Hkv.
+ * - ctx_len (device int32 [B]) gives each sequence's length n_b
+ *   (0 <= n_b <= N_max); NULL means n_b = N_max for all b.  Rows t >= n_b
+ *   are never read and never selected.
+ * - Results are deterministic bit for bit for fixed inputs and sizes.
+ */
+#ifndef KVCC_H
+#define KVCC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kv_status {
+  KV_OK = 0,
+  KV_ERR_NULL = 1,       /* a required pointer is NULL */
+  KV_ERR_ALIGN = 2,      /* a tensor pointer is not 16-byte aligned */
+  KV_ERR_SHAPE = 3,      /* a size is out of range or inconsistent */
+  KV_ERR_DTYPE = 4,      /* dtype is not KV_F32 / KV_BF16 */
+  KV_ERR_MODE = 5,       /* unknown budget mode or out-of-range budget value */
+  KV_ERR_WORKSPACE = 6,  /* workspace missing or smaller than required */
+  KV_ERR_LAUNCH = 7      /* the HIP runtime rejected a kernel launch */
+} kv_status;
+
+typedef enum kv_dtype { KV_F32 = 0, KV_BF16 = 1 } kv_dtype;
+
+typedef enum kv_budget_mode {
+  KV_BUDGET_K = 0,          /* keep k tokens per head */
+  KV_BUDGET_RATIO = 1,      /* keep a fraction r of each head's n tokens */
+  KV_BUDGET_THRESHOLD = 2,  /* keep tokens whose score is >= tau */
+  KV_BUDGET_MASS = 3        /* keep the fewest top tokens holding a fraction f of the score mass */
+} kv_budget_mode;
+
+/*
+ * Per-head budget (host struct; the arrays it points to are device memory).
+ *   mode == KV_BUDGET_K:     k_h = clamp(k ? k[head] : k_scalar, 1, n)
+ *   mode == KV_BUDGET_RATIO: k_h = clamp(floor(r*n + 1/2), 1, n) with
+ *                            r = ratio ? ratio[head] : ratio_scalar, evaluated
+ *                            in double from the fp32 value.
+ *   mode == KV_BUDGET_THRESHOLD: k_h = #{t : s_t >= tau} (fp32 compare),
+ *                            clamped to [lo, hi].
+ *   mode == KV_BUDGET_MASS:  k_h = min{k >= 1 : C(k) >= mass * C(n)}, C(k) the
+ *                            sum of the k largest scores, clamped to [lo, hi].
+ *   lo = max(1, floor(min_ratio*n + 1/2)), hi = min(n, max(1, floor(max_ratio*n + 1/2))).
+ * A head with n = 0 keeps nothing.  `head` is b*Hkv + h.
+ * Threshold pruning with a fixed tau follows "KVzap: Fast, Adaptive, and
+ * Faithful KV Cache Pruning", section 2.3; per-head budgets (any allocation
+ * across heads) follow "KVSculpt: KV Cache Compression as Distillation",
+ * section 2.D.
+ */
+typedef struct kv_budget {
+  int32_t mode;
+  const int32_t* k;        /* device [B*Hkv] or NULL */
+  const float* ratio;      /* device [B*Hkv] or NULL */
+  int32_t k_scalar;
+  float ratio_scalar;      /* 0 <= r <= 1 */
+  float tau;
+  float mass;              /* 0 <= f <= 1 */
+  float min_ratio;         /* 0 <= min_ratio <= 1 */
+  float max_ratio;         /* 0 <= max_ratio <= 1 */
+} kv_budget;
+
+/* ----------------------------------------------------------------------
+ * kv_score - observation-window attention score of every cached token.
+ *
+ * Importance-based eviction scores tokens by the attention they receive
+ * ("A Simple Plug-in for Improving Eviction-Based KV Cache Compression",
+ * section "Enonce du Probleme", which names SnapKV); the row normaliser is
+ * the log-sum-exp ell of "KVSculpt: KV Cache Compression as Distillation",
+ * section 2.B.  For KV head h of sequence b and window row r = (query head
+ * j in h's group, window position w):
+ *   l[r,t]   = scale * <q_win[b,j,w,:], k[b,h,t,:]>        for t < n_b
+ *   lse[r]   = log sum_t exp(l[r,t])
+ *   s[b,h,t] = sum_r exp(l[r,t] - lse[r])     (so sum_t s[b,h,t] = W*G)
+ * With causal != 0, window row w sits at position n_b - W + w and does not
+ * see tokens after it (requires W <= n_b; a row that sees nothing adds 0).
+ *
+ * q_win   [B][Hq][W][d] dtype, window queries (already position-encoded)
+ * k       [B][Hkv][N_max][d] dtype
+ * ctx_len [B] int32 or NULL
+ * scores  [B][Hkv][N_max] fp32 out; entries t >= n_b are not written
+ * row_lse [B][Hq][W] fp32 out (natural log) or NULL
+ * scale   softmax scale; <= 0 selects 1/sqrt(d)
+ * Limits: 1 <= W <= N_max, G*W <= 1024, B*Hkv*N_max < 2^31.
+ * ---------------------------------------------------------------------- */
+size_t kv_score_workspace_size(int B, int Hq, int Hkv, int N_max, int W, int d);
+int kv_score(const void* q_win, const void* k, const int32_t* ctx_len,
+             float* scores, float* row_lse,
+             int B, int Hq, int Hkv, int N_max, int W, int d, int dtype,
+             int causal, float scale,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------------
+ * kv_select - per-head budgeted top-k over the scores.
+ *
+ * Keeps, per KV head, the k_h first tokens of the order "higher score
+ * first, equal scores by lower token index" (-0.0 equals +0.0; NaN scores
+ * are outside the contract), k_h given by `budget`.  Low scorers are
+ * evicted as in importance-based eviction ("A Simple Plug-in for Improving
+ * Eviction-Based KV Cache Compression", section "Enonce du Probleme").
+ *
+ * scores     [B][Hkv][N_max] fp32 (entries t >= n_b are ignored)
+ * budget     host pointer, see kv_budget
+ * kept_idx   [B][Hkv][N_max] int32 out: the first kept_count[head] entries
+ *            of each head are its kept token indices in ascending order; the
+ *            rest are not written
+ * kept_count [B*Hkv] int32 out
+ * workspace  kv_select_workspace_size() bytes (may be 0 bytes / NULL when
+ *            that size is 0)
+ * ---------------------------------------------------------------------- */
+size_t kv_select_workspace_size(int B, int Hkv, int N_max);
+int kv_select(const float* scores, const int32_t* ctx_len,
+              int B, int Hkv, int N_max, const kv_budget* budget,
+              int32_t* kept_idx, int32_t* kept_count,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------------
+ * kv_compact - gather the kept rows into one packed, ordered cache.
+ *
+ * The result keeps the plain K/V row layout so an ordinary attention kernel
+ * reads it ("KV Cache Transform Coding for Compact Storage in LLM
+ * Inference", section 3; "KVzap: Fast, Adaptive, and Faithful KV Cache
+ * Pruning", section 1).  Heads are packed (b, h) row-major:
+ *   offsets[0] = 0, offsets[i+1] = offsets[i] + kept_count[i]
+ *   k_c[offsets[i] + r] = k[b,h,kept_idx[b,h,r]]   (bit-exact), same for v_c
+ *   pos[offsets[i] + r] = kept_idx[b,h,r]          (original token index)
+ *
+ * k, v          [B][Hkv][N_max][d] dtype
+ * kept_idx, kept_count as produced by kv_select (indices must be < N_max)
+ * k_c, v_c      [capacity_rows][d] dtype out
+ * pos           [capacity_rows] int32 out
+ * offsets       [B*Hkv + 1] int64 out; always the true prefix sums
+ * capacity_rows rows available in k_c / v_c / pos.  Rows at or beyond it are
+ *               not written; the caller detects truncation after
+ *               synchronising as offsets[B*Hkv] > capacity_rows.
+ * Limits: B*Hkv <= 4096.
+ * ---------------------------------------------------------------------- */
+int kv_compact(const void* k, const void* v, int B, int Hkv, int N_max, int d, int dtype,
+               const int32_t* kept_idx, const int32_t* kept_count,
+               void* k_c, void* v_c, int32_t* pos, int64_t* offsets,
+               int64_t capacity_rows, void* stream);
+
+/* ----------------------------------------------------------------------
+ * kv_decode_attn - one decode query per query head over the packed cache.
+ *
+ * Decode reads the compacted cache as ordinary softmax attention; it is
+ * bandwidth-bound ("KVzap: Fast, Adaptive, and Faithful KV Cache Pruning",
+ * section 4).  For query head j of KV head h (rows o..o+k-1 of head
+ * b*Hkv+h, clipped to capacity_rows):
+ *   u_i = scale * <q[b,j,:], k_c[o+i,:]>
+ *   out[b,j,:] = sum_i softmax(u)_i v_c[o+i,:],  lse[b,j] = log sum_i exp(u_i)
+ * A head with no rows gives out = 0 and lse = -inf.
+ *
+ * q             [B][Hq][d] dtype
+ * k_c, v_c      [capacity_rows][d] dtype;  offsets [B*Hkv+1] int64
+ * out           [B][Hq][d] fp32 out;  lse [B][Hq] fp32 out (natural log) or NULL
+ * scale         <= 0 selects 1/sqrt(d)
+ * workspace     kv_decode_workspace_size() bytes
+ * Limits: B*Hkv <= 4096, capacity_rows < 2^31.
+ * ---------------------------------------------------------------------- */
+size_t kv_decode_workspace_size(int B, int Hq, int Hkv, int d, int64_t capacity_rows);
+int kv_decode_attn(const void* q, const void* k_c, const void* v_c, const int64_t* offsets,
+                   int B, int Hq, int Hkv, int d, int dtype, float scale,
+                   int64_t capacity_rows, float* out, float* lse,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------------
+ * Measurement hook (not part of the method): per-kernel GPU time.
+ *
+ * kv_timing_enable(1) clears earlier records and makes every kernel the
+ * library launches afterwards be bracketed by two hipEvents recorded on that
+ * launch's own stream; kv_timing_enable(0) stops recording.  kv_timing_read
+ * waits for the recorded events and writes up to max_entries per-kernel
+ * totals (host array, caller-owned), returning the number of distinct
+ * kernels (or a negative kv_status).  Timing adds event records between
+ * launches, so it is meant for measurement runs, not production.
+ * ---------------------------------------------------------------------- */
+typedef struct kv_kernel_time {
+  char name[40];
+  int64_t launches;
+  double total_ms;
+} kv_kernel_time;
+int kv_timing_enable(int on);
+int kv_timing_read(kv_kernel_time* out, int max_entries);
+
+/* Human-readable name of a kv_status value (static string). */
+const char* kv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVCC_H */

@@ -1,0 +1,62 @@
+"""ctypes loader and prototypes for libkvcc.so (declarations in include/kvcc.h)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from ctypes import c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvcc.so")
+
+KV_F32 = 0
+KV_BF16 = 1
+
+
+class KvBudget(ctypes.Structure):
+    _fields_ = [("mode", c_int32), ("k", c_void_p), ("ratio", c_void_p),
+                ("k_scalar", c_int32), ("ratio_scalar", c_float), ("tau", c_float),
+                ("mass", c_float), ("min_ratio", c_float), ("max_ratio", c_float)]
+
+
+class KvKernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 40), ("launches", c_int64), ("total_ms", ctypes.c_double)]
+
+
+# name -> (restype, argtypes)
+PROTOTYPES = {
+    "kv_score_workspace_size": (c_size_t, [c_int] * 6),
+    "kv_score": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                         c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_float,
+                         c_void_p, c_size_t, c_void_p]),
+    "kv_select_workspace_size": (c_size_t, [c_int] * 3),
+    "kv_select": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, ctypes.POINTER(KvBudget),
+                          c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "kv_compact": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
+                           c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                           c_int64, c_void_p]),
+    "kv_decode_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int, c_int64]),
+    "kv_decode_attn": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p,
+                               c_int, c_int, c_int, c_int, c_int, c_float, c_int64,
+                               c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "kv_status_string": (ctypes.c_char_p, [c_int]),
+    "kv_timing_enable": (c_int, [c_int]),
+    "kv_timing_read": (c_int, [ctypes.POINTER(KvKernelTime), c_int]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvcc.so; raises if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m kv_cache_compression_score_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in PROTOTYPES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib

@@ -1,0 +1,162 @@
+"""Python binding of libkvcc.so: the four C entry points over torch tensors.
+
+Each function only checks and marshals arguments (device pointers, sizes,
+the current HIP stream) and allocates outputs and workspace through torch;
+every step of the computation runs in the library's HIP kernels.  Calls are
+asynchronous on ``torch.cuda.current_stream()``.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional
+
+import torch
+
+from ._lib import KV_BF16, KV_F32, KvBudget, lib
+
+BUDGET_K = 0
+BUDGET_RATIO = 1
+BUDGET_THRESHOLD = 2
+BUDGET_MASS = 3
+
+
+class KvError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = lib().kv_status_string(status).decode()
+        super().__init__(f"{fn} failed: {msg} ({status})")
+        self.status = status
+
+
+@dataclasses.dataclass
+class Budget:
+    """Per-head budget; see kv_budget in include/kvcc.h."""
+    mode: int = BUDGET_RATIO
+    k: Optional[torch.Tensor] = None        # device int32 [B*Hkv]
+    ratio: Optional[torch.Tensor] = None    # device fp32 [B*Hkv]
+    k_scalar: int = 0
+    ratio_scalar: float = 0.0
+    tau: float = 0.0
+    mass: float = 0.0
+    min_ratio: float = 0.0
+    max_ratio: float = 1.0
+
+    def to_c(self) -> KvBudget:
+        return KvBudget(self.mode, _ptr(self.k), _ptr(self.ratio), int(self.k_scalar),
+                        float(self.ratio_scalar), float(self.tau), float(self.mass),
+                        float(self.min_ratio), float(self.max_ratio))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KV_BF16
+    if t.dtype == torch.float32:
+        return KV_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _call(fn: str, status: int):
+    if status != 0:
+        raise KvError(fn, status)
+
+
+def kv_score_workspace_size(B, Hq, Hkv, N_max, W, d) -> int:
+    return int(lib().kv_score_workspace_size(B, Hq, Hkv, N_max, W, d))
+
+
+def kv_score(q_win: torch.Tensor, k: torch.Tensor, ctx_len: Optional[torch.Tensor] = None, *,
+             scale: float = 0.0, causal: bool = False, with_row_lse: bool = False,
+             scores: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Window scores [B][Hkv][N_max] fp32 (and row LSE [B][Hq][W] if asked)."""
+    _check(q_win, "q_win"); _check(k, "k")
+    B, Hq, W, d = q_win.shape
+    _, Hkv, N_max, _ = k.shape
+    if scores is None:
+        scores = torch.empty(B, Hkv, N_max, device=k.device, dtype=torch.float32)
+    row_lse = torch.empty(B, Hq, W, device=k.device, dtype=torch.float32) if with_row_lse else None
+    need = kv_score_workspace_size(B, Hq, Hkv, N_max, W, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=k.device, dtype=torch.uint8)
+    if ctx_len is not None:
+        _check(ctx_len, "ctx_len")
+    _call("kv_score", lib().kv_score(
+        _ptr(q_win), _ptr(k), _ptr(ctx_len), _ptr(scores), _ptr(row_lse),
+        B, Hq, Hkv, N_max, W, d, _dtype_code(k), int(bool(causal)), float(scale),
+        _ptr(workspace), workspace.numel(), _stream()))
+    return scores, row_lse
+
+
+def kv_select(scores: torch.Tensor, ctx_len: Optional[torch.Tensor], budget: Budget, *,
+              kept_idx: Optional[torch.Tensor] = None, kept_count: Optional[torch.Tensor] = None):
+    """Kept indices [B][Hkv][N_max] int32 (first count valid, ascending) and counts [B*Hkv]."""
+    _check(scores, "scores")
+    B, Hkv, N_max = scores.shape
+    if kept_idx is None:
+        kept_idx = torch.empty(B, Hkv, N_max, device=scores.device, dtype=torch.int32)
+    if kept_count is None:
+        kept_count = torch.empty(B * Hkv, device=scores.device, dtype=torch.int32)
+    need = int(lib().kv_select_workspace_size(B, Hkv, N_max))
+    ws = torch.empty(need, device=scores.device, dtype=torch.uint8) if need else None
+    cb = budget.to_c()
+    _call("kv_select", lib().kv_select(
+        _ptr(scores), _ptr(ctx_len), B, Hkv, N_max, ctypes.byref(cb),
+        _ptr(kept_idx), _ptr(kept_count), _ptr(ws), need, _stream()))
+    return kept_idx, kept_count
+
+
+def kv_compact(k: torch.Tensor, v: torch.Tensor, kept_idx: torch.Tensor,
+               kept_count: torch.Tensor, capacity_rows: int, *, out=None):
+    """Packed (k_c, v_c, pos, offsets); k_c/v_c [capacity_rows][d] in k's dtype."""
+    _check(k, "k"); _check(v, "v")
+    B, Hkv, N_max, d = k.shape
+    if out is None:
+        k_c = torch.empty(capacity_rows, d, device=k.device, dtype=k.dtype)
+        v_c = torch.empty(capacity_rows, d, device=k.device, dtype=k.dtype)
+        pos = torch.empty(capacity_rows, device=k.device, dtype=torch.int32)
+        offsets = torch.empty(B * Hkv + 1, device=k.device, dtype=torch.int64)
+    else:
+        k_c, v_c, pos, offsets = out
+    _call("kv_compact", lib().kv_compact(
+        _ptr(k), _ptr(v), B, Hkv, N_max, d, _dtype_code(k), _ptr(kept_idx), _ptr(kept_count),
+        _ptr(k_c), _ptr(v_c), _ptr(pos), _ptr(offsets), int(capacity_rows), _stream()))
+    return k_c, v_c, pos, offsets
+
+
+def kv_decode_workspace_size(B, Hq, Hkv, d, capacity_rows) -> int:
+    return int(lib().kv_decode_workspace_size(B, Hq, Hkv, d, capacity_rows))
+
+
+def kv_decode_attn(q: torch.Tensor, k_c: torch.Tensor, v_c: torch.Tensor,
+                   offsets: torch.Tensor, Hkv: int, *, scale: float = 0.0,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None):
+    """Decode attention (out [B][Hq][d] fp32, lse [B][Hq] fp32) over the packed cache."""
+    _check(q, "q"); _check(k_c, "k_c"); _check(v_c, "v_c"); _check(offsets, "offsets")
+    B, Hq, d = q.shape
+    cap = k_c.shape[0]
+    if out is None:
+        out = torch.empty(B, Hq, d, device=q.device, dtype=torch.float32)
+    if lse is None:
+        lse = torch.empty(B, Hq, device=q.device, dtype=torch.float32)
+    need = kv_decode_workspace_size(B, Hq, Hkv, d, cap)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    _call("kv_decode_attn", lib().kv_decode_attn(
+        _ptr(q), _ptr(k_c), _ptr(v_c), _ptr(offsets), B, Hq, Hkv, d, _dtype_code(q),
+        float(scale), cap, _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))
+    return out, lse

@@ -1,0 +1,92 @@
+// Shared device/host helpers for the kvcc HIP library (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "kvcc.h"
+
+namespace kvcc {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int WAVE = 64;
+constexpr double LOG2E_D = 1.4426950408889634;
+constexpr float LN2_F = 0.69314718055994531f;
+
+// Host-side helpers --------------------------------------------------------
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_LAUNCH;
+}
+
+inline float default_scale(float scale, int d) {
+  return scale > 0.f ? scale : (float)(1.0 / __builtin_sqrt((double)d));
+}
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Brackets one kernel launch with hipEvents on its stream while timing is
+// enabled (kv_timing_enable); a no-op otherwise.
+class TimedLaunch {
+ public:
+  TimedLaunch(const char* name, hipStream_t st);
+  ~TimedLaunch();
+  TimedLaunch(const TimedLaunch&) = delete;
+  TimedLaunch& operator=(const TimedLaunch&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t st_;
+  hipEvent_t start_ = nullptr, stop_ = nullptr;
+};
+
+// Device-side helpers ------------------------------------------------------
+
+// 16-byte vector load/store through plain global accesses.
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// exp2 / log2 on the hardware transcendental unit (v_exp_f32 / v_log_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Wave-wide reductions (64 lanes).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+template <typename I>
+__device__ __forceinline__ I wave_incl_scan(I v) {
+  const int lane = threadIdx.x & (WAVE - 1);
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    I u = __shfl_up(v, o, WAVE);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & (WAVE - 1);
+  return lane == 0 ? 0ull : (~0ull >> (WAVE - lane));
+}
+
+}  // namespace kvcc

@@ -1,0 +1,344 @@
+// Split-K decode attention over the packed, ragged compacted cache.
+//
+// One fresh query per query head reads its KV head's kept rows with plain
+// softmax attention; the step is bandwidth-bound ("KVzap: Fast, Adaptive,
+// and Faithful KV Cache Pruning", section 4, on decode cycles otherwise lost
+// to memory bandwidth), so the kernel is organised around streaming each K/V
+// row from HBM exactly once for all G query heads of its group.
+//
+// Work items are chunks of CH consecutive rows of one head; every workgroup
+// rebuilds the item list from the offsets in LDS and walks it grid-stride,
+// so ragged heads balance by rows, not by head count.  Inside an item a group
+// of d*sizeof(T)/16 lanes owns one row at a time (16 bytes of K and of V per
+// lane, RPG rows in flight), forms the G dot products with a butterfly
+// reduction inside the group, and keeps a base-2 (max, sum, o) per query
+// head.  Groups merge through LDS in a fixed order into one partial per item;
+// a second kernel merges a head's items in item order, so the result is
+// deterministic.
+#include <math.h>
+
+#include "common.hpp"
+
+namespace kvcc {
+namespace {
+
+constexpr int DT = 256;
+constexpr int CH = 128;          // rows per work item
+constexpr int MAX_HEADS = 4096;
+
+struct DecodeArgs {
+  const void* q;
+  const char* kc;
+  const char* vc;
+  const int64_t* offsets;
+  int B, Hq, Hkv, G, n_sub, items_max;
+  int64_t cap;
+  float c;                 // scale * log2(e)
+  float* part_o;           // [n_sub][items_max][GT][D]
+  float2* part_ml;         // [n_sub][items_max][GT]
+  int* item_start;         // [B*Hkv+1] first item of every head (written by the split kernel)
+  float* out;
+  float* lse;
+};
+
+// Row offsets clipped to the capacity, and the first item of every head.
+__device__ void build_items(const DecodeArgs& a, long long* off, int* ist, int* wtot) {
+  const int H = a.B * a.Hkv;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  constexpr int NWV = DT / WAVE;
+  for (int i = tid; i <= H; i += DT) {
+    const long long o = a.offsets[i];
+    off[i] = o < 0 ? 0 : (o > a.cap ? a.cap : o);
+  }
+  __syncthreads();
+  int carry = 0;
+  for (int base = 0; base < H; base += DT) {
+    const int i = base + tid;
+    const int ni = i < H ? (int)(max(off[i + 1] - off[i], 0ll) + CH - 1) / CH : 0;
+    const int inc = wave_incl_scan<int>(ni);
+    if (lane == WAVE - 1) wtot[wave] = inc;
+    __syncthreads();
+    int before = 0, chunk = 0;
+    for (int w = 0; w < NWV; ++w) {
+      if (w < wave) before += wtot[w];
+      chunk += wtot[w];
+    }
+    if (i < H) ist[i] = carry + before + inc - ni;
+    carry += chunk;
+    __syncthreads();
+  }
+  if (tid == 0) ist[H] = carry;
+  __syncthreads();
+}
+
+__device__ __forceinline__ int find_item_head(const int* ist, int H, int it) {
+  int lo = 0, hi = H - 1;   // largest i with ist[i] <= it
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (ist[mid] <= it) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4 w, float* x);
+template <>
+__device__ __forceinline__ void unpack16<__bf16>(const uint4 w, float* x) {
+  x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+  x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+}
+template <>
+__device__ __forceinline__ void unpack16<float>(const uint4 w, float* x) {
+  x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y);
+  x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
+}
+
+template <typename T, int D, int GT>
+__global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
+  constexpr int EPL = 16 / (int)sizeof(T);     // elements per lane
+  constexpr int LPR = D / EPL;                 // lanes per row (power of two, <= 32)
+  constexpr int NG = DT / LPR;                 // row groups per workgroup
+  constexpr int RPG = (CH + NG - 1) / NG;      // rows per group per item
+  constexpr int ROWB = D * (int)sizeof(T);
+
+  __shared__ int wtot[DT / WAVE];
+  __shared__ float sm_m[NG][GT], sm_l[NG][GT];
+  __shared__ float sm_o[NG][GT][D];
+  extern __shared__ long long dyn[];   // off[H+1] (int64) then ist[H+1] (int32)
+  const int H = a.B * a.Hkv;
+  long long* off = dyn;
+  int* ist = reinterpret_cast<int*>(dyn + H + 1);
+
+  build_items(a, off, ist, wtot);
+  const int n_items = ist[H];
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i <= H; i += DT) a.item_start[i] = ist[i];
+  const int tid = threadIdx.x, grp = tid / LPR, sub = tid % LPR;
+  const int qsub = blockIdx.y;
+
+  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const int head = find_item_head(ist, H, it);
+    const int b = head / a.Hkv, h = head % a.Hkv;
+    const long long r0 = off[head] + (long long)(it - ist[head]) * CH;
+    const long long r1 = min(r0 + CH, off[head + 1]);
+
+    // query slices (this lane's EPL elements) of the GT query heads, in base 2
+    float qv[GT][EPL];
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      const int jg = qsub * GT + g;
+      if (jg < a.G) {
+        const int j = h * a.G + jg;
+        const char* qp = static_cast<const char*>(a.q) +
+                         (((size_t)b * a.Hq + j) * D + sub * EPL) * sizeof(T);
+        unpack16<T>(ld16(qp), qv[g]);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qv[g][e] *= a.c;
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qv[g][e] = 0.f;
+      }
+    }
+
+    uint4 kr[RPG], vr[RPG];
+#pragma unroll
+    for (int u = 0; u < RPG; ++u) {
+      const long long row = r0 + grp + (long long)u * NG;
+      kr[u] = make_uint4(0, 0, 0, 0);
+      vr[u] = make_uint4(0, 0, 0, 0);
+      if (row < r1) {
+        kr[u] = ld16(a.kc + (size_t)row * ROWB + sub * 16);
+        vr[u] = ld16(a.vc + (size_t)row * ROWB + sub * 16);
+      }
+    }
+
+    float sc[RPG][GT];
+#pragma unroll
+    for (int u = 0; u < RPG; ++u) {
+      float kx[EPL];
+      unpack16<T>(kr[u], kx);
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s = fmaf(qv[g][e], kx[e], s);
+#pragma unroll
+        for (int o = LPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, WAVE);
+        sc[u][g] = s;
+      }
+    }
+
+    float mg[GT], lg[GT], og[GT][EPL];
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < RPG; ++u)
+        if (r0 + grp + (long long)u * NG < r1) m = fmaxf(m, sc[u][g]);
+      mg[g] = m;
+      lg[g] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) og[g][e] = 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < RPG; ++u) {
+      if (r0 + grp + (long long)u * NG < r1) {
+        float vx[EPL];
+        unpack16<T>(vr[u], vx);
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+          const float p = fast_exp2(sc[u][g] - mg[g]);
+          lg[g] += p;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) og[g][e] = fmaf(p, vx[e], og[g][e]);
+        }
+      }
+    }
+
+    // merge the row groups (fixed order) into this item's partial
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      if (sub == 0) { sm_m[grp][g] = mg[g]; sm_l[grp][g] = lg[g]; }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sm_o[grp][g][sub * EPL + e] = og[g][e];
+    }
+    __syncthreads();
+    const size_t pbase = ((size_t)qsub * a.items_max + it) * GT;
+    for (int x = tid; x < GT * D; x += DT) {
+      const int g = x / D, e = x % D;
+      float M = -INFINITY;
+      for (int r = 0; r < NG; ++r) M = fmaxf(M, sm_m[r][g]);
+      float L = 0.f, O = 0.f;
+      if (M != -INFINITY) {
+        for (int r = 0; r < NG; ++r) {
+          const float w = fast_exp2(sm_m[r][g] - M);
+          L = fmaf(sm_l[r][g], w, L);
+          O = fmaf(sm_o[r][g][e], w, O);
+        }
+      }
+      a.part_o[(pbase + g) * D + e] = O;
+      if (e == 0) a.part_ml[pbase + g] = make_float2(M, L);
+    }
+    __syncthreads();
+  }
+}
+
+template <int D, int GT>
+__global__ __launch_bounds__(D) void decode_combine(DecodeArgs a) {
+  const int* ist = a.item_start;
+  const int bj = blockIdx.x;                  // b*Hq + j
+  const int b = bj / a.Hq, j = bj % a.Hq;
+  const int h = j / a.G, jg = j % a.G;
+  const int qsub = jg / GT, g = jg % GT;
+  const int head = b * a.Hkv + h;
+  const int i0 = ist[head], i1 = ist[head + 1];
+  const int e = threadIdx.x;
+  float M = -INFINITY;
+  for (int it = i0; it < i1; ++it)
+    M = fmaxf(M, a.part_ml[((size_t)qsub * a.items_max + it) * GT + g].x);
+  float L = 0.f, O = 0.f;
+  if (M != -INFINITY) {
+    for (int it = i0; it < i1; ++it) {
+      const size_t p = ((size_t)qsub * a.items_max + it) * GT + g;
+      const float2 ml = a.part_ml[p];
+      const float w = exp2f(ml.x - M);
+      L = fmaf(ml.y, w, L);
+      O = fmaf(a.part_o[p * D + e], w, O);
+    }
+  }
+  const bool any = L > 0.f;
+  a.out[(size_t)bj * D + e] = any ? O / L : 0.f;
+  if (a.lse && e == 0) a.lse[bj] = any ? (M + log2f(L)) * LN2_F : -INFINITY;
+}
+
+struct DecodePlan {
+  int GT, n_sub, items_max;
+  size_t off_ml, off_ist, bytes;
+};
+
+bool plan_decode(int B, int Hq, int Hkv, int d, int64_t cap, DecodePlan* p) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || (d != 64 && d != 128) || cap < 0 ||
+      cap >= (int64_t(1) << 31) || (int64_t)B * Hkv > MAX_HEADS)
+    return false;
+  const int G = Hq / Hkv;
+  p->GT = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
+  p->n_sub = ceil_div(G, p->GT);
+  const int64_t items = ceil_div64(cap, CH) + (int64_t)B * Hkv;
+  if (items >= (int64_t(1) << 31)) return false;
+  p->items_max = (int)std::max<int64_t>(items, 1);
+  const size_t slots = (size_t)p->n_sub * p->items_max * p->GT;
+  const size_t po = slots * d * sizeof(float);
+  p->off_ml = (po + 255) & ~size_t(255);
+  p->off_ist = (p->off_ml + slots * sizeof(float2) + 255) & ~size_t(255);
+  p->bytes = p->off_ist + ((size_t)B * Hkv + 1) * sizeof(int);
+  return true;
+}
+
+template <typename T, int D, int GT>
+void launch_decode(const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)std::min(a.items_max, 8192), a.n_sub);
+  const size_t dyn = (size_t)(a.B * a.Hkv + 1) * (sizeof(long long) + sizeof(int));
+  {
+    TimedLaunch t("decode_split", st);
+    decode_split<T, D, GT><<<grid, DT, dyn, st>>>(a);
+  }
+  {
+    TimedLaunch t("decode_combine", st);
+    decode_combine<D, GT><<<a.B * a.Hq, D, 0, st>>>(a);
+  }
+}
+
+template <typename T, int D>
+void launch_decode_g(const DecodeArgs& a, int GT, hipStream_t st) {
+  switch (GT) {
+    case 1: launch_decode<T, D, 1>(a, st); break;
+    case 2: launch_decode<T, D, 2>(a, st); break;
+    case 4: launch_decode<T, D, 4>(a, st); break;
+    default: launch_decode<T, D, 8>(a, st); break;
+  }
+}
+
+}  // namespace
+}  // namespace kvcc
+
+using namespace kvcc;
+
+extern "C" size_t kv_decode_workspace_size(int B, int Hq, int Hkv, int d, int64_t capacity_rows) {
+  DecodePlan p;
+  return plan_decode(B, Hq, Hkv, d, capacity_rows, &p) ? p.bytes : 0;
+}
+
+extern "C" int kv_decode_attn(const void* q, const void* k_c, const void* v_c,
+                              const int64_t* offsets, int B, int Hq, int Hkv, int d, int dtype,
+                              float scale, int64_t capacity_rows, float* out, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !offsets || !out) return KV_ERR_NULL;
+  if (capacity_rows > 0 && (!k_c || !v_c)) return KV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_c) || !aligned16(v_c) || !aligned16(offsets) ||
+      !aligned16(out) || !aligned16(lse) || !aligned16(workspace))
+    return KV_ERR_ALIGN;
+  if (dtype != KV_F32 && dtype != KV_BF16) return KV_ERR_DTYPE;
+  DecodePlan p;
+  if (!plan_decode(B, Hq, Hkv, d, capacity_rows, &p)) return KV_ERR_SHAPE;
+  if (!workspace || workspace_bytes < p.bytes) return KV_ERR_WORKSPACE;
+
+  DecodeArgs a;
+  a.q = q; a.kc = static_cast<const char*>(k_c); a.vc = static_cast<const char*>(v_c);
+  a.offsets = offsets; a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+  a.n_sub = p.n_sub; a.items_max = p.items_max; a.cap = capacity_rows;
+  a.c = (float)((scale > 0.f ? (double)scale : 1.0 / sqrt((double)d)) * LOG2E_D);
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + p.off_ml);
+  a.item_start = reinterpret_cast<int*>(static_cast<char*>(workspace) + p.off_ist);
+  a.out = out; a.lse = lse;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == KV_BF16) {
+    if (d == 128) launch_decode_g<__bf16, 128>(a, p.GT, st);
+    else launch_decode_g<__bf16, 64>(a, p.GT, st);
+  } else {
+    if (d == 128) launch_decode_g<float, 128>(a, p.GT, st);
+    else launch_decode_g<float, 64>(a, p.GT, st);
+  }
+  return launch_status();
+}

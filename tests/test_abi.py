@@ -1,0 +1,113 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any launch (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_compression_score_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvcc.h")
+
+KV_OK, KV_ERR_NULL, KV_ERR_ALIGN, KV_ERR_SHAPE, KV_ERR_DTYPE, KV_ERR_MODE, KV_ERR_WORKSPACE = range(7)
+P = 1 << 20          # a fake, aligned, non-null "device" address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(_lib.PROTOTYPES)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = _lib.lib()
+    for s in range(8):
+        assert L.kv_status_string(s)
+    assert L.kv_status_string(0) == b"ok"
+
+
+def test_workspace_sizes():
+    L = _lib.lib()
+    assert L.kv_score_workspace_size(4, 32, 8, 32768, 64, 128) > 0
+    assert L.kv_score_workspace_size(1, 32, 7, 100, 8, 128) == 0       # Hq % Hkv != 0
+    assert L.kv_score_workspace_size(1, 4, 4, 100, 8, 96) == 0         # d not 64/128
+    assert L.kv_score_workspace_size(1, 4, 4, 100, 200, 64) == 0       # W > N_max
+    assert L.kv_score_workspace_size(1, 64, 1, 4096, 32, 128) == 0     # G*W > 1024
+    assert L.kv_decode_workspace_size(4, 32, 8, 128, 104864) > 0
+    assert L.kv_decode_workspace_size(1, 4, 4, 128, -1) == 0
+    assert L.kv_select_workspace_size(4, 8, 32768) == 0
+
+
+def _score(**kw):
+    a = dict(q=P, k=P, ctx=None, scores=P, lse=None, B=1, Hq=4, Hkv=4, N=256, W=8, d=64,
+             dtype=1, causal=0, scale=0.0, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return _lib.lib().kv_score(a["q"], a["k"], a["ctx"], a["scores"], a["lse"], a["B"], a["Hq"],
+                               a["Hkv"], a["N"], a["W"], a["d"], a["dtype"], a["causal"],
+                               a["scale"], a["ws"], a["wsb"], None)
+
+
+def test_score_validation():
+    assert _score(q=None) == KV_ERR_NULL
+    assert _score(k=P + 8) == KV_ERR_ALIGN
+    assert _score(dtype=7) == KV_ERR_DTYPE
+    assert _score(d=96) == KV_ERR_SHAPE
+    assert _score(Hkv=3) == KV_ERR_SHAPE
+    assert _score(W=0) == KV_ERR_SHAPE
+    assert _score(ws=None) == KV_ERR_WORKSPACE
+    assert _score(wsb=16) == KV_ERR_WORKSPACE
+
+
+def _select(budget, **kw):
+    a = dict(scores=P, ctx=None, B=1, Hkv=2, N=64, idx=P, cnt=P)
+    a.update(kw)
+    return _lib.lib().kv_select(a["scores"], a["ctx"], a["B"], a["Hkv"], a["N"],
+                                ctypes.byref(budget), a["idx"], a["cnt"], None, 0, None)
+
+
+def test_select_validation():
+    B = _lib.KvBudget
+    assert _select(B(1, None, None, 0, 0.5, 0, 0, 0, 1), scores=None) == KV_ERR_NULL
+    assert _select(B(9, None, None, 0, 0.5, 0, 0, 0, 1)) == KV_ERR_MODE
+    assert _select(B(1, None, None, 0, 1.5, 0, 0, 0, 1)) == KV_ERR_MODE
+    assert _select(B(3, None, None, 0, 0, 0, 2.0, 0, 1)) == KV_ERR_MODE
+    assert _select(B(2, None, None, 0, 0, float("nan"), 0, 0, 1)) == KV_ERR_MODE
+    assert _select(B(2, None, None, 0, 0, 0.1, 0, -0.5, 1)) == KV_ERR_MODE
+    assert _select(B(1, None, None, 0, 0.5, 0, 0, 0, 1), N=0) == KV_ERR_SHAPE
+    assert _select(B(1, P + 4, None, 0, 0.5, 0, 0, 0, 1)) == KV_ERR_ALIGN
+
+
+def test_compact_and_decode_validation():
+    L = _lib.lib()
+    assert L.kv_compact(None, P, 1, 2, 64, 64, 1, P, P, P, P, P, P, 10, None) == KV_ERR_NULL
+    assert L.kv_compact(P, P, 1, 2, 64, 80, 1, P, P, P, P, P, P, 10, None) == KV_ERR_SHAPE
+    assert L.kv_compact(P, P, 1, 2, 64, 64, 5, P, P, P, P, P, P, 10, None) == KV_ERR_DTYPE
+    assert L.kv_compact(P, P, 1, 2, 64, 64, 1, P, P, None, P, P, P, 10, None) == KV_ERR_NULL
+    assert L.kv_compact(P, P, 4097, 1, 64, 64, 1, P, P, P, P, P, P, 10, None) == KV_ERR_SHAPE
+    assert L.kv_decode_attn(None, P, P, P, 1, 4, 2, 64, 1, 0.0, 8, P, None, P, 1 << 20,
+                            None) == KV_ERR_NULL
+    assert L.kv_decode_attn(P, P, P, P, 1, 4, 3, 64, 1, 0.0, 8, P, None, P, 1 << 20,
+                            None) == KV_ERR_SHAPE
+    assert L.kv_decode_attn(P, P, P, P, 1, 4, 2, 64, 1, 0.0, 8, P, None, P, 8,
+                            None) == KV_ERR_WORKSPACE
+    assert L.kv_decode_attn(P, P, P + 2, P, 1, 4, 2, 64, 1, 0.0, 8, P, None, P, 1 << 20,
+                            None) == KV_ERR_ALIGN
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.lib()

@@ -1,0 +1,93 @@
+"""kv_score on the GPU vs the float64 oracle (scores and row log-sum-exps)."""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_compression_score_amd import api
+from kv_cache_compression_score_amd import workloads as wl
+from oracle import oracle as orc
+
+from gpu_helpers import check_scores, dev, log
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # B, Hq, Hkv, W, N_max, d, dtype, causal, ctx
+    (1, 4, 4, 32, 1000, 64, torch.float32, False, None),          # fp32, ragged tail
+    (2, 8, 2, 16, 777, 128, torch.bfloat16, False, [777, 300]),   # GQA 4, ragged batch
+    (1, 8, 2, 24, 1300, 64, torch.bfloat16, True, None),          # causal, W not /32
+    (2, 6, 2, 5, 513, 128, torch.float32, True, [513, 64]),       # fp32 d=128, G=3
+    (1, 32, 8, 64, 2048, 128, torch.bfloat16, False, None),       # Llama head shape
+    (1, 64, 4, 32, 700, 128, torch.bfloat16, False, None),        # G*W = 512 rows
+    (1, 4, 1, 256, 300, 64, torch.bfloat16, True, None),          # G*W = 1024 rows
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}Hq{c[1]}Hkv{c[2]}W{c[3]}N{c[4]}"
+                         f"d{c[5]}{'f32' if c[6] == torch.float32 else 'bf16'}{'c' if c[7] else ''}")
+def test_score_small(case):
+    B, Hq, Hkv, W, N, d, dt, causal, ctx = case
+    log(f"score case {case}")
+    lay = wl.random_case(11, B=B, Hq=Hq, Hkv=Hkv, d=d, N_max=N, W=W, dtype=dt, ctx=ctx)
+    s_gpu, lse_gpu = api.kv_score(dev(lay.q_win), dev(lay.k), dev(lay.ctx_len),
+                                  causal=causal, with_row_lse=True)
+    torch.cuda.synchronize()
+    s_ref, lse_ref = orc.window_scores(lay.q_win, lay.k, lay.ctx_len, causal=causal)
+    err = check_scores(s_gpu.cpu().numpy(), s_ref, lay.ctx_len.numpy(), W, Hq // Hkv)
+    np.testing.assert_allclose(lse_gpu.cpu().numpy(), lse_ref, atol=1e-3, rtol=0)
+    log(f"  max rel score err {err:.3e}")
+
+
+def test_score_scale_argument():
+    lay = wl.random_case(3, B=1, Hq=4, Hkv=2, d=64, N_max=400, W=8)
+    s_gpu, _ = api.kv_score(dev(lay.q_win), dev(lay.k), None, scale=0.3)
+    s_ref, _ = orc.window_scores(lay.q_win, lay.k, None, scale=0.3)
+    check_scores(s_gpu.cpu().numpy(), s_ref, [400], 8, 2)
+
+
+def test_score_sum_invariant_and_determinism():
+    lay = wl.random_case(5, B=2, Hq=16, Hkv=4, d=128, N_max=3000, W=64, ctx=[3000, 1111])
+    q, k, c = dev(lay.q_win), dev(lay.k), dev(lay.ctx_len)
+    s1, _ = api.kv_score(q, k, c)
+    s2, _ = api.kv_score(q, k, c)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    for b, n in enumerate([3000, 1111]):
+        tot = s1[b, :, :n].double().sum(dim=1).cpu().numpy()
+        np.testing.assert_allclose(tot, 64 * 4, rtol=1e-4)
+
+
+def test_score_zero_queries_uniform():
+    lay = wl.random_case(8, B=1, Hq=4, Hkv=1, d=64, N_max=640, W=16)
+    q = torch.zeros_like(lay.q_win)
+    s, _ = api.kv_score(dev(q), dev(lay.k), None)
+    np.testing.assert_allclose(s.cpu().numpy(), 64 / 640, rtol=1e-5)
+
+
+def test_score_llama8b_layer_full():
+    cfg = wl.CONFIGS["llama8b_layer"]
+    lay = wl.make_layer(cfg, with_v=False)
+    log("score llama8b_layer full")
+    s_gpu, lse_gpu = api.kv_score(dev(lay.q_win), dev(lay.k), dev(lay.ctx_len), with_row_lse=True)
+    torch.cuda.synchronize()
+    s_ref, lse_ref = orc.window_scores(lay.q_win, lay.k, lay.ctx_len)
+    err = check_scores(s_gpu.cpu().numpy(), s_ref, lay.ctx_len.numpy(), cfg.W, cfg.G)
+    np.testing.assert_allclose(lse_gpu.cpu().numpy(), lse_ref, atol=1e-3, rtol=0)
+    log(f"  max rel score err {err:.3e}")
+
+
+def test_score_long128k_sampled_head():
+    # Full 128K context and W = 128 (512 rows per head): the oracle checks one
+    # head element by element; every head must sum to W * G.
+    cfg = wl.CONFIGS["long128k"]
+    lay = wl.make_layer(cfg, 0, with_v=False)
+    log("score long128k layer 0")
+    s_gpu, _ = api.kv_score(dev(lay.q_win), dev(lay.k), dev(lay.ctx_len))
+    torch.cuda.synchronize()
+    tot = s_gpu.double().sum(dim=2).cpu().numpy()
+    np.testing.assert_allclose(tot, cfg.W * cfg.G, rtol=1e-4)
+    h = 5
+    s_ref, _ = orc.window_scores(lay.q_win[:, h * 4:(h + 1) * 4], lay.k[:, h:h + 1],
+                                 lay.ctx_len)
+    err = check_scores(s_gpu[:, h:h + 1].cpu().numpy(), s_ref, lay.ctx_len.numpy(), cfg.W, cfg.G)
+    log(f"  head {h} max rel score err {err:.3e}")

@@ -73,7 +73,7 @@ class Pipeline:
             self.cap = B * Hkv * max(1, int(math.floor(float(np.float32(cfg.ratio)) * N + 0.5)))
         f32 = torch.float32
         self.scores = torch.empty(B, Hkv, N, device=d, dtype=f32)
-        self.ws_s = torch.empty(api.kv_score_workspace_size(B, cfg.Hq, Hkv, N, cfg.W, D),
+        self.ws_s = torch.zeros(api.kv_score_workspace_size(B, cfg.Hq, Hkv, N, cfg.W, D),
                                 device=d, dtype=torch.uint8)
         self.idx = torch.empty(B, Hkv, N, device=d, dtype=torch.int32)
         self.cnt = torch.empty(B * Hkv, device=d, dtype=torch.int32)
@@ -83,7 +83,7 @@ class Pipeline:
                      torch.empty(B * Hkv + 1, device=d, dtype=torch.int64))
         self.out = torch.empty(B, cfg.Hq, D, device=d, dtype=f32)
         self.lse = torch.empty(B, cfg.Hq, device=d, dtype=f32)
-        self.ws_d = torch.empty(api.kv_decode_workspace_size(B, cfg.Hq, Hkv, D, self.cap),
+        self.ws_d = torch.zeros(api.kv_decode_workspace_size(B, cfg.Hq, Hkv, D, self.cap),
                                 device=d, dtype=torch.uint8)
 
     def step(self):
@@ -190,8 +190,8 @@ def main():
     else:
         achieved, peak, unit = amount / t_dom / 1e9, PEAK_HBM_GBPS, "GB/s"
     t = {k: v[0] * 1e-3 for k, v in kt.items()}
-    t_score = t["score_rowstats"] + t["score_lse"] + t["score_colsum"]
-    t_dec = t["decode_split"] + t["decode_combine"]
+    t_score = t["score_rowstats"] + t["score_fold"] + t["score_colsum"]
+    t_dec = t["decode_split"] + t["decode_merge"]
     t_scd = t["select"] + t["compact"] + t_dec
     res = {
         "metric": METRIC,

@@ -11,7 +11,8 @@
  * - Every tensor pointer is DEVICE memory owned by the caller.  The library
  *   never allocates, frees or retains a pointer beyond the call.  Scratch
  *   memory comes only from the caller's `workspace`, sized by the matching
- *   *_workspace_size() function (a pure host function).
+ *   *_workspace_size() function (a pure host function).  Calls that share
+ *   one workspace must not overlap in time (e.g. on two streams).
  * - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *   enqueue work on it and never synchronise; buffers must stay alive until
  *   the stream has passed the call.

@@ -91,7 +91,7 @@ def kv_score(q_win: torch.Tensor, k: torch.Tensor, ctx_len: Optional[torch.Tenso
     row_lse = torch.empty(B, Hq, W, device=k.device, dtype=torch.float32) if with_row_lse else None
     need = kv_score_workspace_size(B, Hq, Hkv, N_max, W, d)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), device=k.device, dtype=torch.uint8)
+        workspace = torch.zeros(max(need, 1), device=k.device, dtype=torch.uint8)
     if ctx_len is not None:
         _check(ctx_len, "ctx_len")
     _call("kv_score", lib().kv_score(
@@ -155,7 +155,7 @@ def kv_decode_attn(q: torch.Tensor, k_c: torch.Tensor, v_c: torch.Tensor,
         lse = torch.empty(B, Hq, device=q.device, dtype=torch.float32)
     need = kv_decode_workspace_size(B, Hq, Hkv, d, cap)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+        workspace = torch.zeros(max(need, 1), device=q.device, dtype=torch.uint8)
     _call("kv_decode_attn", lib().kv_decode_attn(
         _ptr(q), _ptr(k_c), _ptr(v_c), _ptr(offsets), B, Hq, Hkv, d, _dtype_code(q),
         float(scale), cap, _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))

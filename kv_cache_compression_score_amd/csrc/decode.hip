@@ -13,7 +13,7 @@
 // lane, RPG rows in flight), forms the G dot products with a butterfly
 // reduction inside the group, and keeps a base-2 (max, sum, o) per query
 // head.  Groups merge through LDS in a fixed order into one partial per item;
-// a second kernel merges a head's items in item order, so the result is
+// a second kernel merges each head's items in item order, so the result is
 // deterministic.
 #include <math.h>
 
@@ -223,32 +223,45 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
   }
 }
 
+// Per (head, query sub-group): merge the head's items in item order.  Loads
+// are batched so a head's items are fetched a few at a time, not one by one.
 template <int D, int GT>
-__global__ __launch_bounds__(D) void decode_combine(DecodeArgs a) {
-  const int* ist = a.item_start;
-  const int bj = blockIdx.x;                  // b*Hq + j
-  const int b = bj / a.Hq, j = bj % a.Hq;
-  const int h = j / a.G, jg = j % a.G;
-  const int qsub = jg / GT, g = jg % GT;
-  const int head = b * a.Hkv + h;
-  const int i0 = ist[head], i1 = ist[head + 1];
-  const int e = threadIdx.x;
-  float M = -INFINITY;
-  for (int it = i0; it < i1; ++it)
-    M = fmaxf(M, a.part_ml[((size_t)qsub * a.items_max + it) * GT + g].x);
-  float L = 0.f, O = 0.f;
-  if (M != -INFINITY) {
-    for (int it = i0; it < i1; ++it) {
-      const size_t p = ((size_t)qsub * a.items_max + it) * GT + g;
-      const float2 ml = a.part_ml[p];
-      const float w = exp2f(ml.x - M);
-      L = fmaf(ml.y, w, L);
-      O = fmaf(a.part_o[p * D + e], w, O);
+__global__ __launch_bounds__(GT * D) void decode_merge(DecodeArgs a) {
+  constexpr int U = 16;
+  const int head = blockIdx.x, qsub = blockIdx.y;
+  const int b = head / a.Hkv, h = head % a.Hkv;
+  const int i0 = a.item_start[head], i1 = a.item_start[head + 1];
+  const size_t base = (size_t)qsub * a.items_max;
+  {
+    const int x = threadIdx.x;
+    const int g = x / D, e = x % D, jg = qsub * GT + g;
+    if (jg >= a.G) return;
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    for (int it0 = i0; it0 < i1; it0 += U) {
+      float2 ml[U];
+      float ov[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const size_t p = (base + it0 + u) * GT + g;
+        const bool ok = it0 + u < i1;
+        ml[u] = ok ? a.part_ml[p] : make_float2(-INFINITY, 0.f);
+        ov[u] = ok ? a.part_o[p * D + e] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float mn = fmaxf(M, ml[u].x);
+        if (mn == -INFINITY) continue;
+        const float wa = exp2f(M - mn), wb = exp2f(ml[u].x - mn);
+        L = L * wa + ml[u].y * wb;
+        O = O * wa + ov[u] * wb;
+        M = mn;
+      }
     }
+    const size_t bj = (size_t)b * a.Hq + h * a.G + jg;
+    const bool any = L > 0.f;
+    a.out[bj * D + e] = any ? O / L : 0.f;
+    if (a.lse && e == 0) a.lse[bj] = any ? (M + log2f(L)) * LN2_F : -INFINITY;
   }
-  const bool any = L > 0.f;
-  a.out[(size_t)bj * D + e] = any ? O / L : 0.f;
-  if (a.lse && e == 0) a.lse[bj] = any ? (M + log2f(L)) * LN2_F : -INFINITY;
 }
 
 struct DecodePlan {
@@ -283,8 +296,8 @@ void launch_decode(const DecodeArgs& a, hipStream_t st) {
     decode_split<T, D, GT><<<grid, DT, dyn, st>>>(a);
   }
   {
-    TimedLaunch t("decode_combine", st);
-    decode_combine<D, GT><<<a.B * a.Hq, D, 0, st>>>(a);
+    TimedLaunch t("decode_merge", st);
+    decode_merge<D, GT><<<dim3(a.B * a.Hkv, a.n_sub), GT * D, 0, st>>>(a);
   }
 }
 

@@ -13,14 +13,22 @@
 // fragments of two 32-row blocks in registers:
 //   pass 1: C[token,row] = K * Q^T, so one lane owns one row and 16 tokens
 //           per block and keeps a running (max, sum of exp2) per row in
-//           registers; the two half-waves and then the token chunks are
-//           merged into a base-2 log-sum-exp per row.
+//           registers; the two half-waves are merged by a lane swizzle and
+//           the chunk partials published.
+//   fold:   one wave per row merges the row's chunk partials (lanes over
+//           chunks, then a fixed butterfly) into a base-2 log-sum-exp.
 //   pass 2: C[row,token] = Q * K^T, so one lane owns one token and 16 rows
 //           per block; exp2(l*c - lse2[row]) is summed in-lane, then over
 //           half-waves and waves through LDS in a fixed order.
 // All logits are kept in base-2 units: c = scale*log2(e) is applied to the
-// fp32 dot product after the MFMA (bf16 inputs are never rescaled).
+// fp32 dot product after the MFMA (bf16 inputs are never rescaled).  The
+// exp2 of every logit runs on the VALU's transcendental unit, which sets the
+// pace next to the MFMA, so the per-logit epilogue is kept to one FMA, one
+// exp2 and one add (plus a max in pass 1); masks only exist in tail tiles.
 #include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -30,6 +38,7 @@ namespace {
 constexpr int TOK = 64;          // tokens per LDS tile
 constexpr int TSUB = TOK / 32;   // 32-token MFMA blocks per tile
 constexpr int RBW = 2;           // 32-row blocks per wave
+constexpr int SLOTS_1 = 256 * 3; // pass-1 chunking target: resident workgroups on 256 CUs
 
 template <typename T> struct FragT;
 template <> struct FragT<__bf16> { using vec = bf16x8; };   // 8 elements = 16 B
@@ -69,11 +78,13 @@ struct ScoreArgs {
   const void* k;
   const int32_t* ctx;
   float* scores;
-  float2* part;     // [B*Hkv][n_chunks][R_pad] running (max, sum) per row, base 2
+  float2* part;     // [B*Hkv][R_pad][n_chunks] per-chunk (max, sum of exp2) per row
   float* lse2;      // [B*Hkv][R_pad] base-2 row log-sum-exp (+inf: row adds nothing)
   float* row_lse;   // [B][Hq][W] natural log, optional
-  int B, Hq, Hkv, N_max, W, G, R, R_pad, TC, n_chunks, causal;
-  float c;          // scale * log2(e)
+  int B, Hq, Hkv, N_max, W, G, R, R_pad, causal;
+  int TC, n_chunks;    // pass-1 token chunks (fixed by the sizes: sets the merge order)
+  int TC2, n_chunks2;  // pass-2 token chunks (free: no cross-chunk arithmetic)
+  float c;             // scale * log2(e)
 };
 
 template <typename T, int D, int NW, int PASS>
@@ -86,29 +97,33 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
   constexpr int TILE_VECS = TOK * VPR;
   constexpr int NT = NW * WAVE;
   constexpr int LPT = (TILE_VECS + NT - 1) / NT;
-  constexpr int NRED = PASS == 2 ? 2 * NW : 1;
 
   __shared__ __attribute__((aligned(16))) unsigned char ktile[2][TOK * LDS_STRIDE];
-  __shared__ float red[2][NRED][TOK];
+  __shared__ float red[3][PASS == 2 ? NW : 1][TOK];
+  __shared__ __attribute__((aligned(8))) int rowpos[PASS == 2 ? NW * RBW * 32 : 2];
 
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int hf = lane >> 5, l32 = lane & 31;
   const int n = a.ctx ? min(max(a.ctx[b], 0), a.N_max) : a.N_max;
   const int head = b * a.Hkv + h;
-  const int t0 = c * a.TC;
+  const int TC = PASS == 1 ? a.TC : a.TC2;
+  const int t0 = c * TC;
 
   if (t0 >= n) {
-    if (PASS == 1) {
-      float2* dst = a.part + ((size_t)head * a.n_chunks + c) * a.R_pad;
-      for (int r = tid; r < a.R_pad; r += NT) dst[r] = make_float2(-INFINITY, 0.f);
-    }
+    if (PASS == 1)
+      for (int r = tid; r < a.R_pad; r += NT)
+        a.part[((size_t)head * a.R_pad + r) * a.n_chunks + c] = make_float2(-INFINITY, 0.f);
     return;
   }
-  const int t1 = min(t0 + a.TC, n);
+  const int t1 = min(t0 + TC, n);
   const int ntiles = (t1 - t0 + TOK - 1) / TOK;
   const char* kh = static_cast<const char*>(a.k) + (size_t)head * a.N_max * ROWB;
   const int last_w0 = n - a.W;   // position of window row 0; row w sits at last_w0 + w
+  // Leading tiles whose every token exists and is visible to every row.
+  int clean_tiles = (t1 - t0) / TOK;
+  if (a.causal) clean_tiles = min(clean_tiles, max(0, (last_w0 + 1 - t0) / TOK));
+  const float cc = a.c;
 
   // Q fragments of this wave's row blocks (zero for padding rows).
   V qf[RBW][KS];
@@ -127,9 +142,20 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
     }
   }
 
-  // Pass-1 running state (per row owned by the lane) / pass-2 row lse2.
+  // Causal limits: p_row[i] = position of the lane's pass-1 row (row block i);
+  // rowpos[r] = window position (r mod W) of every row, for the pass-2 masks.
+  int p_row[RBW];
+#pragma unroll
+  for (int i = 0; i < RBW; ++i) {
+    const int r = (wave * RBW + i) * 32 + l32;
+    p_row[i] = a.causal ? last_w0 + (r % a.W) : 0x7fffffff;
+  }
+  if (PASS == 2 && a.causal)
+    for (int r = tid; r < NW * RBW * 32; r += NT) rowpos[r] = r % a.W;
+
+  // Pass-1 running state (per row owned by the lane) / pass-2 negated row lse2.
   float m_run[RBW], s_run[RBW];
-  float l2[RBW][16];
+  float nl2[RBW][16];
   if (PASS == 1) {
 #pragma unroll
     for (int i = 0; i < RBW; ++i) { m_run[i] = -INFINITY; s_run[i] = 0.f; }
@@ -139,7 +165,7 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = (wave * RBW + i) * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
-        l2[i][e] = r < a.R ? a.lse2[(size_t)head * a.R_pad + r] : INFINITY;
+        nl2[i][e] = r < a.R ? -a.lse2[(size_t)head * a.R_pad + r] : -INFINITY;
       }
     }
   }
@@ -148,14 +174,12 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
   auto gload = [&](int tile) {
     const int tt0 = t0 + tile * TOK;
     const int rows = min(TOK, t1 - tt0);
+    const char* base = kh + (size_t)tt0 * ROWB;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int v = tid + i * NT;
-      const int row = v / VPR, col = v % VPR;
-      if (v < TILE_VECS && row < rows)
-        pre[i] = ld16(kh + (size_t)(tt0 + row) * ROWB + col * 16);
-      else
-        pre[i] = make_uint4(0, 0, 0, 0);
+      const int row = v / VPR;
+      pre[i] = (v < TILE_VECS && row < rows) ? ld16(base + (size_t)v * 16) : make_uint4(0, 0, 0, 0);
     }
   };
   auto sstore = [&](int buf) {
@@ -169,99 +193,169 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
     }
   };
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  // ---- software pipeline over 32-token blocks j (two per 64-token tile) ----
+  // The two 32-row blocks of the wave alternate between the matrix core and
+  // the VALU: while the MFMAs of (block j, rows 0..31) run, the epilogue of
+  // (block j-1, rows 32..63) executes, and while (block j, rows 32..63)
+  // multiplies, (block j, rows 0..31) is finished.  Each MFMA is paired with
+  // an eighth of the other row block's epilogue; sched_barrier keeps the
+  // pairing, so the exp2 work hides under the MFMA pipe of the same wave.
+  static_assert(RBW == 2, "the pipeline alternates two row blocks");
+  V kf[KS];
+  f32x16 acc[RBW];
+  float col_cur = 0.f;                 // pass 2: column sum of the block in flight
+  // per-epilogue scratch (pass 1)
+  float e_nm = 0.f, e_sum = 0.f, e_mn = 0.f;
 
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
-    const int tt0 = t0 + tile * TOK;
-    if (tile + 1 < ntiles) gload(tile + 1);
-
+  auto load_k = [&](int buf, int sub) __attribute__((always_inline)) {
+    const unsigned char* krow = &ktile[buf][(sub * 32 + l32) * LDS_STRIDE + 8 * hf * sizeof(T)];
 #pragma unroll
-    for (int sub = 0; sub < TSUB; ++sub) {
-      const int ts = tt0 + sub * 32;   // first token of this 32-token block
-      f32x16 acc[RBW];
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = load_frag<T>(krow + ks * 16 * sizeof(T));
+  };
+  auto mma_step = [&](int i, int q) __attribute__((always_inline)) {
+    // q-th of 8 MFMA slots of row block i: k-steps [q*KS/8, (q+1)*KS/8)
 #pragma unroll
-      for (int i = 0; i < RBW; ++i) acc[i] = f32x16{};
-      const unsigned char* krow = &ktile[buf][(sub * 32 + l32) * LDS_STRIDE + 8 * hf * sizeof(T)];
+    for (int ks = q * KS / 8; ks < (q + 1) * KS / 8; ++ks) {
+      if (ks == 0)
+        acc[i] = PASS == 1 ? mma(kf[0], qf[i][0], f32x16{}) : mma(qf[i][0], kf[0], f32x16{});
+      else
+        acc[i] = PASS == 1 ? mma(kf[ks], qf[i][ks], acc[i]) : mma(qf[i][ks], kf[ks], acc[i]);
+    }
+  };
+  // q-th eighth of the epilogue of row block i for the block starting at token ts.
+  auto epi_step = [&](int i, int q, int ts, auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    if (PASS == 1) {
+      // acc[i][e] = dot(row (wave*RBW+i)*32 + l32, token ts + 8*(e/4) + 4*hf + e%4)
+      if (q == 0) {
+        if (MASKED) {
+          // token ts + off_e + 4*hf is kept iff off_e <= lim (off_e = 8*(e/4) + e%4)
+          const int lim = min(t1 - 1, p_row[i]) - ts - 4 * hf;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const V kf = load_frag<T>(krow + ks * 16 * sizeof(T));
-#pragma unroll
-        for (int i = 0; i < RBW; ++i)
-          acc[i] = PASS == 1 ? mma(kf, qf[i][ks], acc[i]) : mma(qf[i][ks], kf, acc[i]);
-      }
-
-      const bool clean = (ts + 32 <= t1) && (!a.causal || ts + 31 <= last_w0);
-      if (PASS == 1) {
-        // acc[i][e] = dot(row (wave*RBW+i)*32 + l32, token ts + 8*(e/4) + 4*hf + e%4)
-#pragma unroll
-        for (int i = 0; i < RBW; ++i) {
-          const int r = (wave * RBW + i) * 32 + l32;
-          float v[16];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) v[e] = acc[i][e];
-          if (!clean) {
-            const int p = a.causal ? last_w0 + (r % a.W) : 0x7fffffff;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int t = ts + 8 * (e >> 2) + 4 * hf + (e & 3);
-              if (t >= t1 || t > p) v[e] = -INFINITY;
-            }
-          }
-          float vmax = v[0];
-#pragma unroll
-          for (int e = 1; e < 16; ++e) vmax = fmaxf(vmax, v[e]);
-          const float mn = fmaxf(m_run[i], vmax * a.c);
-          if (mn != -INFINITY) {
-            float sum = 0.f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) sum += fast_exp2(fmaf(v[e], a.c, -mn));
-            s_run[i] = s_run[i] * fast_exp2(m_run[i] - mn) + sum;
-            m_run[i] = mn;
-          }
+          for (int e = 0; e < 16; ++e)
+            acc[i][e] = (8 * (e >> 2) + (e & 3)) > lim ? -INFINITY : acc[i][e];
         }
+        e_mn = fmaxf(fmaxf(acc[i][0], acc[i][1]), fmaxf(acc[i][2], acc[i][3]));
+        e_mn = fmaxf(e_mn, fmaxf(acc[i][4], acc[i][5]));
+        e_mn = fmaxf(e_mn, fmaxf(acc[i][6], acc[i][7]));
+      } else if (q == 1) {
+        e_mn = fmaxf(e_mn, fmaxf(acc[i][8], acc[i][9]));
+        e_mn = fmaxf(e_mn, fmaxf(acc[i][10], acc[i][11]));
+        e_mn = fmaxf(e_mn, fmaxf(acc[i][12], acc[i][13]));
+        e_mn = fmaxf(e_mn, fmaxf(acc[i][14], acc[i][15]));
+        e_mn = fmaxf(m_run[i], e_mn * cc);
+        // a fully masked row keeps (-inf, 0): exp2(-inf - 0) = 0 everywhere
+        e_nm = MASKED && e_mn == -INFINITY ? 0.f : -e_mn;
+        e_sum = 0.f;
       } else {
-        // acc[i][e] = dot(row (wave*RBW+i)*32 + 8*(e/4) + 4*hf + e%4, token ts + l32)
-        float col = 0.f;
-        if (!a.causal || ts + 31 <= last_w0) {
+        // slots 2..7 take 3,3,3,3,2,2 of the 16 exponentials
+        constexpr int lo_tab[9] = {0, 0, 0, 3, 6, 9, 12, 14, 16};
+        const int lo = lo_tab[q], hi = lo_tab[q + 1];
 #pragma unroll
-          for (int i = 0; i < RBW; ++i)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) col += fast_exp2(fmaf(acc[i][e], a.c, -l2[i][e]));
-        } else {
-          const int t = ts + l32;
-#pragma unroll
-          for (int i = 0; i < RBW; ++i)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int r = (wave * RBW + i) * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
-              const float x = fast_exp2(fmaf(acc[i][e], a.c, -l2[i][e]));
-              if (t <= last_w0 + (r % a.W)) col += x;
-            }
+        for (int e = lo; e < hi; ++e) e_sum += fast_exp2(fmaf(acc[i][e], cc, e_nm));
+        if (q == 7) {
+          s_run[i] = fmaf(s_run[i], fast_exp2(m_run[i] + e_nm), e_sum);
+          m_run[i] = e_mn;
         }
-        red[buf][wave * 2 + hf][sub * 32 + l32] = col;
+      }
+    } else {
+      // acc[i][e] = dot(row (wave*RBW+i)*32 + 8*(e/4) + 4*hf + e%4, token ts + l32)
+      // causal: the lane's token t sees row r iff t - last_w0 <= (r mod W), read from LDS
+      int2 wpos = make_int2(0, 0);
+      if (MASKED && a.causal)
+        wpos = *reinterpret_cast<const int2*>(
+            &rowpos[(wave * RBW + i) * 32 + 8 * (q >> 1) + 4 * hf + ((2 * q) & 3)]);
+#pragma unroll
+      for (int e = 2 * q; e < 2 * q + 2; ++e) {
+        const float x = fast_exp2(fmaf(acc[i][e], cc, nl2[i][e]));
+        if (MASKED && a.causal)
+          col_cur += ts + l32 - last_w0 <= (e == 2 * q ? wpos.x : wpos.y) ? x : 0.f;
+        else
+          col_cur += x;
       }
     }
-
-    if (tile + 1 < ntiles) sstore(buf ^ 1);
-    __syncthreads();
-
+  };
+  // One pipeline step: MFMAs of row block im (if any) paired with the
+  // epilogue of row block ie of the block at token ts (if any).
+  // (do_mma, im, do_epi, ie) are compile-time tags so acc[] stays in registers.
+  auto step = [&](auto do_mma, auto im, auto do_epi, auto ie, int ts, auto masked_tag)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if constexpr (decltype(do_mma)::value) mma_step(decltype(im)::value, q);
+      if constexpr (decltype(do_epi)::value) epi_step(decltype(ie)::value, q, ts, masked_tag);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  auto step_m = [&](auto do_mma, auto im, auto do_epi, auto ie, int ts, bool masked)
+      __attribute__((always_inline)) {
+    if (masked) step(do_mma, im, do_epi, ie, ts, T_{});
+    else step(do_mma, im, do_epi, ie, ts, F_{});
+  };
+  auto emit_col = [&](int tile, int sub) __attribute__((always_inline)) {   // pass 2: block column sums -> LDS
+    if (PASS == 2) {
+      const float c2 = col_cur + __shfl_xor(col_cur, 32, WAVE);   // other half-wave's rows
+      if (hf == 0) red[tile % 3][wave][sub * 32 + l32] = c2;
+      col_cur = 0.f;
+    }
+  };
+  auto reduce_tile = [&](int tile) {
     if (PASS == 2 && tid < TOK) {
-      const int t = tt0 + tid;
+      const int t = t0 + tile * TOK + tid;
       if (t < t1) {
         float s = 0.f;
 #pragma unroll
-        for (int w2 = 0; w2 < NRED; ++w2) s += red[buf][w2][tid];
+        for (int w2 = 0; w2 < NW; ++w2) s += red[tile % 3][w2][tid];
         a.scores[(size_t)head * a.N_max + t] = s;
       }
     }
+  };
+  auto masked_tile = [&](int tile) { return tile >= clean_tiles; };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  if (ntiles > 1) gload(1);
+  // tile 0
+  load_k(0, 0);
+  step_m(T_{}, I0{}, F_{}, I1{}, 0, false);                     // MMA(0, r0)
+  step_m(T_{}, I1{}, T_{}, I0{}, t0, masked_tile(0));           // MMA(0, r1) | epi(0, r0)
+  load_k(0, 1);
+  step_m(T_{}, I0{}, T_{}, I1{}, t0, masked_tile(0));           // MMA(1, r0) | epi(0, r1)
+  emit_col(0, 0);
+  step_m(T_{}, I1{}, T_{}, I0{}, t0 + 32, masked_tile(0));      // MMA(1, r1) | epi(1, r0)
+  if (ntiles > 1) sstore(1);
+  __syncthreads();
+  for (int tile = 1; tile < ntiles; ++tile) {
+    const int buf = tile & 1;
+    const int tt0 = t0 + tile * TOK;
+    if (tile + 1 < ntiles) gload(tile + 1);
+    load_k(buf, 0);
+    step_m(T_{}, I0{}, T_{}, I1{}, tt0 - 32, masked_tile(tile - 1));  // MMA(2t, r0) | epi(2t-1, r1)
+    emit_col(tile - 1, 1);
+    step_m(T_{}, I1{}, T_{}, I0{}, tt0, masked_tile(tile));           // MMA(2t, r1) | epi(2t, r0)
+    load_k(buf, 1);
+    step_m(T_{}, I0{}, T_{}, I1{}, tt0, masked_tile(tile));           // MMA(2t+1, r0) | epi(2t, r1)
+    emit_col(tile, 0);
+    step_m(T_{}, I1{}, T_{}, I0{}, tt0 + 32, masked_tile(tile));      // MMA(2t+1, r1) | epi(2t+1, r0)
+    if (tile + 1 < ntiles) sstore((tile + 1) & 1);
+    __syncthreads();
+    reduce_tile(tile - 1);
+  }
+  // drain: the last block's second row block
+  step_m(F_{}, I0{}, T_{}, I1{}, t0 + (ntiles - 1) * TOK + 32, masked_tile(ntiles - 1));
+  emit_col(ntiles - 1, 1);
+  if (PASS == 2) {
+    __syncthreads();
+    reduce_tile(ntiles - 1);
   }
 
   if (PASS == 1) {
     // Merge the two half-waves (same row, disjoint tokens), then publish.
-    float2* dst = a.part + ((size_t)head * a.n_chunks + c) * a.R_pad;
 #pragma unroll
     for (int i = 0; i < RBW; ++i) {
       const float mo = __shfl_xor(m_run[i], 32, WAVE);
@@ -270,30 +364,49 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
       float s = 0.f;
       if (mn != -INFINITY) s = s_run[i] * fast_exp2(m_run[i] - mn) + so * fast_exp2(mo - mn);
       const int r = (wave * RBW + i) * 32 + l32;
-      if (hf == 0 && r < a.R_pad) dst[r] = make_float2(mn, s);
+      if (hf == 0 && r < a.R_pad)
+        a.part[((size_t)head * a.R_pad + r) * a.n_chunks + c] = make_float2(mn, s);
     }
   }
 }
 
-// Fold the per-chunk (max, sum) of every row, in chunk order, into lse2.
-__global__ __launch_bounds__(256) void score_lse(ScoreArgs a) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  const int total = a.B * a.Hkv * a.R_pad;
-  if (idx >= total) return;
-  const int head = idx / a.R_pad, r = idx % a.R_pad;
-  if (r >= a.R) { a.lse2[idx] = INFINITY; return; }
-  float m = -INFINITY, s = 0.f;
-  const float2* src = a.part + (size_t)head * a.n_chunks * a.R_pad + r;
-  for (int c = 0; c < a.n_chunks; ++c) {
-    const float2 p = src[(size_t)c * a.R_pad];
-    if (p.x == -INFINITY) continue;
-    const float mn = fmaxf(m, p.x);
-    s = s * exp2f(m - mn) + p.y * exp2f(p.x - mn);
-    m = mn;
+__device__ __forceinline__ void merge(float& m, float& s, float pm, float ps) {
+  const float mn = fmaxf(m, pm);
+  if (mn == -INFINITY) return;
+  s = s * exp2f(m - mn) + ps * exp2f(pm - mn);
+  m = mn;
+}
+
+// One wave per row: lanes merge chunks c = lane, lane+64, ... in order, then a
+// fixed butterfly merges the lanes; deterministic for fixed sizes.
+__global__ __launch_bounds__(256) void score_fold(ScoreArgs a) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int row_id = blockIdx.x * 4 + threadIdx.x / WAVE;
+  if (row_id >= a.B * a.Hkv * a.R_pad) return;
+  const int head = row_id / a.R_pad, r = row_id % a.R_pad;
+  if (r >= a.R) {
+    if (lane == 0) a.lse2[row_id] = INFINITY;
+    return;
   }
+  const float2* src = a.part + (size_t)row_id * a.n_chunks;
+  float m = -INFINITY, s = 0.f;
+  for (int c = lane; c < a.n_chunks; c += WAVE) {
+    const float2 p = src[c];
+    merge(m, s, p.x, p.y);
+  }
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    const float pm = __shfl_xor(m, o, WAVE), ps = __shfl_xor(s, o, WAVE);
+    // both partners compute the same merge in the same operand order
+    const bool lower = (lane & o) == 0;
+    float m1 = lower ? m : pm, s1 = lower ? s : ps;
+    merge(m1, s1, lower ? pm : m, lower ? ps : s);
+    m = m1; s = s1;
+  }
+  if (lane != 0) return;
   const bool seen = s > 0.f;
   const float l2v = seen ? m + log2f(s) : INFINITY;
-  a.lse2[idx] = l2v;
+  a.lse2[row_id] = l2v;
   if (a.row_lse) {
     const int b = head / a.Hkv, h = head % a.Hkv;
     const int j = h * a.G + r / a.W, w = r % a.W;
@@ -305,6 +418,20 @@ struct ScorePlan {
   int G, R, R_pad, NW, TC, n_chunks;
   size_t off_lse, bytes;
 };
+
+// Tokens per workgroup: the tile count per chunk (at least `min_tiles`) that
+// minimises rounds * tiles-per-chunk when `slots` workgroups are resident,
+// i.e. the fewest tile-times for the whole grid; ties go to bigger chunks.
+int chunk_tokens(int64_t heads, int N_max, int64_t slots, int min_tiles) {
+  const int64_t tiles = ceil_div64(N_max, TOK);
+  int64_t best = tiles, best_cost = INT64_MAX;
+  for (int64_t tpc = std::min<int64_t>(min_tiles, tiles); tpc <= tiles; ++tpc) {
+    const int64_t wgs = heads * ceil_div64(tiles, tpc);
+    const int64_t cost = ceil_div64(wgs, slots) * tpc;
+    if (cost <= best_cost) { best_cost = cost; best = tpc; }
+  }
+  return (int)(best * TOK);
+}
 
 bool plan_score(int B, int Hq, int Hkv, int N_max, int W, int d, ScorePlan* p) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || N_max < 1 || W < 1 || W > N_max) return false;
@@ -318,15 +445,9 @@ bool plan_score(int B, int Hq, int Hkv, int N_max, int W, int d, ScorePlan* p) {
   p->R_pad = RB * 32;
   const int nw = ceil_div(RB, RBW);
   p->NW = nw <= 1 ? 1 : nw <= 2 ? 2 : nw <= 4 ? 4 : nw <= 8 ? 8 : 16;
-  // Aim at ~2048 workgroups over the whole call; chunks are whole tiles.
-  const int64_t total = (int64_t)B * Hkv * N_max;
-  int64_t tc = ceil_div64(total, 2048);
-  tc = ceil_div64(tc, TOK) * TOK;
-  if (tc < 256) tc = 256;
-  if (tc > 8192) tc = 8192;
-  const int64_t nmax_r = ceil_div64(N_max, TOK) * TOK;
-  if (tc > nmax_r) tc = nmax_r;
-  p->TC = (int)tc;
+  // Pass-1 chunking depends on the sizes only, so the merge order (and the
+  // result, bit for bit) does not depend on the device.
+  p->TC = chunk_tokens((int64_t)B * Hkv, N_max, SLOTS_1, 4);
   p->n_chunks = ceil_div(N_max, p->TC);
   const size_t part = (size_t)B * Hkv * p->n_chunks * p->R_pad * sizeof(float2);
   p->off_lse = (part + 255) & ~size_t(255);
@@ -334,21 +455,38 @@ bool plan_score(int B, int Hq, int Hkv, int N_max, int W, int d, ScorePlan* p) {
   return true;
 }
 
+// Resident workgroups of a kernel on the current device (cached per kernel).
+template <typename K>
+int64_t resident_slots(K kernel, int threads, int* cache) {
+  if (*cache > 0) return *cache;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+      cus < 1 || per_cu < 1)
+    return SLOTS_1;
+  *cache = cus * per_cu;
+  return *cache;
+}
+
 template <typename T, int D, int NW>
-void launch_score(const ScoreArgs& a, hipStream_t st) {
-  const dim3 grid(a.n_chunks, a.Hkv, a.B);
+void launch_score(ScoreArgs a, hipStream_t st) {
+  static int slots2 = 0;
+  a.TC2 = chunk_tokens((int64_t)a.B * a.Hkv, a.N_max,
+                       resident_slots(score_pass<T, D, NW, 2>, NW * WAVE, &slots2), 4);
+  a.n_chunks2 = ceil_div(a.N_max, a.TC2);
   {
     TimedLaunch t("score_rowstats", st);
-    score_pass<T, D, NW, 1><<<grid, NW * WAVE, 0, st>>>(a);
+    score_pass<T, D, NW, 1><<<dim3(a.n_chunks, a.Hkv, a.B), NW * WAVE, 0, st>>>(a);
   }
   {
-    TimedLaunch t("score_lse", st);
+    TimedLaunch t("score_fold", st);
     const int rows = a.B * a.Hkv * a.R_pad;
-    score_lse<<<ceil_div(rows, 256), 256, 0, st>>>(a);
+    score_fold<<<ceil_div(rows, 4), 256, 0, st>>>(a);
   }
   {
     TimedLaunch t("score_colsum", st);
-    score_pass<T, D, NW, 2><<<grid, NW * WAVE, 0, st>>>(a);
+    score_pass<T, D, NW, 2><<<dim3(a.n_chunks2, a.Hkv, a.B), NW * WAVE, 0, st>>>(a);
   }
 }
 
@@ -393,6 +531,7 @@ extern "C" int kv_score(const void* q_win, const void* k, const int32_t* ctx_len
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_lse);
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N_max = N_max; a.W = W; a.G = p.G;
   a.R = p.R; a.R_pad = p.R_pad; a.TC = p.TC; a.n_chunks = p.n_chunks;
+  a.TC2 = p.TC; a.n_chunks2 = p.n_chunks;
   a.causal = causal ? 1 : 0;
   a.c = (float)((scale > 0.f ? (double)scale : 1.0 / sqrt((double)d)) * LOG2E_D);
 

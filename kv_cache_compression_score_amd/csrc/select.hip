@@ -88,16 +88,47 @@ struct Keys {
   }
 };
 
+// Top key bits shared by every token of the head (min/max reduction): the
+// digit passes start below them, so the first histogram spreads over the
+// bits that actually vary.
+template <class KF>
+__device__ int common_prefix(const KF& key, int n, Smem& sm, uint32_t* lo_key) {
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  for (int t = tid; t < n; t += NT) {
+    const uint32_t kk = key(t);
+    mn = min(mn, kk);
+    mx = max(mx, kk);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, WAVE));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, WAVE));
+  }
+  if (lane == 0) { sm.wcnt_gt[wave] = mn; sm.wcnt_eq[wave] = mx; }
+  __syncthreads();
+  mn = 0xffffffffu; mx = 0u;
+  for (int w = 0; w < NWV; ++w) { mn = min(mn, sm.wcnt_gt[w]); mx = max(mx, sm.wcnt_eq[w]); }
+  __syncthreads();
+  *lo_key = mn;
+  return mn == mx ? 32 : __clz(mn ^ mx);
+}
+
 // Radix descent for the k-th key (1 <= k <= n).  Returns T; *quota = number
 // of tokens with key == T that are kept.
 template <class KF>
-__device__ uint32_t kth_key(const KF& key, int n, int k, Smem& sm, uint32_t* quota) {
-  uint32_t prefix = 0, pmask = 0, rem = (uint32_t)k;
+__device__ uint32_t kth_key(const KF& key, int n, int k, int cp, uint32_t lo_key, Smem& sm,
+                            uint32_t* quota) {
+  if (cp >= 32) { *quota = (uint32_t)k; return lo_key; }   // every key equal
+  uint32_t pmask = cp == 0 ? 0u : ~0u << (32 - cp);
+  uint32_t prefix = lo_key & pmask, rem = (uint32_t)k;
   const int tid = threadIdx.x;
+  int left = 32 - cp;
 #pragma unroll 1
-  for (int p = 0; p < 3; ++p) {
-    const int shift = p == 0 ? 21 : p == 1 ? 10 : 0;
-    const int nb = p == 2 ? 1024 : 2048;
+  while (left > 0) {
+    const int bits = min(11, left);
+    const int shift = left - bits;
+    const int nb = 1 << bits;
     for (int i = tid; i < nb; i += NT) sm.hist[i] = 0;
     __syncthreads();
     for (int t = tid; t < n; t += NT) {
@@ -119,6 +150,7 @@ __device__ uint32_t kth_key(const KF& key, int n, int k, Smem& sm, uint32_t* quo
     rem -= sm.cnt_above;
     prefix |= sm.bin << shift;
     pmask |= (uint32_t)(nb - 1) << shift;
+    left -= bits;
     __syncthreads();
   }
   *quota = rem;
@@ -128,7 +160,7 @@ __device__ uint32_t kth_key(const KF& key, int n, int k, Smem& sm, uint32_t* quo
 // Mass budget: fewest top tokens whose fixed-point score sum reaches
 // ceil(f * total).  Returns k >= 1 (before clamping).
 template <class KF>
-__device__ int mass_count(const KF& key, int n, float f, Smem& sm) {
+__device__ int mass_count(const KF& key, int n, float f, int cp, uint32_t lo_key, Smem& sm) {
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   // exponent of the total (fixed-order fp64 reduction; only picks F)
   double part = 0.0;
@@ -160,12 +192,15 @@ __device__ int mass_count(const KF& key, int n, float f, Smem& sm) {
   if (target > tot_fx) target = tot_fx;   // double rounding of f * total
   if (target == 0) return 1;
 
-  uint32_t prefix = 0, pmask = 0, cnt_above = 0;
+  uint32_t pmask = cp == 0 ? 0u : (cp >= 32 ? ~0u : ~0u << (32 - cp));
+  uint32_t prefix = lo_key & pmask, cnt_above = 0;
   unsigned long long rem = target;
+  int left = cp >= 32 ? 0 : 32 - cp;
 #pragma unroll 1
-  for (int p = 0; p < 3; ++p) {
-    const int shift = p == 0 ? 21 : p == 1 ? 10 : 0;
-    const int nb = p == 2 ? 1024 : 2048;
+  while (left > 0) {
+    const int bits = min(11, left);
+    const int shift = left - bits;
+    const int nb = 1 << bits;
     for (int i = tid; i < nb; i += NT) { sm.hist[i] = 0; sm.hmass[i] = 0; }
     __syncthreads();
     for (int t = tid; t < n; t += NT) {
@@ -194,6 +229,7 @@ __device__ int mass_count(const KF& key, int n, float f, Smem& sm) {
     cnt_above += sm.cnt_above;
     prefix |= sm.bin << shift;
     pmask |= (uint32_t)(nb - 1) << shift;
+    left -= bits;
     __syncthreads();
   }
   const unsigned long long fv = fx(prefix);   // > 0: the bin holds mass
@@ -214,7 +250,27 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   }
   const float* src = a.scores + (size_t)head * a.N_max;
   if (IN_LDS) {
-    for (int t = tid; t < n; t += NT) keys_lds[t] = to_key(src[t]);
+    // 16-byte loads, all in flight before the first LDS store.
+    constexpr int PER = LDS_KEYS / 4 / NT;
+    const int n4 = ((a.N_max & 3) == 0) ? n >> 2 : 0;
+    const float4* src4 = reinterpret_cast<const float4*>(src);
+    float4 v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + u * NT;
+      v[u] = i < n4 ? src4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + u * NT;
+      if (i < n4) {
+        keys_lds[4 * i + 0] = to_key(v[u].x);
+        keys_lds[4 * i + 1] = to_key(v[u].y);
+        keys_lds[4 * i + 2] = to_key(v[u].z);
+        keys_lds[4 * i + 3] = to_key(v[u].w);
+      }
+    }
+    for (int t = 4 * n4 + tid; t < n; t += NT) keys_lds[t] = to_key(src[t]);
     __syncthreads();
   }
   Keys<IN_LDS> key{keys_lds, src};
@@ -227,7 +283,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   lo = max(lo, 1);
   hi = min(max(hi, 1), n);
   lo = min(lo, hi);
-  int k;
+  int k = 1;
   if (bu.mode == KV_BUDGET_K) {
     k = bu.k ? bu.k[head] : bu.k_scalar;
     k = min(max(k, 1), n);
@@ -247,13 +303,16 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     for (int w = 0; w < NWV; ++w) tot += sm.wcnt_gt[w];
     __syncthreads();
     k = min(max((int)tot, lo), hi);
-  } else {
-    k = mass_count(key, n, bu.mass, sm);
+  }
+  uint32_t lo_key;
+  const int cp = common_prefix(key, n, sm, &lo_key);
+  if (bu.mode == KV_BUDGET_MASS) {
+    k = mass_count(key, n, bu.mass, cp, lo_key, sm);
     k = min(max(k, lo), hi);
   }
 
   uint32_t quota;
-  const uint32_t T = kth_key(key, n, k, sm, &quota);
+  const uint32_t T = kth_key(key, n, k, cp, lo_key, sm, &quota);
 
   // Emit.  Wave w owns tokens [w*seg, min((w+1)*seg, n)), seg a multiple of 64.
   const int seg = ((n + NWV - 1) / NWV + WAVE - 1) / WAVE * WAVE;

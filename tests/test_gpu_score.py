@@ -51,7 +51,8 @@ def test_score_sum_invariant_and_determinism():
     s1, _ = api.kv_score(q, k, c)
     s2, _ = api.kv_score(q, k, c)
     torch.cuda.synchronize()
-    assert torch.equal(s1, s2)
+    for b, n in enumerate([3000, 1111]):     # entries t >= n are not written
+        assert torch.equal(s1[b, :, :n], s2[b, :, :n])
     for b, n in enumerate([3000, 1111]):
         tot = s1[b, :, :n].double().sum(dim=1).cpu().numpy()
         np.testing.assert_allclose(tot, 64 * 4, rtol=1e-4)

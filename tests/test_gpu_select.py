@@ -98,14 +98,25 @@ def test_select_threshold(kind, shape):
         compare_sets(idx_g, cnt_g, idx_r, cnt_r)
 
 
-def mass_bracket_ok(s_head, k_g, f):
-    """k_g brackets f * C(n) within 1e-12 * C(n): C(k_g - 1) < f*C + band <= C(k_g) + 2*band."""
+def mass_count_ok(s_head, k_g, f, lo, hi):
+    """A GPU count that differs from the oracle's is accepted only if it is the
+    clamp of a count that brackets f * C(n) to within 1e-12 * C(n) on the
+    oracle's float64 sums, C(k) the sum of the k largest scores."""
     c = np.cumsum(s_head[orc.total_order(s_head)])
     target = float(np.float32(f)) * c[-1]
     band = 1e-12 * c[-1]
-    lo_ok = k_g == 1 or c[k_g - 2] < target + band
-    hi_ok = c[k_g - 1] >= target - band
-    return lo_ok and hi_ok
+    n = len(s_head)
+    k_lo = max(1, int(np.floor(np.float32(lo) * n + 0.5)))
+    k_hi = min(n, max(1, int(np.floor(np.float32(hi) * n + 0.5))))
+    reaches = lambda k: c[k - 1] >= target - band          # C(k) reaches the target
+    short = lambda k: k == 1 or c[k - 2] < target + band   # C(k-1) does not (within band)
+    if k_lo < k_g < k_hi:
+        return reaches(k_g) and short(k_g)
+    if k_g == k_hi:
+        return short(k_g)          # the crossing lies at or beyond the upper clamp
+    if k_g == k_lo:
+        return reaches(k_g)        # the crossing lies at or below the lower clamp
+    return False
 
 
 @pytest.mark.parametrize("kind", ["ties", "heavy", "uniform"])
@@ -122,12 +133,9 @@ def test_select_mass(kind, shape):
                 i = bb * Hkv + h
                 kg, kr = int(cnt_g[i]), int(cnt_r[i])
                 if kg != kr:
-                    # unclamped counts may differ only where the mass boundary
-                    # is flat to within 1e-12 of the head's total
                     n = ctx[bb]
-                    k_un = kg if lo * n < kg < hi * n else None
-                    assert k_un is not None and \
-                        mass_bracket_ok(s[bb, h, :n].astype(np.float64), kg, f), (bb, h, kg, kr)
+                    assert mass_count_ok(s[bb, h, :n].astype(np.float64), kg, f, lo, hi), \
+                        (bb, h, kg, kr)
                 ref = np.sort(orc.total_order(s[bb, h, :ctx[bb]].astype(np.float64))[:kg])
                 assert np.array_equal(idx_g[bb, h, :kg], ref), (bb, h)
 

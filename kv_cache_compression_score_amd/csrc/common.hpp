@@ -84,6 +84,56 @@ __device__ __forceinline__ I wave_incl_scan(I v) {
   return v;
 }
 
+// Set lanes of a wave-wide mask below the calling lane (v_mbcnt).
+__device__ __forceinline__ uint32_t mbcnt(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Inclusive scans over a wave's 64 lanes with DPP moves: shifts by 1, 2, 4
+// and 8 inside each 16-lane row, then lane 15 broadcast into rows 1 and 3
+// and lane 31 into rows 2 and 3.  Lanes a move cannot source keep `id`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t id, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROWS, 0xf, false);
+}
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t x, uint32_t id, Op op) {
+  x = op(x, dpp_mov<0x111, 0xf>(id, x));
+  x = op(x, dpp_mov<0x112, 0xf>(id, x));
+  x = op(x, dpp_mov<0x114, 0xf>(id, x));
+  x = op(x, dpp_mov<0x118, 0xf>(id, x));
+  x = op(x, dpp_mov<0x142, 0xa>(id, x));
+  x = op(x, dpp_mov<0x143, 0xc>(id, x));
+  return x;
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_add_step(uint64_t x) {
+  const uint32_t lo = dpp_mov<CTRL, ROWS>(0u, (uint32_t)x);
+  const uint32_t hi = dpp_mov<CTRL, ROWS>(0u, (uint32_t)(x >> 32));
+  return x + (((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ uint64_t wave_scan_add_u64(uint64_t x) {
+  x = dpp_add_step<0x111, 0xf>(x);
+  x = dpp_add_step<0x112, 0xf>(x);
+  x = dpp_add_step<0x114, 0xf>(x);
+  x = dpp_add_step<0x118, 0xf>(x);
+  x = dpp_add_step<0x142, 0xa>(x);
+  x = dpp_add_step<0x143, 0xc>(x);
+  return x;
+}
+struct OpAdd { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+struct OpMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
+struct OpMax { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
+
+// Value of lane 63 (the total of an inclusive scan), wave-uniform.
+__device__ __forceinline__ uint32_t last_lane(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, WAVE - 1);
+}
+__device__ __forceinline__ uint64_t last_lane(uint64_t v) {
+  return ((uint64_t)last_lane((uint32_t)(v >> 32)) << 32) | last_lane((uint32_t)v);
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & (WAVE - 1);
   return lane == 0 ? 0ull : (~0ull >> (WAVE - lane));

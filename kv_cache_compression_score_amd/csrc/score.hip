@@ -38,7 +38,7 @@ namespace {
 constexpr int TOK = 64;          // tokens per LDS tile
 constexpr int TSUB = TOK / 32;   // 32-token MFMA blocks per tile
 constexpr int RBW = 2;           // 32-row blocks per wave
-constexpr int SLOTS_1 = 256 * 3; // pass-1 chunking target: resident workgroups on 256 CUs
+constexpr int SLOTS_1 = 256 * 2; // pass-1 chunking target: resident workgroups on 256 CUs
 
 template <typename T> struct FragT;
 template <> struct FragT<__bf16> { using vec = bf16x8; };   // 8 elements = 16 B
@@ -126,19 +126,19 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
   const float cc = a.c;
 
   // Q fragments of this wave's row blocks (zero for padding rows).
+  // Loads are branch-free (clamped row, then a select) so they all issue at once.
   V qf[RBW][KS];
 #pragma unroll
   for (int i = 0; i < RBW; ++i) {
     const int r = (wave * RBW + i) * 32 + l32;
-    if (r < a.R) {
-      const int j = h * a.G + r / a.W, w = r % a.W;
-      const char* qp = static_cast<const char*>(a.q) +
-                       ((((size_t)b * a.Hq + j) * a.W + w) * D + 8 * hf) * sizeof(T);
+    const int rc = min(r, a.R - 1);
+    const int j = h * a.G + rc / a.W, w = rc % a.W;
+    const char* qp = static_cast<const char*>(a.q) +
+                     ((((size_t)b * a.Hq + j) * a.W + w) * D + 8 * hf) * sizeof(T);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[i][ks] = load_frag<T>(qp + ks * 16 * sizeof(T));
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[i][ks] = V{};
+    for (int ks = 0; ks < KS; ++ks) {
+      const V v = load_frag<T>(qp + ks * 16 * sizeof(T));
+      qf[i][ks] = r < a.R ? v : V{};
     }
   }
 
@@ -165,7 +165,8 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = (wave * RBW + i) * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
-        nl2[i][e] = r < a.R ? -a.lse2[(size_t)head * a.R_pad + r] : -INFINITY;
+        const float v = a.lse2[(size_t)head * a.R_pad + min(r, a.R_pad - 1)];
+        nl2[i][e] = r < a.R ? -v : -INFINITY;
       }
     }
   }

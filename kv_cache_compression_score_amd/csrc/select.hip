@@ -11,15 +11,20 @@
 // One 1024-thread workgroup owns one (sequence, KV head).  Scores become
 // order-preserving uint32 keys (-0.0 folded onto +0.0).  The k-th key T of
 // the order "higher score first, lower index first among equals" is found by
-// three digit passes (11 + 11 + 10 bits) of LDS histograms; the keep rule is
-// then key > T, or key == T and among the first q such tokens.  The emit is
-// two sweeps over wave-contiguous token segments with ballot/popcount
-// prefixes, so indices come out ascending.  Heads of up to 32768 tokens keep
-// their keys in LDS; longer heads re-read the scores from global memory.
+// a radix descent over the key bits below the prefix every token shares
+// (min/max from the staging pass), 11 bits per digit: all waves build an LDS
+// histogram, then every thread takes two bins (descending), a DPP wave scan
+// and the sixteen wave totals locate the digit, and each owner clears its
+// bins for the next digit.  Sweeps over LDS-resident keys read four
+// consecutive keys per lane.  The keep rule is key > T, or key == T and among
+// the first q such tokens; the emit walks wave-contiguous token segments with
+// ballot/mbcnt prefixes, so indices come out ascending.  Heads of up to 32768
+// tokens keep their keys in LDS (and a wave's segment in registers for the
+// emit); longer heads re-read the scores.
 //
 // The mass budget sums scores in 64-bit fixed point (scale 2^F with F picked
 // from the head's total so the sum stays below 2^62), which makes every
-// histogram sum exact and order independent.
+// histogram sum exact and independent of the order of the atomic adds.
 #include <math.h>
 
 #include "common.hpp"
@@ -31,6 +36,7 @@ constexpr int NT = 1024;
 constexpr int NWV = NT / WAVE;
 constexpr int LDS_KEYS = 32768;
 constexpr int NBINS = 2048;
+constexpr int DIGIT = 11;
 
 struct SelectArgs {
   const float* scores;
@@ -53,31 +59,14 @@ __device__ __forceinline__ float from_key(uint32_t k) {
 struct Smem {
   uint32_t hist[NBINS];
   unsigned long long hmass[NBINS];
-  unsigned long long wtot[NWV];
-  double wsum[NWV];
-  uint32_t wcnt_gt[NWV], wcnt_eq[NWV], keep_before[NWV], eq_before[NWV];
+  uint32_t w_min[NWV], w_max[NWV], w_cnt[NWV], w_gt[NWV], w_eq[NWV];
+  double w_sum[NWV];
+  unsigned long long w_fx[NWV];
+  unsigned long long f_m[NWV];   // bin search: per-wave totals
+  uint32_t f_c[NWV];
   uint32_t bin, cnt_above;
   unsigned long long mass_above;
-  int found;
 };
-
-// Exclusive prefix over the 1024 threads (block order); wtot is scratch.
-template <typename I>
-__device__ I block_excl_scan(I v, unsigned long long* wtot) {
-  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
-  const I inc = wave_incl_scan<I>(v);
-  if (lane == WAVE - 1) wtot[wave] = (unsigned long long)inc;
-  __syncthreads();
-  if (wave == 0) {
-    const I x = lane < NWV ? (I)wtot[lane] : (I)0;
-    const I xi = wave_incl_scan<I>(x);
-    if (lane < NWV) wtot[lane] = (unsigned long long)(xi - x);
-  }
-  __syncthreads();
-  const I r = inc - v + (I)wtot[wave];
-  __syncthreads();
-  return r;
-}
 
 template <bool IN_LDS>
 struct Keys {
@@ -88,158 +77,122 @@ struct Keys {
   }
 };
 
-// Top key bits shared by every token of the head (min/max reduction): the
-// digit passes start below them, so the first histogram spreads over the
-// bits that actually vary.
-template <class KF>
-__device__ int common_prefix(const KF& key, int n, Smem& sm, uint32_t* lo_key) {
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
-  uint32_t mn = 0xffffffffu, mx = 0u;
-  for (int t = tid; t < n; t += NT) {
-    const uint32_t kk = key(t);
-    mn = min(mn, kk);
-    mx = max(mx, kk);
-  }
+template <typename I>
+__device__ __forceinline__ I wave_sum_i(I v) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, WAVE));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, WAVE));
-  }
-  if (lane == 0) { sm.wcnt_gt[wave] = mn; sm.wcnt_eq[wave] = mx; }
-  __syncthreads();
-  mn = 0xffffffffu; mx = 0u;
-  for (int w = 0; w < NWV; ++w) { mn = min(mn, sm.wcnt_gt[w]); mx = max(mx, sm.wcnt_eq[w]); }
-  __syncthreads();
-  *lo_key = mn;
-  return mn == mx ? 32 : __clz(mn ^ mx);
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
 }
 
-// Radix descent for the k-th key (1 <= k <= n).  Returns T; *quota = number
-// of tokens with key == T that are kept.
-template <class KF>
-__device__ uint32_t kth_key(const KF& key, int n, int k, int cp, uint32_t lo_key, Smem& sm,
-                            uint32_t* quota) {
-  if (cp >= 32) { *quota = (uint32_t)k; return lo_key; }   // every key equal
-  uint32_t pmask = cp == 0 ? 0u : ~0u << (32 - cp);
-  uint32_t prefix = lo_key & pmask, rem = (uint32_t)k;
+// Apply f to every key of the head.  With the keys in LDS a lane takes four
+// consecutive keys per step (one 16-byte read).
+template <bool IN_LDS, class F>
+__device__ __forceinline__ void for_keys(const Keys<IN_LDS>& key, int n, const F& f) {
   const int tid = threadIdx.x;
-  int left = 32 - cp;
-#pragma unroll 1
-  while (left > 0) {
-    const int bits = min(11, left);
-    const int shift = left - bits;
-    const int nb = 1 << bits;
-    for (int i = tid; i < nb; i += NT) sm.hist[i] = 0;
-    __syncthreads();
-    for (int t = tid; t < n; t += NT) {
-      const uint32_t kk = key(t);
-      if ((kk & pmask) == prefix) atomicAdd(&sm.hist[(kk >> shift) & (nb - 1)], 1u);
+  if (IN_LDS) {
+    constexpr int PER = LDS_KEYS / 4 / NT;   // n <= LDS_KEYS
+    const int n4 = n >> 2;
+    const uint4* k4 = reinterpret_cast<const uint4*>(key.lds);
+    uint4 v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + u * NT;
+      v[u] = i < n4 ? k4[i] : make_uint4(0u, 0u, 0u, 0u);
     }
-    __syncthreads();
-    // positions in descending bin order: thread owns positions 2*tid, 2*tid+1
-    const int p0 = 2 * tid, p1 = 2 * tid + 1;
-    const uint32_t h0 = p0 < nb ? sm.hist[nb - 1 - p0] : 0u;
-    const uint32_t h1 = p1 < nb ? sm.hist[nb - 1 - p1] : 0u;
-    const uint32_t above = block_excl_scan<uint32_t>(h0 + h1, sm.wtot);
-    if (p0 < nb && above < rem && rem <= above + h0) {
-      sm.bin = (uint32_t)(nb - 1 - p0); sm.cnt_above = above;
-    } else if (p1 < nb && above + h0 < rem && rem <= above + h0 + h1) {
-      sm.bin = (uint32_t)(nb - 1 - p1); sm.cnt_above = above + h0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      if (tid + u * NT < n4) { f(v[u].x); f(v[u].y); f(v[u].z); f(v[u].w); }
     }
-    __syncthreads();
-    rem -= sm.cnt_above;
-    prefix |= sm.bin << shift;
-    pmask |= (uint32_t)(nb - 1) << shift;
-    left -= bits;
-    __syncthreads();
+    for (int t = 4 * n4 + tid; t < n; t += NT) f(key.lds[t]);
+  } else {
+    for (int t = tid; t < n; t += NT) f(key(t));
   }
-  *quota = rem;
-  return prefix;
 }
 
-// Mass budget: fewest top tokens whose fixed-point score sum reaches
-// ceil(f * total).  Returns k >= 1 (before clamping).
-template <class KF>
-__device__ int mass_count(const KF& key, int n, float f, int cp, uint32_t lo_key, Smem& sm) {
+// Radix descent.  Without MASS: the k-th key T (rem = k, 1 <= k <= n) and,
+// in *rem_out, the quota of keys equal to T that are kept.  With MASS: the
+// key T at which the top-down fixed-point mass reaches rem, the count of
+// keys above it and the mass still missing at T.
+// On entry sm.hist (and, with MASS, sm.hmass) are zero; on exit too.  The
+// sm.bin/cnt_above/mass_above reads of one digit all precede the next
+// digit's first barrier, so one set of fields serves every digit.
+template <bool MASS, bool IN_LDS, class FX>
+__device__ uint32_t descend(const Keys<IN_LDS>& key, int n, int cp, uint32_t lo_key,
+                            unsigned long long rem, Smem& sm, const FX& fx,
+                            uint32_t* cnt_above_out, unsigned long long* rem_out) {
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
-  // exponent of the total (fixed-order fp64 reduction; only picks F)
-  double part = 0.0;
-  for (int t = tid; t < n; t += NT) part += (double)from_key(key(t));
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, WAVE);
-  if (lane == 0) sm.wsum[wave] = part;
-  __syncthreads();
-  double total = 0.0;
-  for (int w = 0; w < NWV; ++w) total += sm.wsum[w];
-  __syncthreads();
-  if (!(total > 0.0)) return 1;
-  const double scale = ldexp(1.0, 61 - ilogb(total));
-  auto fx = [&](uint32_t kk) -> unsigned long long {
-    const double v = (double)from_key(kk) * scale;
-    return v > 0.0 ? (unsigned long long)v : 0ull;
-  };
-  // exact fixed-point total
-  unsigned long long tp = 0;
-  for (int t = tid; t < n; t += NT) tp += fx(key(t));
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) tp += __shfl_xor(tp, o, WAVE);
-  if (lane == 0) sm.wtot[wave] = tp;
-  __syncthreads();
-  unsigned long long tot_fx = 0;
-  for (int w = 0; w < NWV; ++w) tot_fx += sm.wtot[w];
-  __syncthreads();
-  unsigned long long target = (unsigned long long)ceil((double)f * (double)tot_fx);
-  if (target > tot_fx) target = tot_fx;   // double rounding of f * total
-  if (target == 0) return 1;
-
-  uint32_t pmask = cp == 0 ? 0u : (cp >= 32 ? ~0u : ~0u << (32 - cp));
+  uint32_t pmask = cp <= 0 ? 0u : (cp >= 32 ? ~0u : ~0u << (32 - cp));
   uint32_t prefix = lo_key & pmask, cnt_above = 0;
-  unsigned long long rem = target;
   int left = cp >= 32 ? 0 : 32 - cp;
 #pragma unroll 1
   while (left > 0) {
-    const int bits = min(11, left);
+    const int bits = min(DIGIT, left);
     const int shift = left - bits;
     const int nb = 1 << bits;
-    for (int i = tid; i < nb; i += NT) { sm.hist[i] = 0; sm.hmass[i] = 0; }
-    __syncthreads();
-    for (int t = tid; t < n; t += NT) {
-      const uint32_t kk = key(t);
+    for_keys(key, n, [&](uint32_t kk) {
       if ((kk & pmask) == prefix) {
         const int bin = (kk >> shift) & (nb - 1);
         atomicAdd(&sm.hist[bin], 1u);
-        atomicAdd(&sm.hmass[bin], fx(kk));
+        if (MASS) atomicAdd(&sm.hmass[bin], fx(kk));
+      }
+    });
+    __syncthreads();
+    // Thread t owns descending positions 2t and 2t+1 (bins nb-1-2t, nb-2-2t):
+    // it reads them, clears them for the next digit, and scans.
+    const int p0 = 2 * tid;
+    uint32_t c0 = 0, c1 = 0;
+    unsigned long long m0 = 0, m1 = 0;
+    if (p0 < nb) {
+      const int b0 = nb - 1 - p0, b1 = b0 - 1;   // nb is even
+      c0 = sm.hist[b0]; c1 = sm.hist[b1];
+      sm.hist[b0] = 0; sm.hist[b1] = 0;
+      if (MASS) {
+        m0 = sm.hmass[b0]; m1 = sm.hmass[b1];
+        sm.hmass[b0] = 0; sm.hmass[b1] = 0;
       }
     }
+    if (!MASS) { m0 = c0; m1 = c1; }
+    const unsigned long long own = m0 + m1;
+    const uint32_t own_c = c0 + c1;
+    unsigned long long incl;
+    uint32_t incl_c;
+    if (MASS) {
+      incl = wave_scan_add_u64(own);
+      incl_c = wave_scan_u32(own_c, 0u, OpAdd());
+    } else {
+      incl_c = wave_scan_u32(own_c, 0u, OpAdd());
+      incl = incl_c;
+    }
+    if (lane == WAVE - 1) { sm.f_m[wave] = incl; sm.f_c[wave] = incl_c; }
     __syncthreads();
-    const int p0 = 2 * tid, p1 = 2 * tid + 1;
-    const unsigned long long m0 = p0 < nb ? sm.hmass[nb - 1 - p0] : 0ull;
-    const unsigned long long m1 = p1 < nb ? sm.hmass[nb - 1 - p1] : 0ull;
-    const uint32_t c0 = p0 < nb ? sm.hist[nb - 1 - p0] : 0u;
-    const uint32_t c1 = p1 < nb ? sm.hist[nb - 1 - p1] : 0u;
-    const unsigned long long mab = block_excl_scan<unsigned long long>(m0 + m1, sm.wtot);
-    const uint32_t cab = block_excl_scan<uint32_t>(c0 + c1, sm.wtot);
-    if (p0 < nb && mab < rem && rem <= mab + m0) {
-      sm.bin = (uint32_t)(nb - 1 - p0); sm.mass_above = mab; sm.cnt_above = cab;
-    } else if (p1 < nb && mab + m0 < rem && rem <= mab + m0 + m1) {
-      sm.bin = (uint32_t)(nb - 1 - p1); sm.mass_above = mab + m0; sm.cnt_above = cab + c0;
+    unsigned long long wb = 0;
+    uint32_t wbc = 0;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      if (w < wave) { wb += sm.f_m[w]; wbc += sm.f_c[w]; }
+    }
+    const unsigned long long before = wb + incl - own;
+    if (before < rem && rem <= before + own) {   // exactly one thread
+      const bool first = before + m0 >= rem;      // then m0 > 0
+      sm.bin = (uint32_t)(first ? nb - 1 - p0 : nb - 2 - p0);
+      sm.cnt_above = wbc + incl_c - own_c + (first ? 0u : c0);
+      sm.mass_above = first ? before : before + m0;
     }
     __syncthreads();
-    rem -= sm.mass_above;
+    rem -= MASS ? sm.mass_above : (unsigned long long)sm.cnt_above;
     cnt_above += sm.cnt_above;
     prefix |= sm.bin << shift;
     pmask |= (uint32_t)(nb - 1) << shift;
     left -= bits;
-    __syncthreads();
   }
-  const unsigned long long fv = fx(prefix);   // > 0: the bin holds mass
-  const unsigned long long j = fv ? (rem + fv - 1) / fv : 1ull;
-  return (int)(cnt_above + (uint32_t)j);
+  *cnt_above_out = cnt_above;
+  *rem_out = rem;
+  return prefix;
 }
 
 template <bool IN_LDS>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
-  __shared__ uint32_t keys_lds[IN_LDS ? LDS_KEYS : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t keys_lds[IN_LDS ? LDS_KEYS : 4];
   __shared__ Smem sm;
   const int head = blockIdx.x, b = head / a.Hkv;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
@@ -249,8 +202,21 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     return;
   }
   const float* src = a.scores + (size_t)head * a.N_max;
+  const kv_budget& bu = a.bud;
+  const bool mass = bu.mode == KV_BUDGET_MASS;
+  const uint32_t tk = to_key(bu.tau);
+
+  // Staging pass: keys (to LDS), min/max key, threshold count, fp64 total.
+  uint32_t mn = 0xffffffffu, mx = 0u, cnt = 0u;
+  double tot = 0.0;
+  auto visit = [&](uint32_t kk) {
+    mn = min(mn, kk);
+    mx = max(mx, kk);
+    cnt += kk >= tk ? 1u : 0u;
+    if (mass) tot += (double)from_key(kk);
+  };
+  for (int i = tid; i < NBINS; i += NT) { sm.hist[i] = 0; sm.hmass[i] = 0; }
   if (IN_LDS) {
-    // 16-byte loads, all in flight before the first LDS store.
     constexpr int PER = LDS_KEYS / 4 / NT;
     const int n4 = ((a.N_max & 3) == 0) ? n >> 2 : 0;
     const float4* src4 = reinterpret_cast<const float4*>(src);
@@ -264,19 +230,37 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     for (int u = 0; u < PER; ++u) {
       const int i = tid + u * NT;
       if (i < n4) {
-        keys_lds[4 * i + 0] = to_key(v[u].x);
-        keys_lds[4 * i + 1] = to_key(v[u].y);
-        keys_lds[4 * i + 2] = to_key(v[u].z);
-        keys_lds[4 * i + 3] = to_key(v[u].w);
+        const uint32_t k0 = to_key(v[u].x), k1 = to_key(v[u].y);
+        const uint32_t k2 = to_key(v[u].z), k3 = to_key(v[u].w);
+        *reinterpret_cast<uint4*>(&keys_lds[4 * i]) = make_uint4(k0, k1, k2, k3);
+        visit(k0); visit(k1); visit(k2); visit(k3);
       }
     }
-    for (int t = 4 * n4 + tid; t < n; t += NT) keys_lds[t] = to_key(src[t]);
-    __syncthreads();
+    for (int t = 4 * n4 + tid; t < n; t += NT) {
+      const uint32_t kk = to_key(src[t]);
+      keys_lds[t] = kk;
+      visit(kk);
+    }
+  } else {
+    for (int t = tid; t < n; t += NT) visit(to_key(src[t]));
   }
+  mn = last_lane(wave_scan_u32(mn, 0xffffffffu, OpMin()));
+  mx = last_lane(wave_scan_u32(mx, 0u, OpMax()));
+  cnt = last_lane(wave_scan_u32(cnt, 0u, OpAdd()));
+  if (mass) tot = wave_sum_i<double>(tot);
+  if (lane == 0) {
+    sm.w_min[wave] = mn; sm.w_max[wave] = mx; sm.w_cnt[wave] = cnt; sm.w_sum[wave] = tot;
+  }
+  __syncthreads();
+  mn = 0xffffffffu; mx = 0u; cnt = 0u; tot = 0.0;
+  for (int w = 0; w < NWV; ++w) {
+    mn = min(mn, sm.w_min[w]); mx = max(mx, sm.w_max[w]);
+    cnt += sm.w_cnt[w]; tot += sm.w_sum[w];
+  }
+  const int cp = mn == mx ? 32 : __clz(mn ^ mx);   // top key bits every token shares
   Keys<IN_LDS> key{keys_lds, src};
 
   // Budget -> k.
-  const kv_budget& bu = a.bud;
   const double nd = (double)n;
   int lo = (int)floor((double)bu.min_ratio * nd + 0.5);
   int hi = (int)floor((double)bu.max_ratio * nd + 0.5);
@@ -292,67 +276,141 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     const double x = floor((double)r * nd + 0.5);
     k = x >= 1.0 ? (x >= nd ? n : (int)x) : 1;
   } else if (bu.mode == KV_BUDGET_THRESHOLD) {
-    const uint32_t tk = to_key(bu.tau);
-    uint32_t c = 0;
-    for (int t = tid; t < n; t += NT) c += key(t) >= tk ? 1u : 0u;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o, WAVE);
-    if (lane == 0) sm.wcnt_gt[wave] = c;
+    k = min(max((int)cnt, lo), hi);
+  } else if (tot > 0.0) {
+    // mass: fixed point with 2^(61 - floor(log2 total)) so every sum < 2^62
+    const double scale = ldexp(1.0, 61 - ilogb(tot));
+    auto fx = [&](uint32_t kk) -> unsigned long long {
+      const double v = (double)from_key(kk) * scale;
+      return v > 0.0 ? (unsigned long long)v : 0ull;
+    };
+    unsigned long long tp = 0;
+    for_keys(key, n, [&](uint32_t kk) { tp += fx(kk); });
+    tp = last_lane(wave_scan_add_u64(tp));
+    if (lane == 0) sm.w_fx[wave] = tp;
     __syncthreads();
-    uint32_t tot = 0;
-    for (int w = 0; w < NWV; ++w) tot += sm.wcnt_gt[w];
-    __syncthreads();
-    k = min(max((int)tot, lo), hi);
-  }
-  uint32_t lo_key;
-  const int cp = common_prefix(key, n, sm, &lo_key);
-  if (bu.mode == KV_BUDGET_MASS) {
-    k = mass_count(key, n, bu.mass, cp, lo_key, sm);
-    k = min(max(k, lo), hi);
-  }
-
-  uint32_t quota;
-  const uint32_t T = kth_key(key, n, k, cp, lo_key, sm, &quota);
-
-  // Emit.  Wave w owns tokens [w*seg, min((w+1)*seg, n)), seg a multiple of 64.
-  const int seg = ((n + NWV - 1) / NWV + WAVE - 1) / WAVE * WAVE;
-  const int s0 = wave * seg, s1 = min(s0 + seg, n);
-  uint32_t gt = 0, eq = 0;
-  for (int base = s0; base < s1; base += WAVE) {
-    const int t = base + lane;
-    const uint32_t kk = t < s1 ? key(t) : 0u;
-    gt += __popcll(__ballot(t < s1 && kk > T));
-    eq += __popcll(__ballot(t < s1 && kk == T));
-  }
-  if (lane == 0) { sm.wcnt_gt[wave] = gt; sm.wcnt_eq[wave] = eq; }
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t eb = 0, kb = 0;
-    for (int w = 0; w < NWV; ++w) {
-      sm.eq_before[w] = eb;
-      sm.keep_before[w] = kb;
-      const uint32_t left = quota > eb ? quota - eb : 0u;
-      kb += sm.wcnt_gt[w] + min(left, sm.wcnt_eq[w]);
-      eb += sm.wcnt_eq[w];
+    unsigned long long tot_fx = 0;
+    for (int w = 0; w < NWV; ++w) tot_fx += sm.w_fx[w];
+    unsigned long long target = (unsigned long long)ceil((double)bu.mass * (double)tot_fx);
+    if (target > tot_fx) target = tot_fx;   // double rounding of f * total
+    if (target > 0) {
+      uint32_t above;
+      unsigned long long rem;
+      const uint32_t Tm = descend<true>(key, n, cp, mn, target, sm, fx, &above, &rem);
+      const unsigned long long fv = fx(Tm);   // > 0: its bin holds mass
+      const unsigned long long j = fv ? (rem + fv - 1) / fv : 1ull;
+      k = (int)(above + (uint32_t)j);
     }
-    a.kept_count[head] = k;
+    k = min(max(k, lo), hi);
+  } else {
+    k = lo;
   }
-  __syncthreads();
-  uint32_t eqr = sm.eq_before[wave], slot = sm.keep_before[wave];
+
+  // The k-th key and the tie quota.
+  uint32_t T, quota;
+  {
+    uint32_t above;
+    unsigned long long rem;
+    auto nofx = [](uint32_t) { return 0ull; };
+    T = descend<false>(key, n, cp, mn, (unsigned long long)k, sm, nofx, &above, &rem);
+    quota = (uint32_t)rem;
+  }
+
+  // Emit.  Wave w owns tokens [w*seg, min((w+1)*seg, n)), seg a multiple of
+  // 256, and walks it in steps of 256 (four consecutive tokens per lane).
+  // Lane order is token order, so per-step ballots give each lane the tie
+  // rank of its first equal key and the output slot of its first kept key.
+  const int seg = ((n + NWV - 1) / NWV + 4 * WAVE - 1) / (4 * WAVE) * (4 * WAVE);
+  const int s0 = wave * seg, s1 = min(s0 + seg, n);
   int32_t* dst = a.kept_idx + (size_t)head * a.N_max;
-  const uint64_t lt = lanemask_lt();
-  for (int base = s0; base < s1; base += WAVE) {
-    const int t = base + lane;
-    const uint32_t kk = t < s1 ? key(t) : 0u;
-    const bool is_eq = t < s1 && kk == T;
-    const uint64_t eqm = __ballot(is_eq);
-    const uint32_t my_eq_rank = eqr + (uint32_t)__popcll(eqm & lt);
-    const bool keep = t < s1 && (kk > T || (is_eq && my_eq_rank < quota));
-    const uint64_t km = __ballot(keep);
-    const uint32_t at = slot + (uint32_t)__popcll(km & lt);
-    if (keep && at < (uint32_t)n) dst[at] = t;
-    slot += (uint32_t)__popcll(km);
-    eqr += (uint32_t)__popcll(eqm);
+  uint32_t gt = 0, eq = 0, slot = 0, eqr = 0;
+  auto count4 = [&](int t, const uint32_t* kk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool valid = t + u < s1;
+      gt += (uint32_t)__popcll(__ballot(valid && kk[u] > T));
+      eq += (uint32_t)__popcll(__ballot(valid && kk[u] == T));
+    }
+  };
+  auto prefix_of_waves = [&]() __attribute__((always_inline)) {
+    if (lane == 0) { sm.w_gt[wave] = gt; sm.w_eq[wave] = eq; }
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) {
+      const uint32_t left = quota > eqr ? quota - eqr : 0u;
+      slot += sm.w_gt[w] + min(left, sm.w_eq[w]);
+      eqr += sm.w_eq[w];
+    }
+  };
+  auto write4 = [&](int t, const uint32_t* kk) __attribute__((always_inline)) {
+    bool is_gt[4], is_eq[4], keep[4];
+    uint64_t be[4], bk[4];
+    uint32_t r = eqr;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool valid = t + u < s1;
+      is_gt[u] = valid && kk[u] > T;
+      is_eq[u] = valid && kk[u] == T;
+      be[u] = __ballot(is_eq[u]);
+      r += mbcnt(be[u]);
+    }
+    uint32_t at = slot;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      keep[u] = is_gt[u] || (is_eq[u] && r < quota);
+      r += is_eq[u] ? 1u : 0u;
+      bk[u] = __ballot(keep[u]);
+      at += mbcnt(bk[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (keep[u]) {
+        if (at < (uint32_t)n) dst[at] = t + u;
+        ++at;
+      }
+      slot += (uint32_t)__popcll(bk[u]);
+      eqr += (uint32_t)__popcll(be[u]);
+    }
+  };
+  if (tid == 0) a.kept_count[head] = k;
+  if (IN_LDS) {
+    constexpr int EPI = LDS_KEYS / NWV / (4 * WAVE);   // seg <= EPI * 256
+    uint4 ek[EPI];
+#pragma unroll
+    for (int j = 0; j < EPI; ++j) {
+      const int t = s0 + j * 4 * WAVE + 4 * lane;
+      ek[j] = t < s1 ? *reinterpret_cast<const uint4*>(&keys_lds[t]) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < EPI; ++j) {
+      if (s0 + j * 4 * WAVE < s1) {
+        const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
+        count4(s0 + j * 4 * WAVE + 4 * lane, kk);
+      }
+    }
+    prefix_of_waves();
+#pragma unroll
+    for (int j = 0; j < EPI; ++j) {
+      if (s0 + j * 4 * WAVE < s1) {
+        const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
+        write4(s0 + j * 4 * WAVE + 4 * lane, kk);
+      }
+    }
+  } else {
+    auto four = [&](int t, uint32_t* kk) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kk[u] = t + u < s1 ? key(t + u) : 0u;
+    };
+    for (int base = s0; base < s1; base += 4 * WAVE) {
+      uint32_t kk[4];
+      four(base + 4 * lane, kk);
+      count4(base + 4 * lane, kk);
+    }
+    prefix_of_waves();
+    for (int base = s0; base < s1; base += 4 * WAVE) {
+      uint32_t kk[4];
+      four(base + 4 * lane, kk);
+      write4(base + 4 * lane, kk);
+    }
   }
 }
 

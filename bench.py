@@ -9,14 +9,22 @@ in HBM before timing starts.  Prints one JSON line:
   value       cached tokens per second over the whole step
   roofline    the kernel with the most GPU time: algorithmic FLOPs (MFMA
               kernels) or bytes (HBM kernels) per launch / its mean duration,
-              durations from hipEvents recorded on the library's stream
+              durations from hipEvents the library records on its launch
+              stream around every kernel of the timed steps; `traffic` is the
+              HBM bytes per launch that rocprofv3's FETCH_SIZE + WRITE_SIZE
+              counters read for that kernel (scaled by the ratio of known to
+              counted bytes of a plain device copy), taken from the committed
+              summary under profiles/ and reported only while the kernel's
+              sources still hash to the recorded value
+  copy_gbps   a 1 GiB device-to-device copy (read + write bytes / time)
   cpu_baseline the float64 oracle on a bounded sample on the host cores
 """
 from __future__ import annotations
 
 import argparse
-import ctypes
+import hashlib
 import json
+import re
 import math
 import os
 import sys
@@ -95,19 +103,79 @@ class Pipeline:
                            workspace=self.ws_d)
 
 
-def kernel_times(pipe: Pipeline, steps: int):
+def timed_steps(pipe: Pipeline, steps: int, only=None):
+    """Wall-clock ms per step and the event timings of the same steps: every
+    kernel, or (only=name) one kernel, so that the timed region carries two
+    event records per step instead of two per launch."""
     L = _lib.lib()
+    torch.cuda.synchronize()
+    L.kv_timing_only(only.encode() if only else None)
     L.kv_timing_enable(1)
+    t0 = time.perf_counter()
     for _ in range(steps):
         pipe.step()
     torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
     buf = (_lib.KvKernelTime * 32)()
     n = L.kv_timing_read(buf, 32)
     L.kv_timing_enable(0)
+    L.kv_timing_only(None)
     if n < 0:
         raise RuntimeError(f"kv_timing_read failed: {n}")
-    return {buf[i].name.decode(): (buf[i].total_ms / buf[i].launches, buf[i].launches)
-            for i in range(n)}
+    return ms, {buf[i].name.decode(): (buf[i].total_ms / buf[i].launches, buf[i].launches)
+                for i in range(n)}
+
+
+COPY_BYTES = 1 << 30
+
+
+def copy_gbps(reps: int = 5) -> float:
+    """Read + write bandwidth of a plain 1 GiB device copy (torch copy_)."""
+    src = torch.empty(COPY_BYTES // 4, device="cuda:0", dtype=torch.float32).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    sec = ev[0].elapsed_time(ev[1]) * 1e-3 / reps
+    del src, dst
+    return 2.0 * COPY_BYTES / sec / 1e9
+
+
+# Sources each timed kernel is built from (the traffic figures are tied to them).
+KERNEL_SOURCES = {
+    "score_rowstats": ("score.hip", "common.hpp"), "score_colsum": ("score.hip", "common.hpp"),
+    "score_fold": ("score.hip", "common.hpp"), "select": ("select.hip", "common.hpp"),
+    "compact": ("compact.hip", "common.hpp"), "decode_split": ("decode.hip", "common.hpp"),
+    "decode_merge": ("decode.hip", "common.hpp"),
+}
+CSRC = os.path.join(ROOT, "kv_cache_compression_score_amd", "csrc")
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from profiles/hbm_traffic_<workload>.md, or None
+    when absent or when the kernel's sources changed since the counters ran."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    pat = re.compile(r"^traffic: kernel=(\S+) src=(\S+) bytes_per_launch=(\d+)")
+    with open(path) as fh:
+        for line in fh:
+            m = pat.match(line.strip())
+            if m and m.group(1) == kernel and m.group(2) == source_hash(kernel):
+                return int(m.group(3))
+    return None
 
 
 def cpu_baseline(lay: wl.Layer, nseq: int):
@@ -152,19 +220,16 @@ def main():
     log(f"bench: generating {cfg.name}")
     lay = wl.make_layer(cfg)
     pipe = Pipeline(lay)
-    log(f"bench: {torch.cuda.get_device_name(0)}; warmup {args.warmup}")
+    log("bench: device copy bandwidth")
+    copy_bw = copy_gbps()
+    log(f"bench: {torch.cuda.get_device_name(0)}; copy {copy_bw:.0f} GB/s; warmup {args.warmup}")
     for _ in range(args.warmup):
         pipe.step()
     torch.cuda.synchronize()
 
-    log(f"bench: timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        pipe.step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
-
-    kt = kernel_times(pipe, args.steps)
+    # Per-kernel breakdown (all kernels bracketed), then the timed region with
+    # events around the roofline kernel only.
+    _, kt = timed_steps(pipe, args.steps)
     log("bench: per-kernel mean ms " + ", ".join(f"{k}={v[0]:.4f}" for k, v in kt.items()))
 
     B, Hkv, N, D = lay.k.shape
@@ -183,8 +248,10 @@ def main():
             "select": ("hbm", bytes_sel), "compact": ("hbm", bytes_comp),
             "decode_split": ("hbm", bytes_dec)}
     dom = max(work, key=lambda k: kt.get(k, (0.0,))[0])
+    log(f"bench: timing {args.steps} steps (events around {dom})")
+    ms, kt_dom = timed_steps(pipe, args.steps, only=dom)
     bound, amount = work[dom]
-    t_dom = kt[dom][0] * 1e-3
+    t_dom = kt_dom[dom][0] * 1e-3
     if bound == "mfma":
         achieved, peak, unit = amount / t_dom / 1e12, peak_f, "TFLOP/s"
     else:
@@ -210,7 +277,9 @@ def main():
                    "d": D, "W": W, "budget": "mass" if cfg.budget_mode == wl.BUDGET_MASS
                    else f"ratio {cfg.ratio}", "kept_rows": kept},
         "roofline": {"kernel": dom, "bound": bound, "achieved": achieved, "peak": peak,
-                     "unit": unit, "frac": achieved / peak, "traffic": None},
+                     "unit": unit, "frac": achieved / peak,
+                     "traffic": measured_traffic(dom, cfg.name)},
+        "copy_gbps": copy_bw,
         "decode_hbm_gbps": bytes_dec / t_dec / 1e9,
         "score_stage": {"ms": t_score * 1e3,
                         "algorithmic_tflops": flop_pass / t_score / 1e12,

@@ -202,8 +202,12 @@ int kv_decode_attn(const void* q, const void* k_c, const void* v_c, const int64_
  * launch's own stream; kv_timing_enable(0) stops recording.  kv_timing_read
  * waits for the recorded events and writes up to max_entries per-kernel
  * totals (host array, caller-owned), returning the number of distinct
- * kernels (or a negative kv_status).  Timing adds event records between
- * launches, so it is meant for measurement runs, not production.
+ * kernels (or a negative kv_status).  kv_timing_only(name) restricts the
+ * recording to launches of that kernel name (one of "score_rowstats",
+ * "score_fold", "score_colsum", "select", "compact", "decode_split",
+ * "decode_merge"); NULL or "" records every launch.  The name is copied.
+ * Timing adds event records between launches, so it is meant for
+ * measurement runs, not production.
  * ---------------------------------------------------------------------- */
 typedef struct kv_kernel_time {
   char name[40];
@@ -211,6 +215,7 @@ typedef struct kv_kernel_time {
   double total_ms;
 } kv_kernel_time;
 int kv_timing_enable(int on);
+int kv_timing_only(const char* name);
 int kv_timing_read(kv_kernel_time* out, int max_entries);
 
 /* Human-readable name of a kv_status value (static string). */

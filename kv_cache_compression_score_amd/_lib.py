@@ -40,6 +40,7 @@ PROTOTYPES = {
                                c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "kv_status_string": (ctypes.c_char_p, [c_int]),
     "kv_timing_enable": (c_int, [c_int]),
+    "kv_timing_only": (c_int, [ctypes.c_char_p]),
     "kv_timing_read": (c_int, [ctypes.POINTER(KvKernelTime), c_int]),
 }
 

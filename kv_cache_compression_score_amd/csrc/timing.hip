@@ -1,5 +1,6 @@
 // Opt-in per-kernel timing: when enabled, every kernel the library launches
-// is bracketed by hipEvents recorded on the launch's own stream.
+// (or only those of one name) is bracketed by hipEvents recorded on the
+// launch's own stream.
 #include <string.h>
 
 #include <mutex>
@@ -20,6 +21,7 @@ std::mutex g_mu;
 std::vector<Record> g_records;
 std::vector<hipEvent_t> g_pool;
 bool g_enabled = false;
+std::string g_only;   // record only launches of this name (empty: all)
 
 hipEvent_t take_event() {
   if (!g_pool.empty()) {
@@ -36,7 +38,7 @@ hipEvent_t take_event() {
 
 TimedLaunch::TimedLaunch(const char* name, hipStream_t st) : name_(name), st_(st) {
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_enabled) return;
+  if (!g_enabled || (!g_only.empty() && g_only != name)) return;
   start_ = take_event();
   stop_ = take_event();
   if (start_ && stop_) (void)hipEventRecord(start_, st_);
@@ -62,6 +64,12 @@ extern "C" int kv_timing_enable(int on) {
   }
   g_records.clear();
   g_enabled = on != 0;
+  return KV_OK;
+}
+
+extern "C" int kv_timing_only(const char* name) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_only = name ? name : "";
   return KV_OK;
 }
 

@@ -156,9 +156,12 @@ CSRC = os.path.join(ROOT, "kv_cache_compression_score_amd", "csrc")
 
 
 def source_hash(kernel: str) -> str:
+    """Hash of the kernel's sources and of the build script (its flags)."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
+    paths = [os.path.join(CSRC, f) for f in KERNEL_SOURCES[kernel]]
+    paths.append(os.path.join(ROOT, "kv_cache_compression_score_amd", "build.py"))
+    for p in paths:
+        with open(p, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 

@@ -27,6 +27,12 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE,
          "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
+# Per-source extra flags.  The score kernels never carry NaNs (masked logits
+# are -inf), so their device code drops the sNaN-quieting v_max that IEEE
+# mode puts in front of every fmax of an MFMA result; infinities stay exact.
+EXTRA = {"score.hip": ["-Xarch_device", "-fno-honor-nans"]}
+
+
 def _hipcc() -> str:
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -45,7 +51,8 @@ def build(verbose: bool = False) -> str:
     objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
     jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        futs = [ex.submit(_run, [_hipcc(), *FLAGS, "-c", s, "-o", o]) for s, o in zip(srcs, objs)]
+        futs = [ex.submit(_run, [_hipcc(), *FLAGS, *EXTRA.get(os.path.basename(s), []), "-c", s,
+                                 "-o", o]) for s, o in zip(srcs, objs)]
         for f in futs:
             out = f.result()
             if verbose and out.strip():

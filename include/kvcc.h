@@ -73,6 +73,14 @@ typedef enum kv_budget_mode {
  *                            sum of the k largest scores, clamped to [lo, hi].
  *   lo = max(1, floor(min_ratio*n + 1/2)), hi = min(n, max(1, floor(max_ratio*n + 1/2))).
  * A head with n = 0 keeps nothing.  `head` is b*Hkv + h.
+ * Protected tokens: the first n_sink and the last n_recent tokens of every
+ * head (P, |P| = min(n, n_sink + n_recent) after clamping each to [0, n])
+ * come first in the order, ahead of every other token, and are always kept:
+ * the threshold count is #{t in P or s_t >= tau}, C(k) sums the real scores
+ * of P first, and k_h = min(n, max(k_h, |P|)) after the mode's clamps.  The
+ * recent window follows KVzap's sliding window (same section 2.3); sinks and
+ * window are the tokens "KV Cache Transform Coding for Compact Storage in LLM
+ * Inference", section 3, leaves uncompressed.  0 / 0 protects nothing.
  * Threshold pruning with a fixed tau follows "KVzap: Fast, Adaptive, and
  * Faithful KV Cache Pruning", section 2.3; per-head budgets (any allocation
  * across heads) follow "KVSculpt: KV Cache Compression as Distillation",
@@ -88,6 +96,8 @@ typedef struct kv_budget {
   float mass;              /* 0 <= f <= 1 */
   float min_ratio;         /* 0 <= min_ratio <= 1 */
   float max_ratio;         /* 0 <= max_ratio <= 1 */
+  int32_t n_sink;          /* >= 0: first tokens always kept */
+  int32_t n_recent;        /* >= 0: last tokens always kept */
 } kv_budget;
 
 /* ----------------------------------------------------------------------
@@ -123,9 +133,10 @@ int kv_score(const void* q_win, const void* k, const int32_t* ctx_len,
 /* ----------------------------------------------------------------------
  * kv_select - per-head budgeted top-k over the scores.
  *
- * Keeps, per KV head, the k_h first tokens of the order "higher score
- * first, equal scores by lower token index" (-0.0 equals +0.0; NaN scores
- * are outside the contract), k_h given by `budget`.  Low scorers are
+ * Keeps, per KV head, the k_h first tokens of the order "protected tokens
+ * first, then higher score first, equal scores by lower token index" (-0.0
+ * equals +0.0; NaN and +inf scores are outside the contract), k_h and the
+ * protected tokens given by `budget`.  Low scorers are
  * evicted as in importance-based eviction ("A Simple Plug-in for Improving
  * Eviction-Based KV Cache Compression", section "Enonce du Probleme").
  *

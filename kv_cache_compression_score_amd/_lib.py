@@ -15,7 +15,8 @@ KV_BF16 = 1
 class KvBudget(ctypes.Structure):
     _fields_ = [("mode", c_int32), ("k", c_void_p), ("ratio", c_void_p),
                 ("k_scalar", c_int32), ("ratio_scalar", c_float), ("tau", c_float),
-                ("mass", c_float), ("min_ratio", c_float), ("max_ratio", c_float)]
+                ("mass", c_float), ("min_ratio", c_float), ("max_ratio", c_float),
+                ("n_sink", c_int32), ("n_recent", c_int32)]
 
 
 class KvKernelTime(ctypes.Structure):

@@ -40,11 +40,14 @@ class Budget:
     mass: float = 0.0
     min_ratio: float = 0.0
     max_ratio: float = 1.0
+    n_sink: int = 0                         # first tokens always kept
+    n_recent: int = 0                       # last tokens always kept
 
     def to_c(self) -> KvBudget:
         return KvBudget(self.mode, _ptr(self.k), _ptr(self.ratio), int(self.k_scalar),
                         float(self.ratio_scalar), float(self.tau), float(self.mass),
-                        float(self.min_ratio), float(self.max_ratio))
+                        float(self.min_ratio), float(self.max_ratio),
+                        int(self.n_sink), int(self.n_recent))
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -22,6 +22,12 @@
 // tokens keep their keys in LDS (and a wave's segment in registers for the
 // emit); longer heads re-read the scores.
 //
+// Protected tokens (the first n_sink and last n_recent of a head) get the
+// largest key, 0xffffffff, above every finite score: they lead the order,
+// pass any threshold and, with k raised to at least their number, are always
+// kept.  In the mass budget their key carries no mass; their real scores are
+// summed separately and count first.
+//
 // The mass budget sums scores in 64-bit fixed point (scale 2^F with F picked
 // from the head's total so the sum stays below 2^62), which makes every
 // histogram sum exact and independent of the order of the atomic adds.
@@ -68,12 +74,16 @@ struct Smem {
   unsigned long long mass_above;
 };
 
+constexpr uint32_t PROTECTED_KEY = 0xffffffffu;
+
 template <bool IN_LDS>
 struct Keys {
   const uint32_t* lds;
   const float* g;
+  int p_end, r_begin;   // protected: t < p_end or t >= r_begin
   __device__ __forceinline__ uint32_t operator()(int t) const {
-    return IN_LDS ? lds[t] : to_key(g[t]);
+    if (IN_LDS) return lds[t];
+    return (t < p_end || t >= r_begin) ? PROTECTED_KEY : to_key(g[t]);
   }
 };
 
@@ -205,15 +215,23 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   const kv_budget& bu = a.bud;
   const bool mass = bu.mode == KV_BUDGET_MASS;
   const uint32_t tk = to_key(bu.tau);
+  // protected tokens: [0, p_end) and [r_begin, n)
+  const int p_end = min(max(bu.n_sink, 0), n);
+  const int r_begin = n - min(max(bu.n_recent, 0), n);
+  const int n_prot = min(n, p_end + (n - r_begin));
+  auto is_prot = [&](int t) { return t < p_end || t >= r_begin; };
 
-  // Staging pass: keys (to LDS), min/max key, threshold count, fp64 total.
+  // Staging pass: keys (to LDS), min/max key, threshold count, fp64 total
+  // of the real scores.
   uint32_t mn = 0xffffffffu, mx = 0u, cnt = 0u;
   double tot = 0.0;
-  auto visit = [&](uint32_t kk) {
+  auto visit = [&](uint32_t kr, bool prot) -> uint32_t {
+    const uint32_t kk = prot ? PROTECTED_KEY : kr;
     mn = min(mn, kk);
     mx = max(mx, kk);
     cnt += kk >= tk ? 1u : 0u;
-    if (mass) tot += (double)from_key(kk);
+    if (mass) tot += (double)from_key(kr);
+    return kk;
   };
   for (int i = tid; i < NBINS; i += NT) { sm.hist[i] = 0; sm.hmass[i] = 0; }
   if (IN_LDS) {
@@ -230,19 +248,17 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     for (int u = 0; u < PER; ++u) {
       const int i = tid + u * NT;
       if (i < n4) {
-        const uint32_t k0 = to_key(v[u].x), k1 = to_key(v[u].y);
-        const uint32_t k2 = to_key(v[u].z), k3 = to_key(v[u].w);
-        *reinterpret_cast<uint4*>(&keys_lds[4 * i]) = make_uint4(k0, k1, k2, k3);
-        visit(k0); visit(k1); visit(k2); visit(k3);
+        const int t = 4 * i;
+        const uint32_t k0 = visit(to_key(v[u].x), is_prot(t));
+        const uint32_t k1 = visit(to_key(v[u].y), is_prot(t + 1));
+        const uint32_t k2 = visit(to_key(v[u].z), is_prot(t + 2));
+        const uint32_t k3 = visit(to_key(v[u].w), is_prot(t + 3));
+        *reinterpret_cast<uint4*>(&keys_lds[t]) = make_uint4(k0, k1, k2, k3);
       }
     }
-    for (int t = 4 * n4 + tid; t < n; t += NT) {
-      const uint32_t kk = to_key(src[t]);
-      keys_lds[t] = kk;
-      visit(kk);
-    }
+    for (int t = 4 * n4 + tid; t < n; t += NT) keys_lds[t] = visit(to_key(src[t]), is_prot(t));
   } else {
-    for (int t = tid; t < n; t += NT) visit(to_key(src[t]));
+    for (int t = tid; t < n; t += NT) visit(to_key(src[t]), is_prot(t));
   }
   mn = last_lane(wave_scan_u32(mn, 0xffffffffu, OpMin()));
   mx = last_lane(wave_scan_u32(mx, 0u, OpMax()));
@@ -258,7 +274,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     cnt += sm.w_cnt[w]; tot += sm.w_sum[w];
   }
   const int cp = mn == mx ? 32 : __clz(mn ^ mx);   // top key bits every token shares
-  Keys<IN_LDS> key{keys_lds, src};
+  Keys<IN_LDS> key{keys_lds, src, p_end, r_begin};
 
   // Budget -> k.
   const double nd = (double)n;
@@ -280,31 +296,43 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   } else if (tot > 0.0) {
     // mass: fixed point with 2^(61 - floor(log2 total)) so every sum < 2^62
     const double scale = ldexp(1.0, 61 - ilogb(tot));
-    auto fx = [&](uint32_t kk) -> unsigned long long {
-      const double v = (double)from_key(kk) * scale;
+    auto fx = [&](uint32_t kk) -> unsigned long long {   // protected keys: no mass
+      const double v = kk == PROTECTED_KEY ? 0.0 : (double)from_key(kk) * scale;
       return v > 0.0 ? (unsigned long long)v : 0ull;
     };
-    unsigned long long tp = 0;
+    unsigned long long tp = 0, pm = 0;
     for_keys(key, n, [&](uint32_t kk) { tp += fx(kk); });
+    if (n_prot > 0) {   // real mass of the protected tokens
+      for (int t = tid; t < p_end; t += NT) pm += fx(to_key(src[t]));
+      for (int t = max(r_begin, p_end) + tid; t < n; t += NT) pm += fx(to_key(src[t]));
+    }
     tp = last_lane(wave_scan_add_u64(tp));
-    if (lane == 0) sm.w_fx[wave] = tp;
+    pm = last_lane(wave_scan_add_u64(pm));
+    if (lane == 0) { sm.w_fx[wave] = tp; sm.f_m[wave] = pm; }
     __syncthreads();
-    unsigned long long tot_fx = 0;
-    for (int w = 0; w < NWV; ++w) tot_fx += sm.w_fx[w];
+    unsigned long long pm_fx = 0, tot_fx = 0;
+    for (int w = 0; w < NWV; ++w) { tot_fx += sm.w_fx[w]; pm_fx += sm.f_m[w]; }
+    __syncthreads();   // sm.f_m is reused by the descent
+    tot_fx += pm_fx;
     unsigned long long target = (unsigned long long)ceil((double)bu.mass * (double)tot_fx);
     if (target > tot_fx) target = tot_fx;   // double rounding of f * total
-    if (target > 0) {
+    if (target > pm_fx) {
+      // the protected tokens come first (their bin holds no mass and only
+      // adds to the count above); descend for the mass still missing
       uint32_t above;
       unsigned long long rem;
-      const uint32_t Tm = descend<true>(key, n, cp, mn, target, sm, fx, &above, &rem);
+      const uint32_t Tm = descend<true>(key, n, cp, mn, target - pm_fx, sm, fx, &above, &rem);
       const unsigned long long fv = fx(Tm);   // > 0: its bin holds mass
       const unsigned long long j = fv ? (rem + fv - 1) / fv : 1ull;
       k = (int)(above + (uint32_t)j);
+    } else if (target > 0) {
+      k = n_prot;
     }
     k = min(max(k, lo), hi);
   } else {
     k = lo;
   }
+  k = min(max(k, n_prot), n);
 
   // The k-th key and the tie quota.
   uint32_t T, quota;
@@ -443,6 +471,7 @@ extern "C" int kv_select(const float* scores, const int32_t* ctx_len,
     return KV_ERR_MODE;
   if (bu.mode == KV_BUDGET_MASS && !(bu.mass >= 0.f && bu.mass <= 1.f)) return KV_ERR_MODE;
   if (bu.mode == KV_BUDGET_THRESHOLD && isnan(bu.tau)) return KV_ERR_MODE;
+  if (bu.n_sink < 0 || bu.n_recent < 0) return KV_ERR_MODE;
 
   SelectArgs a;
   a.scores = scores; a.ctx = ctx_len; a.B = B; a.Hkv = Hkv; a.N_max = N_max;

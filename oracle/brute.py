@@ -78,6 +78,38 @@ def mass_count(s, f: float) -> int:
     return n
 
 
+def precedes_protected(s, prot, a: int, b: int) -> bool:
+    """Protected tokens come first (by index), then the plain order."""
+    if prot[a] != prot[b]:
+        return prot[a]
+    if prot[a]:
+        return a < b
+    return precedes(s, a, b)
+
+
+def top_k_protected(s, prot, k: int):
+    """Kept set with protected tokens: max(k, #protected) tokens of lowest
+    rank under precedes_protected, ascending."""
+    n = len(s)
+    k = min(n, max(k, sum(1 for x in prot if x)))
+    return [t for t in range(n)
+            if sum(1 for u in range(n) if u != t and precedes_protected(s, prot, u, t)) < k]
+
+
+def mass_count_protected(s, prot, f: float) -> int:
+    """Fewest k >= 1 whose first-k exact sum (protected first, real scores)
+    reaches f times the exact total (before any clamp)."""
+    n = len(s)
+    rk = {t: sum(1 for u in range(n) if u != t and precedes_protected(s, prot, u, t))
+          for t in range(n)}
+    order = sorted(range(n), key=lambda t: rk[t])
+    total = math.fsum(s)
+    for k in range(1, n + 1):
+        if math.fsum(s[t] for t in order[:k]) >= f * total:
+            return k
+    return n
+
+
 def attend(q, k_rows, v_rows, scale: float):
     """Softmax attention of one query over the given rows: (out, lse)."""
     u = [scale * math.fsum(a * b for a, b in zip(q, kr)) for kr in k_rows]

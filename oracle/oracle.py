@@ -120,11 +120,30 @@ def window_scores(q_win, k, ctx_len=None, scale=None, causal=False):
     return scores, lse
 
 
-def total_order(s: np.ndarray) -> np.ndarray:
-    """Token indices of one head from first to last: higher score first,
-    equal scores by lower index (-0.0 and +0.0 compare equal)."""
+def protected_mask(n: int, n_sink: int = 0, n_recent: int = 0) -> np.ndarray:
+    """Tokens a head always keeps: the first n_sink (attention sinks) and the
+    last n_recent (the recent window).  "KVzap: Fast, Adaptive, and Faithful
+    KV Cache Pruning", section 2.3, keeps a sliding window of recent tokens
+    whatever their score; "KV Cache Transform Coding for Compact Storage in
+    LLM Inference", section 3, leaves the first tokens (attention sinks) and
+    the most recent ones uncompressed."""
+    p = np.zeros(n, dtype=bool)
+    p[:max(0, min(int(n_sink), n))] = True
+    if n_recent > 0:
+        p[max(0, n - int(n_recent)):] = True
+    return p
+
+
+def total_order(s: np.ndarray, protected=None) -> np.ndarray:
+    """Token indices of one head from first to last: protected tokens first
+    (by index), then higher score first, equal scores by lower index (-0.0
+    and +0.0 compare equal)."""
     s = np.asarray(s, dtype=np.float64)
-    return np.lexsort((np.arange(s.shape[0]), -s))
+    idx = np.arange(s.shape[0])
+    if protected is None or not np.any(protected):
+        return np.lexsort((idx, -s))
+    p = np.asarray(protected, dtype=bool)
+    return np.lexsort((idx, np.where(p, 0.0, -s), (~p).astype(np.int8)))
 
 
 def _round_half_up(x: float) -> int:
@@ -138,49 +157,59 @@ def _clamp_bounds(n: int, min_ratio: float, max_ratio: float):
 
 
 def budget_count(s, mode: int, *, k=None, ratio=None, tau=None, mass=None,
-                 min_ratio: float = 0.0, max_ratio: float = 1.0) -> int:
+                 min_ratio: float = 0.0, max_ratio: float = 1.0, protected=None) -> int:
     """Number of tokens one head keeps, from its n scores ``s``.
 
     BUDGET_K:         clamp(k, 1, n)
     BUDGET_RATIO:     clamp(floor(r*n + 1/2), 1, n), r the fp32 ratio widened
-    BUDGET_THRESHOLD: #{t : s_t >= tau}, tau fp32, then clamped to
-                      [max(1, round(min_ratio*n)), round(max_ratio*n)]
-    BUDGET_MASS:      fewest k >= 1 whose top-k score sum C(k) >= f*C(n)
-                      (f fp32; sums in float64 in the total order), then the
+    BUDGET_THRESHOLD: #{t : t protected or s_t >= tau}, tau fp32, then clamped
+                      to [max(1, round(min_ratio*n)), round(max_ratio*n)]
+    BUDGET_MASS:      fewest k >= 1 whose first-k score sum C(k) in the
+                      total order (protected tokens first, with their real
+                      scores) reaches f*C(n) (f fp32; float64 sums), then the
                       same clamp as the threshold mode
+    Protected tokens count toward k and are always kept: the result is at
+    least their number.
     """
     s = np.asarray(s, dtype=np.float64)
     n = s.shape[0]
     if n == 0:
         return 0
+    p = np.zeros(n, dtype=bool) if protected is None else np.asarray(protected, dtype=bool)
+    n_prot = int(np.count_nonzero(p))
     if mode == BUDGET_K:
-        return int(min(max(int(k), 1), n))
-    if mode == BUDGET_RATIO:
+        kk = min(max(int(k), 1), n)
+    elif mode == BUDGET_RATIO:
         r = float(np.float32(ratio))
-        return int(min(max(int(math.floor(r * n + 0.5)), 1), n))
-    lo, hi = _clamp_bounds(n, min_ratio, max_ratio)
-    if mode == BUDGET_THRESHOLD:
+        kk = min(max(int(math.floor(r * n + 0.5)), 1), n)
+    elif mode == BUDGET_THRESHOLD:
+        lo, hi = _clamp_bounds(n, min_ratio, max_ratio)
         t = float(np.float32(tau))
-        cnt = int(np.count_nonzero(s >= t))
-        return int(min(max(cnt, lo), hi))
-    if mode == BUDGET_MASS:
+        cnt = int(np.count_nonzero(p | (s >= t)))
+        kk = min(max(cnt, lo), hi)
+    elif mode == BUDGET_MASS:
+        lo, hi = _clamp_bounds(n, min_ratio, max_ratio)
         f = float(np.float32(mass))
-        c = np.cumsum(s[total_order(s)])
+        c = np.cumsum(s[total_order(s, p)])
         target = f * c[-1]
         kk = int(np.searchsorted(c, target, side="left")) + 1
         kk = min(kk, n)
-        return int(min(max(kk, lo), hi))
-    raise ValueError(f"unknown budget mode {mode}")
+        kk = min(max(kk, lo), hi)
+    else:
+        raise ValueError(f"unknown budget mode {mode}")
+    return int(min(max(kk, n_prot), n))
 
 
-def select(scores, ctx_len=None, mode=BUDGET_RATIO, **params):
+def select(scores, ctx_len=None, mode=BUDGET_RATIO, n_sink: int = 0, n_recent: int = 0,
+           **params):
     """Per-head kept token indices.
 
     scores [B][Hkv][N_max]; params as ``budget_count`` (``k``/``ratio`` may
-    also be per-head arrays of length B*Hkv).  Returns ``(kept_idx, count)``:
-    kept_idx [B][Hkv][N_max] int32 (first count entries valid, ascending, the
-    rest -1) and count [B*Hkv] int32.  The kept set of a head is the first
-    count tokens of ``total_order``.
+    also be per-head arrays of length B*Hkv); n_sink / n_recent protect the
+    first / last tokens of every head (``protected_mask``).  Returns
+    ``(kept_idx, count)``: kept_idx [B][Hkv][N_max] int32 (first count entries
+    valid, ascending, the rest -1) and count [B*Hkv] int32.  The kept set of a
+    head is the first count tokens of ``total_order``.
     """
     s_all = _f64(scores)
     B, Hkv, N_max = s_all.shape
@@ -196,8 +225,9 @@ def select(scores, ctx_len=None, mode=BUDGET_RATIO, **params):
                 if key in p and p[key] is not None and np.ndim(p[key]) > 0:
                     p[key] = np.asarray(p[key]).reshape(-1)[i]
             s = s_all[b, h, :n]
-            kk = budget_count(s, mode, **p)
-            idx = np.sort(total_order(s)[:kk])
+            prot = protected_mask(n, n_sink, n_recent)
+            kk = budget_count(s, mode, protected=prot, **p)
+            idx = np.sort(total_order(s, prot)[:kk])
             kept[b, h, :kk] = idx
             count[i] = kk
     return kept, count

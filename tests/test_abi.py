@@ -85,6 +85,8 @@ def test_select_validation():
     assert _select(B(3, None, None, 0, 0, 0, 2.0, 0, 1)) == KV_ERR_MODE
     assert _select(B(2, None, None, 0, 0, float("nan"), 0, 0, 1)) == KV_ERR_MODE
     assert _select(B(2, None, None, 0, 0, 0.1, 0, -0.5, 1)) == KV_ERR_MODE
+    assert _select(B(1, None, None, 0, 0.5, 0, 0, 0, 1, -1, 0)) == KV_ERR_MODE   # n_sink < 0
+    assert _select(B(1, None, None, 0, 0.5, 0, 0, 0, 1, 0, -4)) == KV_ERR_MODE   # n_recent < 0
     assert _select(B(1, None, None, 0, 0.5, 0, 0, 0, 1), N=0) == KV_ERR_SHAPE
     assert _select(B(1, P + 4, None, 0, 0.5, 0, 0, 0, 1)) == KV_ERR_ALIGN
 

@@ -98,16 +98,20 @@ def test_select_threshold(kind, shape):
         compare_sets(idx_g, cnt_g, idx_r, cnt_r)
 
 
-def mass_count_ok(s_head, k_g, f, lo, hi):
+def mass_count_ok(s_head, k_g, f, lo, hi, prot=None):
     """A GPU count that differs from the oracle's is accepted only if it is the
     clamp of a count that brackets f * C(n) to within 1e-12 * C(n) on the
-    oracle's float64 sums, C(k) the sum of the k largest scores."""
-    c = np.cumsum(s_head[orc.total_order(s_head)])
+    oracle's float64 sums, C(k) the sum of the first k scores in the total
+    order (protected tokens first).  Raising k to the protected count makes
+    the clamp [max(lo, |P|), max(hi, |P|)]."""
+    c = np.cumsum(s_head[orc.total_order(s_head, prot)])
     target = float(np.float32(f)) * c[-1]
     band = 1e-12 * c[-1]
     n = len(s_head)
+    n_prot = 0 if prot is None else int(np.count_nonzero(prot))
     k_lo = max(1, int(np.floor(np.float32(lo) * n + 0.5)))
     k_hi = min(n, max(1, int(np.floor(np.float32(hi) * n + 0.5))))
+    k_lo, k_hi = max(min(k_lo, k_hi), n_prot), max(k_hi, n_prot)
     reaches = lambda k: c[k - 1] >= target - band          # C(k) reaches the target
     short = lambda k: k == 1 or c[k - 2] < target + band   # C(k-1) does not (within band)
     if k_lo < k_g < k_hi:
@@ -156,3 +160,47 @@ def test_select_on_real_scores_and_determinism():
         assert torch.equal(i1[0, h, :k], i2[0, h, :k])
     idx_r, cnt_r = orc.select(s.cpu().numpy(), lay.ctx_len, orc.BUDGET_RATIO, ratio=cfg.ratio)
     compare_sets(i1.cpu().numpy(), n1.cpu().numpy(), idx_r, cnt_r)
+
+
+PROT = [(4, 64), (0, 128), (3000, 0), (10, 100000), (1, 1)]
+
+
+@pytest.mark.parametrize("kind", ["ties", "heavy"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"B{s[0]}H{s[1]}N{s[2]}")
+def test_select_protected(kind, shape):
+    # Sinks and recent window: stage parity on the same fp32 scores in every
+    # budget mode (mass counts within the fixed-point bracket), and every
+    # protected token is kept.
+    B, Hkv, N, ctx = shape
+    log(f"select protected {kind} {shape}")
+    s = synth_scores(13 + N, B, Hkv, N, ctx, kind)
+    for n_sink, n_recent in PROT:
+        pr = dict(n_sink=n_sink, n_recent=n_recent)
+        cases = [
+            (api.Budget(api.BUDGET_RATIO, ratio_scalar=0.05, **pr), dict(mode=orc.BUDGET_RATIO, ratio=0.05)),
+            (api.Budget(api.BUDGET_K, k_scalar=3, **pr), dict(mode=orc.BUDGET_K, k=3)),
+            (api.Budget(api.BUDGET_THRESHOLD, tau=0.5, min_ratio=0.0, max_ratio=0.3, **pr),
+             dict(mode=orc.BUDGET_THRESHOLD, tau=0.5, min_ratio=0.0, max_ratio=0.3)),
+        ]
+        for bud, ref in cases:
+            idx_g, cnt_g = run_select(s, ctx, bud)
+            idx_r, cnt_r = orc.select(s, ctx, **ref, **pr)
+            compare_sets(idx_g, cnt_g, idx_r, cnt_r)
+        for f, lo, hi in [(0.9, 0.02, 0.5), (0.3, 0.0, 1.0)]:
+            idx_g, cnt_g = run_select(s, ctx, api.Budget(api.BUDGET_MASS, mass=f, min_ratio=lo,
+                                                         max_ratio=hi, **pr))
+            idx_r, cnt_r = orc.select(s, ctx, orc.BUDGET_MASS, mass=f, min_ratio=lo,
+                                      max_ratio=hi, **pr)
+            for bb in range(B):
+                n = ctx[bb]
+                prot = orc.protected_mask(n, n_sink, n_recent)
+                for h in range(Hkv):
+                    i = bb * Hkv + h
+                    kg, kr = int(cnt_g[i]), int(cnt_r[i])
+                    sh = s[bb, h, :n].astype(np.float64)
+                    if kg != kr:
+                        assert mass_count_ok(sh, kg, f, lo, hi, prot), (bb, h, kg, kr)
+                    ref = np.sort(orc.total_order(sh, prot)[:kg])
+                    assert np.array_equal(idx_g[bb, h, :kg], ref), (bb, h)
+                    assert set(np.flatnonzero(prot)) <= set(idx_g[bb, h, :kg].tolist())
+

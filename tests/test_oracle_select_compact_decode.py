@@ -178,3 +178,77 @@ def test_full_keep_reproduces_full_attention_exactly():
     out, lse = orc.decode(q, kc_t, vc_t, off, 2)
     out_f, lse_f = orc.attend_full(q, k, v, [24, 19])
     assert np.array_equal(out, out_f) and np.array_equal(lse, lse_f)
+
+
+# ---- protected sinks and recent window ------------------------------------
+
+PROT_CASES = [(0, 0), (2, 0), (0, 3), (2, 3), (4, 9), (20, 0), (1, 30)]
+
+
+def _tied_scores(rng, n):
+    # few distinct values so that ties are common
+    return rng.integers(0, 5, size=n).astype(np.float64) / 4.0
+
+
+@pytest.mark.parametrize("n_sink,n_recent", PROT_CASES)
+def test_protected_topk_matches_brute_force(n_sink, n_recent):
+    rng = np.random.default_rng(40 + n_sink + 7 * n_recent)
+    n = 17
+    for trial in range(6):
+        s = _tied_scores(rng, n)
+        prot = orc.protected_mask(n, n_sink, n_recent)
+        for k in (1, 3, 8, 17):
+            idx, cnt = orc.select(s[None, None, :], None, orc.BUDGET_K, k=k,
+                                  n_sink=n_sink, n_recent=n_recent)
+            expect = brute.top_k_protected(list(s), list(prot), k)
+            assert idx[0, 0, :cnt[0]].tolist() == expect
+            # protected tokens are always kept
+            assert set(np.flatnonzero(prot)) <= set(expect)
+
+
+def test_protected_mask_union_and_overlap():
+    assert orc.protected_mask(10, 2, 3).tolist() == [1, 1, 0, 0, 0, 0, 0, 1, 1, 1]
+    assert orc.protected_mask(5, 4, 4).all()          # overlap covers everything
+    assert not orc.protected_mask(6, 0, 0).any()
+    assert orc.protected_mask(4, 9, 0).all()          # longer than the head
+
+
+@pytest.mark.parametrize("n_sink,n_recent", PROT_CASES)
+def test_protected_threshold_is_union(n_sink, n_recent):
+    # Without clamps the kept set is the protected tokens plus every token at
+    # or above tau (a set definition, no counting).
+    rng = np.random.default_rng(3 + n_sink)
+    n = 23
+    s = rng.random(n)
+    for tau in (0.2, 0.5, 0.9, 2.0):
+        idx, cnt = orc.select(s[None, None, :], None, orc.BUDGET_THRESHOLD, tau=tau,
+                              n_sink=n_sink, n_recent=n_recent)
+        prot = orc.protected_mask(n, n_sink, n_recent)
+        want = sorted(set(np.flatnonzero(prot)) | set(np.flatnonzero(s >= np.float32(tau))))
+        if not want:      # nothing qualifies: one token, the lowest-index maximum
+            want = [int(np.argmax(s))]
+        assert idx[0, 0, :cnt[0]].tolist() == want
+
+
+@pytest.mark.parametrize("n_sink,n_recent", PROT_CASES)
+def test_protected_mass_matches_brute_force(n_sink, n_recent):
+    rng = np.random.default_rng(11 + n_recent)
+    n = 15
+    for trial in range(5):
+        s = list(rng.random(n) ** 3)
+        prot = list(orc.protected_mask(n, n_sink, n_recent))
+        for f in (0.3, 0.6, 0.95):
+            idx, cnt = orc.select(np.array(s)[None, None, :], None, orc.BUDGET_MASS,
+                                  mass=f, n_sink=n_sink, n_recent=n_recent)
+            k = max(brute.mass_count_protected(s, prot, float(np.float32(f))), sum(prot))
+            assert cnt[0] == min(k, n)
+            assert idx[0, 0, :cnt[0]].tolist() == brute.top_k_protected(s, prot, k)
+
+
+def test_protected_zero_is_plain_selection():
+    rng = np.random.default_rng(5)
+    s = rng.random((2, 3, 50))
+    for mode, p in ((orc.BUDGET_RATIO, {"ratio": 0.2}), (orc.BUDGET_MASS, {"mass": 0.7})):
+        a = orc.select(s, None, mode, **p)
+        b = orc.select(s, None, mode, n_sink=0, n_recent=0, **p)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

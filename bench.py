@@ -17,6 +17,8 @@ in HBM before timing starts.  Prints one JSON line:
               summary under profiles/ and reported only while the kernel's
               sources still hash to the recorded value
   copy_gbps   a 1 GiB device-to-device copy (read + write bytes / time)
+  score_one_pass  kv_score_from_lse (row LSEs given, as a prefill pass
+              yields them): one sweep over K instead of two
   cpu_baseline the float64 oracle on a bounded sample on the host cores
 """
 from __future__ import annotations
@@ -124,6 +126,29 @@ def timed_steps(pipe: Pipeline, steps: int, only=None):
         raise RuntimeError(f"kv_timing_read failed: {n}")
     return ms, {buf[i].name.decode(): (buf[i].total_ms / buf[i].launches, buf[i].launches)
                 for i in range(n)}
+
+
+def one_pass_score_ms(pipe: Pipeline, steps: int) -> float:
+    """Mean event time of kv_score_from_lse (the score stage when the row
+    LSEs come from the prefill), fed the row LSEs of a two-pass call."""
+    L = _lib.lib()
+    _, lse = api.kv_score(pipe.q, pipe.k, pipe.c, with_row_lse=True)
+    out = torch.empty_like(pipe.scores)
+    for _ in range(3):
+        api.kv_score_from_lse(pipe.q, pipe.k, pipe.c, lse, scores=out)
+    torch.cuda.synchronize()
+    L.kv_timing_only(b"score_colsum")
+    L.kv_timing_enable(1)
+    for _ in range(steps):
+        api.kv_score_from_lse(pipe.q, pipe.k, pipe.c, lse, scores=out)
+    torch.cuda.synchronize()
+    buf = (_lib.KvKernelTime * 4)()
+    n = L.kv_timing_read(buf, 4)
+    L.kv_timing_enable(0)
+    L.kv_timing_only(None)
+    if n != 1:
+        raise RuntimeError(f"kv_timing_read returned {n}")
+    return buf[0].total_ms / buf[0].launches
 
 
 COPY_BYTES = 1 << 30
@@ -259,6 +284,7 @@ def main():
         achieved, peak, unit = amount / t_dom / 1e12, peak_f, "TFLOP/s"
     else:
         achieved, peak, unit = amount / t_dom / 1e9, PEAK_HBM_GBPS, "GB/s"
+    t_one = one_pass_score_ms(pipe, args.steps) * 1e-3
     t = {k: v[0] * 1e-3 for k, v in kt.items()}
     t_score = t["score_rowstats"] + t["score_fold"] + t["score_colsum"]
     t_dec = t["decode_split"] + t["decode_merge"]
@@ -288,6 +314,9 @@ def main():
                         "algorithmic_tflops": flop_pass / t_score / 1e12,
                         "algorithmic_frac": flop_pass / t_score / 1e12 / peak_f,
                         "executed_frac": 2 * flop_pass / t_score / 1e12 / peak_f},
+        "score_one_pass": {"ms": t_one * 1e3,
+                           "algorithmic_tflops": flop_pass / t_one / 1e12,
+                           "algorithmic_frac": flop_pass / t_one / 1e12 / peak_f},
         "select_compact_decode": {"ms": t_scd * 1e3,
                                   "gbps": (bytes_sel + bytes_comp + bytes_dec) / t_scd / 1e9,
                                   "frac": (bytes_sel + bytes_comp + bytes_dec) / t_scd / 1e9

@@ -131,6 +131,29 @@ int kv_score(const void* q_win, const void* k, const int32_t* ctx_len,
              void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------
+ * kv_score_from_lse - the same scores in one sweep over K, given the row
+ * log-sum-exps.
+ *
+ * Pruning runs after the attention op ("KVzap: Fast, Adaptive, and Faithful
+ * KV Cache Pruning", section 2.3), and a prefill attention pass already
+ * yields each window row's log-sum-exp ell ("KVSculpt: KV Cache Compression
+ * as Distillation", section 2.B).  Given it, the first sweep of kv_score is
+ * skipped:
+ *   s[b,h,t] = sum_r exp(l[r,t] - row_lse_in[r])
+ * with l, r, the GQA group and the causal rule as in kv_score.  The scores
+ * are the normalised ones only if row_lse_in is the LSE over the same keys
+ * (same ctx_len, scale and causal flag); the call trusts it.  A row whose
+ * row_lse_in is +inf adds nothing; -inf and NaN are outside the contract.
+ *
+ * row_lse_in [B][Hq][W] fp32 (natural log), device memory, read only
+ * other arguments as kv_score; no workspace.
+ * ---------------------------------------------------------------------- */
+int kv_score_from_lse(const void* q_win, const void* k, const int32_t* ctx_len,
+                      const float* row_lse_in, float* scores,
+                      int B, int Hq, int Hkv, int N_max, int W, int d, int dtype,
+                      int causal, float scale, void* stream);
+
+/* ----------------------------------------------------------------------
  * kv_select - per-head budgeted top-k over the scores.
  *
  * Keeps, per KV head, the k_h first tokens of the order "protected tokens

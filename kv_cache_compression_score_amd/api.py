@@ -104,6 +104,25 @@ def kv_score(q_win: torch.Tensor, k: torch.Tensor, ctx_len: Optional[torch.Tenso
     return scores, row_lse
 
 
+def kv_score_from_lse(q_win: torch.Tensor, k: torch.Tensor, ctx_len: Optional[torch.Tensor],
+                      row_lse_in: torch.Tensor, *, scale: float = 0.0, causal: bool = False,
+                      scores: Optional[torch.Tensor] = None):
+    """Window scores [B][Hkv][N_max] fp32 in one sweep, given the row LSE [B][Hq][W]."""
+    _check(q_win, "q_win"); _check(k, "k"); _check(row_lse_in, "row_lse_in")
+    B, Hq, W, d = q_win.shape
+    _, Hkv, N_max, _ = k.shape
+    if row_lse_in.dtype != torch.float32 or tuple(row_lse_in.shape) != (B, Hq, W):
+        raise ValueError("row_lse_in must be fp32 [B][Hq][W]")
+    if scores is None:
+        scores = torch.empty(B, Hkv, N_max, device=k.device, dtype=torch.float32)
+    if ctx_len is not None:
+        _check(ctx_len, "ctx_len")
+    _call("kv_score_from_lse", lib().kv_score_from_lse(
+        _ptr(q_win), _ptr(k), _ptr(ctx_len), _ptr(row_lse_in), _ptr(scores),
+        B, Hq, Hkv, N_max, W, d, _dtype_code(k), int(bool(causal)), float(scale), _stream()))
+    return scores
+
+
 def kv_select(scores: torch.Tensor, ctx_len: Optional[torch.Tensor], budget: Budget, *,
               kept_idx: Optional[torch.Tensor] = None, kept_count: Optional[torch.Tensor] = None):
     """Kept indices [B][Hkv][N_max] int32 (first count valid, ascending) and counts [B*Hkv]."""

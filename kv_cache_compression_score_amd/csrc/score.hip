@@ -81,6 +81,7 @@ struct ScoreArgs {
   float2* part;     // [B*Hkv][R_pad][n_chunks] per-chunk (max, sum of exp2) per row
   float* lse2;      // [B*Hkv][R_pad] base-2 row log-sum-exp (+inf: row adds nothing)
   float* row_lse;   // [B][Hq][W] natural log, optional
+  const float* lse_in;  // [B][Hq][W] natural-log row LSE given by the caller (one-pass), or null
   int B, Hq, Hkv, N_max, W, G, R, R_pad, causal;
   int TC, n_chunks;    // pass-1 token chunks (fixed by the sizes: sets the merge order)
   int TC2, n_chunks2;  // pass-2 token chunks (free: no cross-chunk arithmetic)
@@ -165,7 +166,14 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = (wave * RBW + i) * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
-        const float v = a.lse2[(size_t)head * a.R_pad + min(r, a.R_pad - 1)];
+        float v;
+        if (a.lse_in) {   // caller's natural-log LSE of row (j, w), to base 2
+          const int rc = min(r, a.R - 1);
+          const int j = h * a.G + rc / a.W, w = rc % a.W;
+          v = a.lse_in[((size_t)b * a.Hq + j) * a.W + w] * (float)LOG2E_D;
+        } else {
+          v = a.lse2[(size_t)head * a.R_pad + min(r, a.R_pad - 1)];
+        }
         nl2[i][e] = r < a.R ? -v : -INFINITY;
       }
     }
@@ -476,6 +484,11 @@ void launch_score(ScoreArgs a, hipStream_t st) {
   a.TC2 = chunk_tokens((int64_t)a.B * a.Hkv, a.N_max,
                        resident_slots(score_pass<T, D, NW, 2>, NW * WAVE, &slots2), 4);
   a.n_chunks2 = ceil_div(a.N_max, a.TC2);
+  if (a.lse_in) {   // row LSEs given: the column-sum pass alone
+    TimedLaunch t("score_colsum", st);
+    score_pass<T, D, NW, 2><<<dim3(a.n_chunks2, a.Hkv, a.B), NW * WAVE, 0, st>>>(a);
+    return;
+  }
   {
     TimedLaunch t("score_rowstats", st);
     score_pass<T, D, NW, 1><<<dim3(a.n_chunks, a.Hkv, a.B), NW * WAVE, 0, st>>>(a);
@@ -528,8 +541,41 @@ extern "C" int kv_score(const void* q_win, const void* k, const int32_t* ctx_len
 
   ScoreArgs a;
   a.q = q_win; a.k = k; a.ctx = ctx_len; a.scores = scores; a.row_lse = row_lse;
+  a.lse_in = nullptr;
   a.part = static_cast<float2*>(workspace);
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_lse);
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N_max = N_max; a.W = W; a.G = p.G;
+  a.R = p.R; a.R_pad = p.R_pad; a.TC = p.TC; a.n_chunks = p.n_chunks;
+  a.TC2 = p.TC; a.n_chunks2 = p.n_chunks;
+  a.causal = causal ? 1 : 0;
+  a.c = (float)((scale > 0.f ? (double)scale : 1.0 / sqrt((double)d)) * LOG2E_D);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == KV_BF16) {
+    if (d == 128) launch_score_nw<__bf16, 128>(a, p.NW, st);
+    else launch_score_nw<__bf16, 64>(a, p.NW, st);
+  } else {
+    if (d == 128) launch_score_nw<float, 128>(a, p.NW, st);
+    else launch_score_nw<float, 64>(a, p.NW, st);
+  }
+  return launch_status();
+}
+
+extern "C" int kv_score_from_lse(const void* q_win, const void* k, const int32_t* ctx_len,
+                                 const float* row_lse_in, float* scores,
+                                 int B, int Hq, int Hkv, int N_max, int W, int d, int dtype,
+                                 int causal, float scale, void* stream) {
+  if (!q_win || !k || !scores || !row_lse_in) return KV_ERR_NULL;
+  if (!aligned16(q_win) || !aligned16(k) || !aligned16(scores) || !aligned16(ctx_len) ||
+      !aligned16(row_lse_in))
+    return KV_ERR_ALIGN;
+  if (dtype != KV_F32 && dtype != KV_BF16) return KV_ERR_DTYPE;
+  ScorePlan p;
+  if (!plan_score(B, Hq, Hkv, N_max, W, d, &p)) return KV_ERR_SHAPE;
+
+  ScoreArgs a;
+  a.q = q_win; a.k = k; a.ctx = ctx_len; a.scores = scores; a.row_lse = nullptr;
+  a.lse_in = row_lse_in; a.part = nullptr; a.lse2 = nullptr;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N_max = N_max; a.W = W; a.G = p.G;
   a.R = p.R; a.R_pad = p.R_pad; a.TC = p.TC; a.n_chunks = p.n_chunks;
   a.TC2 = p.TC; a.n_chunks2 = p.n_chunks;

@@ -42,6 +42,25 @@ def score(q, k, n: int, G: int, scale: float, causal: bool = False):
     return scores, [lse[j * W:(j + 1) * W] for j in range(G)]
 
 
+def score_from_lse(q, k, n: int, G: int, scale: float, lse, causal: bool = False):
+    """Scores of one KV head with given row normalisers lse[G][W]."""
+    W = len(q[0])
+    out = [0.0] * n
+    terms = [[] for _ in range(n)]
+    for j in range(G):
+        for w in range(W):
+            if lse[j][w] == math.inf:
+                continue
+            for t in range(n):
+                if causal and t > n - W + w:
+                    continue
+                x = scale * math.fsum(a * b for a, b in zip(q[j][w], k[t]))
+                terms[t].append(math.exp(x - lse[j][w]))
+    for t in range(n):
+        out[t] = math.fsum(terms[t])
+    return out
+
+
 def precedes(s, a: int, b: int) -> bool:
     """Token a comes before token b: higher score, or equal score and lower index."""
     return s[a] > s[b] or (s[a] == s[b] and a < b)

@@ -120,6 +120,44 @@ def window_scores(q_win, k, ctx_len=None, scale=None, causal=False):
     return scores, lse
 
 
+def window_scores_from_lse(q_win, k, row_lse, ctx_len=None, scale=None, causal=False):
+    """Window scores with the row normalisers given instead of computed.
+
+    A prefill attention pass already yields each window row's log-sum-exp
+    ell ("KVSculpt: KV Cache Compression as Distillation", section 2.B), and
+    pruning runs after that attention op ("KVzap: Fast, Adaptive, and
+    Faithful KV Cache Pruning", section 2.3).  With row_lse [B][Hq][W]
+    (natural log) supplied:
+      s[h, t] = sum_r exp(l[r, t] - row_lse[r])
+    with l and the causal rule as in ``window_scores``.  A row whose row_lse
+    is +inf adds nothing.  Returns scores [B][Hkv][N_max] float64.
+    """
+    q = _f64(q_win)
+    kk = _f64(k)
+    given = _f64(row_lse)
+    B, Hq, W, d = q.shape
+    _, Hkv, N_max, _ = kk.shape
+    G = Hq // Hkv
+    sc = _scale(scale, d)
+    ctx = _ctx(ctx_len, B, N_max)
+    scores = np.zeros((B, Hkv, N_max), dtype=np.float64)
+    for b in range(B):
+        n = int(ctx[b])
+        for h in range(Hkv):
+            rows = q[b, h * G:(h + 1) * G].reshape(G * W, d)
+            logits = sc * (rows @ kk[b, h, :n].T)               # [G*W, n]
+            if causal:
+                w_of_row = np.tile(np.arange(W), G)
+                hidden = np.arange(n)[None, :] > (n - W + w_of_row)[:, None]
+                logits[hidden] = -np.inf
+            norm = given[b, h * G:(h + 1) * G].reshape(G * W, 1)
+            with np.errstate(invalid="ignore"):
+                p = np.exp(logits - norm)
+            p[np.isinf(norm[:, 0])] = 0.0
+            scores[b, h, :n] = p.sum(axis=0)
+    return scores
+
+
 def protected_mask(n: int, n_sink: int = 0, n_recent: int = 0) -> np.ndarray:
     """Tokens a head always keeps: the first n_sink (attention sinks) and the
     last n_recent (the recent window).  "KVzap: Fast, Adaptive, and Faithful

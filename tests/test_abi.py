@@ -70,6 +70,21 @@ def test_score_validation():
     assert _score(wsb=16) == KV_ERR_WORKSPACE
 
 
+def test_score_from_lse_validation():
+    # every call fails before any launch
+    def call(**kw):
+        a = dict(q=P, k=P, ctx=None, lse=P, s=P, B=1, Hq=4, Hkv=2, N=64, W=8, d=64, dtype=1)
+        a.update(kw)
+        return _lib.lib().kv_score_from_lse(a["q"], a["k"], a["ctx"], a["lse"], a["s"], a["B"],
+                                            a["Hq"], a["Hkv"], a["N"], a["W"], a["d"],
+                                            a["dtype"], 0, 0.0, None)
+    assert call(lse=None) == KV_ERR_NULL
+    assert call(lse=P + 4) == KV_ERR_ALIGN
+    assert call(dtype=3) == KV_ERR_DTYPE
+    assert call(W=65) == KV_ERR_SHAPE
+    assert call(d=32) == KV_ERR_SHAPE
+
+
 def _select(budget, **kw):
     a = dict(scores=P, ctx=None, B=1, Hkv=2, N=64, idx=P, cnt=P)
     a.update(kw)

@@ -92,3 +92,41 @@ def test_score_long128k_sampled_head():
                                  lay.ctx_len)
     err = check_scores(s_gpu[:, h:h + 1].cpu().numpy(), s_ref, lay.ctx_len.numpy(), cfg.W, cfg.G)
     log(f"  head {h} max rel score err {err:.3e}")
+
+
+# ---- one pass from given row LSEs -----------------------------------------
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}Hq{c[1]}Hkv{c[2]}W{c[3]}N{c[4]}"
+                         f"d{c[5]}{'f32' if c[6] == torch.float32 else 'bf16'}{'c' if c[7] else ''}")
+def test_score_from_lse_small(case):
+    # The oracle's row LSE (rounded to fp32, with one row set to +inf) goes to
+    # both sides; the GPU's one-pass scores must match the oracle's.
+    B, Hq, Hkv, W, N, d, dt, causal, ctx = case
+    log(f"score_from_lse case {case}")
+    lay = wl.random_case(12, B=B, Hq=Hq, Hkv=Hkv, d=d, N_max=N, W=W, dtype=dt, ctx=ctx)
+    _, lse = orc.window_scores(lay.q_win, lay.k, lay.ctx_len, causal=causal)
+    lse32 = lse.astype(np.float32)
+    lse32[0, 0, W - 1] = np.inf
+    s_gpu = api.kv_score_from_lse(dev(lay.q_win), dev(lay.k), dev(lay.ctx_len),
+                                  dev(torch.from_numpy(lse32)), causal=causal)
+    torch.cuda.synchronize()
+    s_ref = orc.window_scores_from_lse(lay.q_win, lay.k, lse32.astype(np.float64),
+                                       lay.ctx_len, causal=causal)
+    err = check_scores(s_gpu.cpu().numpy(), s_ref, lay.ctx_len.numpy(), W, Hq // Hkv)
+    log(f"  max rel score err {err:.3e}")
+
+
+def test_score_from_own_lse_equals_two_pass():
+    # Feeding back kv_score's own row LSE reproduces its two-pass scores.
+    cfg = wl.CONFIGS["llama8b_layer"]
+    lay = wl.make_layer(cfg, with_v=False)
+    q, k, c = dev(lay.q_win), dev(lay.k), dev(lay.ctx_len)
+    s2, lse = api.kv_score(q, k, c, with_row_lse=True)
+    s1 = api.kv_score_from_lse(q, k, c, lse)
+    torch.cuda.synchronize()
+    a, b = s1.double().cpu().numpy(), s2.double().cpu().numpy()
+    big = b > 2.0 ** -92 * cfg.W * cfg.G
+    rel = np.abs(a - b)[big] / b[big]
+    assert rel.max() < 1e-4, rel.max()
+    s_ref, _ = orc.window_scores(lay.q_win, lay.k, lay.ctx_len)
+    check_scores(s1.cpu().numpy(), s_ref, lay.ctx_len.numpy(), cfg.W, cfg.G)

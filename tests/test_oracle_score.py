@@ -145,3 +145,40 @@ def test_causal_single_row_equals_noncausal():
     a, la = orc.window_scores(q, k, [33, 20], causal=True)
     b, lb = orc.window_scores(q, k, [33, 20], causal=False)
     assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+# ---- one-pass scores from given row LSEs -----------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_from_lse_with_own_lse_is_two_pass(causal):
+    # Handing the oracle's own row LSE back must reproduce the two-pass scores.
+    q, k = _rand(21, 2, 6, 2, 5, 40, 8)
+    ctx = [40, 23]
+    s, lse = orc.window_scores(q, k, ctx, causal=causal)
+    s1 = orc.window_scores_from_lse(q, k, lse, ctx, causal=causal)
+    np.testing.assert_allclose(s1, s, rtol=1e-12, atol=1e-300)
+
+
+def test_from_lse_shift_scales_scores():
+    # Raising every normaliser by log 2 halves every score (closed form).
+    q, k = _rand(22, 1, 4, 2, 3, 30, 8)
+    s, lse = orc.window_scores(q, k)
+    s2 = orc.window_scores_from_lse(q, k, lse + math.log(2.0))
+    np.testing.assert_allclose(s2, s / 2.0, rtol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_from_lse_matches_brute_force(causal):
+    rng = np.random.default_rng(23)
+    B, Hkv, G, W, N, d = 1, 2, 2, 3, 11, 5
+    q, k = _rand(24, B, Hkv * G, Hkv, W, N, d)
+    lse = rng.standard_normal((B, Hkv * G, W)) + 3.0
+    lse[0, 1, 2] = np.inf                      # a row that adds nothing
+    s = orc.window_scores_from_lse(q, k, lse, causal=causal)
+    scale = 1.0 / math.sqrt(d)
+    for h in range(Hkv):
+        qs = [[list(q[0, h * G + j, w]) for w in range(W)] for j in range(G)]
+        ks = [list(k[0, h, t]) for t in range(N)]
+        ls = [[float(lse[0, h * G + j, w]) for w in range(W)] for j in range(G)]
+        ref = brute.score_from_lse(qs, ks, N, G, scale, ls, causal)
+        np.testing.assert_allclose(s[0, h], ref, rtol=1e-12, atol=1e-300)

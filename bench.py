@@ -17,6 +17,9 @@ in HBM before timing starts.  Prints one JSON line:
               summary under profiles/ and reported only while the kernel's
               sources still hash to the recorded value
   copy_gbps   a 1 GiB device-to-device copy (read + write bytes / time)
+  fidelity    output / log-sum-exp loss terms of the compacted cache
+              against the full cache for the step's decode queries (and,
+              fidelity_window_query, for the last window row of each head)
   score_one_pass  kv_score_from_lse (row LSEs given, as a prefill pass
               yields them): one sweep over K instead of two
   cpu_baseline the float64 oracle on a bounded sample on the host cores
@@ -39,7 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-from kv_cache_compression_score_amd import _lib, api  # noqa: E402
+from kv_cache_compression_score_amd import _lib, api, fidelity  # noqa: E402
 from kv_cache_compression_score_amd import workloads as wl  # noqa: E402
 
 METRIC = "cached tokens/sec scored+selected+compacted at 32K ctx; decode-attn HBM GB/s"
@@ -324,6 +327,19 @@ def main():
         "kernels_ms": {k: v[0] for k, v in kt.items()},
         "cpu_baseline": None,
     }
+    # Quality beside throughput: loss terms of the step's compacted cache
+    # against the full cache for the step's decode queries.
+    # Two query sets: the workload's i.i.d. decode queries, and the last
+    # window row of every query head (the window is the method's own proxy
+    # for the queries to come).
+    out_f, lse_f = fidelity.full_cache_decode(pipe.qd, pipe.k, pipe.v, pipe.c)
+    res["fidelity"] = fidelity.summary(fidelity.fidelity(pipe.out, pipe.lse, out_f, lse_f))
+    q_last = pipe.q[:, :, -1, :].contiguous()
+    out_w, lse_w = api.kv_decode_attn(q_last, pipe.comp[0], pipe.comp[1], pipe.comp[3],
+                                      cfg.Hkv, workspace=pipe.ws_d)
+    out_f, lse_f = fidelity.full_cache_decode(q_last, pipe.k, pipe.v, pipe.c)
+    res["fidelity_window_query"] = fidelity.summary(fidelity.fidelity(out_w, lse_w, out_f, lse_f))
+    del out_f, lse_f, out_w, lse_w
     if not args.no_cpu_baseline:
         log("bench: oracle baseline on the host")
         res["cpu_baseline"] = cpu_baseline(lay, min(args.cpu_seqs, B))

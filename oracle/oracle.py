@@ -353,3 +353,34 @@ def attend_full(q, k, v, ctx_len=None, scale=None):
             offsets[i + 1] = offsets[i] + n
             i += 1
     return decode(q, np.concatenate(rows_k), np.concatenate(rows_v), offsets, Hkv, scale)
+
+
+def fidelity(q, k, v, kept_idx, count, ctx_len=None, scale=None):
+    """Loss terms of "KVSculpt: KV Cache Compression as Distillation", section
+    2.B, for a compacted cache against the full one, over decode queries q
+    [B][Hq][d]: with Y, ell the attention output and log-sum-exp over the full
+    cache and Y^, ell^ over the kept rows,
+      out_err2[b, j] = ||Y^ - Y||^2,  lse_diff[b, j] = ell^ - ell,
+      loss = sum out_err2 + sum lse_diff^2   (the Frobenius norms squared).
+    Returns a dict of those plus out_norm2 = ||Y||^2.
+    """
+    kk = _f64(k)
+    vv = _f64(v)
+    idx = _ints(kept_idx)
+    cnt = _ints(count)
+    B, Hkv = kk.shape[0], kk.shape[1]
+    rows_k, rows_v = [], []
+    offsets = np.zeros(B * Hkv + 1, dtype=np.int64)
+    for b in range(B):
+        for h in range(Hkv):
+            i = b * Hkv + h
+            sel = idx[b, h, :int(cnt[i])]
+            rows_k.append(kk[b, h, sel])
+            rows_v.append(vv[b, h, sel])
+            offsets[i + 1] = offsets[i] + len(sel)
+    y_hat, l_hat = decode(q, np.concatenate(rows_k), np.concatenate(rows_v), offsets, Hkv, scale)
+    y, ell = attend_full(q, k, v, ctx_len, scale)
+    err2 = ((y_hat - y) ** 2).sum(axis=-1)
+    dl = l_hat - ell
+    return {"out_err2": err2, "out_norm2": (y ** 2).sum(axis=-1), "lse_diff": dl,
+            "loss": float(err2.sum() + (dl ** 2).sum())}

@@ -252,3 +252,44 @@ def test_protected_zero_is_plain_selection():
         a = orc.select(s, None, mode, **p)
         b = orc.select(s, None, mode, n_sink=0, n_recent=0, **p)
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---- fidelity of a compacted cache (output and log-sum-exp terms) ----------
+
+def test_fidelity_full_keep_is_zero():
+    rng = np.random.default_rng(31)
+    B, Hkv, G, N, d = 2, 2, 2, 30, 8
+    k = rng.standard_normal((B, Hkv, N, d)); v = rng.standard_normal((B, Hkv, N, d))
+    q = rng.standard_normal((B, Hkv * G, d))
+    ctx = [30, 17]
+    idx = np.tile(np.arange(N, dtype=np.int32), (B, Hkv, 1))
+    cnt = np.repeat(np.array(ctx, np.int32), Hkv)
+    f = orc.fidelity(q, k, v, idx, cnt, ctx)
+    assert np.abs(f["out_err2"]).max() < 1e-24 and np.abs(f["lse_diff"]).max() < 1e-12
+
+
+def test_fidelity_matches_brute_force():
+    # exp(l^ - l) is the full softmax mass on the kept rows (so l^ <= l), and
+    # Y^ is attention over the kept rows alone: both from pure-Python loops.
+    rng = np.random.default_rng(32)
+    B, Hkv, G, N, d = 1, 2, 2, 12, 4
+    k = rng.standard_normal((B, Hkv, N, d)); v = rng.standard_normal((B, Hkv, N, d))
+    q = rng.standard_normal((B, Hkv * G, d))
+    s = rng.random((B, Hkv, N))
+    idx, cnt = orc.select(s, None, orc.BUDGET_K, k=5)
+    f = orc.fidelity(q, k, v, idx, cnt)
+    scale = 1.0 / math.sqrt(d)
+    for h in range(Hkv):
+        kept = idx[0, h, :5].tolist()
+        for g in range(G):
+            j = h * G + g
+            y, l = brute.attend(list(q[0, j]), [list(r) for r in k[0, h]], [list(r) for r in v[0, h]], scale)
+            yh, lh = brute.attend(list(q[0, j]), [list(k[0, h, t]) for t in kept],
+                                  [list(v[0, h, t]) for t in kept], scale)
+            u = [scale * math.fsum(a * b for a, b in zip(q[0, j], k[0, h, t])) for t in range(N)]
+            mass = math.fsum(math.exp(u[t] - l) for t in kept)
+            assert f["lse_diff"][0, j] <= 0.0
+            assert math.isclose(math.exp(f["lse_diff"][0, j]), mass, rel_tol=1e-12)
+            assert math.isclose(f["lse_diff"][0, j], lh - l, abs_tol=1e-12)
+            assert math.isclose(f["out_err2"][0, j], math.fsum((a - b) ** 2 for a, b in zip(yh, y)),
+                                rel_tol=1e-10, abs_tol=1e-24)

@@ -126,6 +126,26 @@ struct OpAdd { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { re
 struct OpMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
 struct OpMax { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
 
+// Sum over aligned groups of L lanes (L = 2, 4, ..., 32), result in every
+// lane of the group.  DPP moves on the VALU: quad_perm swaps lanes 1 and 2
+// apart, then the half-row mirror (lane i <-> 7-i) joins the two quads of an
+// 8-lane group and the row mirror (i <-> 15-i) the two halves of a 16-lane
+// row; 32-lane groups add the other row with one cross-row swizzle.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int L>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(L >= 2 && L <= 32 && (L & (L - 1)) == 0, "group of 2..32 lanes");
+  x += dpp_f32<0xB1>(x);                       // quad_perm [1,0,3,2]
+  if constexpr (L >= 4) x += dpp_f32<0x4E>(x);  // quad_perm [2,3,0,1]
+  if constexpr (L >= 8) x += dpp_f32<0x141>(x); // row_half_mirror
+  if constexpr (L >= 16) x += dpp_f32<0x140>(x); // row_mirror
+  if constexpr (L >= 32) x += __shfl_xor(x, 16, WAVE);
+  return x;
+}
+
 // Value of lane 63 (the total of an inclusive scan), wave-uniform.
 __device__ __forceinline__ uint32_t last_lane(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, WAVE - 1);

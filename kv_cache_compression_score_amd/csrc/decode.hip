@@ -10,8 +10,8 @@
 // rebuilds the item list from the offsets in LDS and walks it grid-stride,
 // so ragged heads balance by rows, not by head count.  Inside an item a group
 // of d*sizeof(T)/16 lanes owns one row at a time (16 bytes of K and of V per
-// lane, RPG rows in flight), forms the G dot products with a butterfly
-// reduction inside the group, and keeps a base-2 (max, sum, o) per query
+// lane, RPG rows in flight), forms the G dot products with a DPP reduction
+// inside the group, and keeps a base-2 (max, sum, o) per query
 // head.  Groups merge through LDS in a fixed order into one partial per item;
 // a second kernel merges each head's items in item order, so the result is
 // deterministic.
@@ -24,6 +24,8 @@ namespace {
 
 constexpr int DT = 256;
 constexpr int CH = 128;          // rows per work item
+constexpr int RPG = 8;           // rows per lane group per pass over an item
+constexpr bool PERSISTENT = false;   // grid = resident workgroups, items walked grid-stride
 constexpr int MAX_HEADS = 4096;
 
 struct DecodeArgs {
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
   constexpr int EPL = 16 / (int)sizeof(T);     // elements per lane
   constexpr int LPR = D / EPL;                 // lanes per row (power of two, <= 32)
   constexpr int NG = DT / LPR;                 // row groups per workgroup
-  constexpr int RPG = (CH + NG - 1) / NG;      // rows per group per item
+  constexpr int PASS = NG * RPG;               // rows per pass over an item
   constexpr int ROWB = D * (int)sizeof(T);
 
   __shared__ int wtot[DT / WAVE];
@@ -140,57 +142,66 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
       }
     }
 
-    uint4 kr[RPG], vr[RPG];
-#pragma unroll
-    for (int u = 0; u < RPG; ++u) {
-      const long long row = r0 + grp + (long long)u * NG;
-      kr[u] = make_uint4(0, 0, 0, 0);
-      vr[u] = make_uint4(0, 0, 0, 0);
-      if (row < r1) {
-        kr[u] = ld16(a.kc + (size_t)row * ROWB + sub * 16);
-        vr[u] = ld16(a.vc + (size_t)row * ROWB + sub * 16);
-      }
-    }
-
-    float sc[RPG][GT];
-#pragma unroll
-    for (int u = 0; u < RPG; ++u) {
-      float kx[EPL];
-      unpack16<T>(kr[u], kx);
-#pragma unroll
-      for (int g = 0; g < GT; ++g) {
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) s = fmaf(qv[g][e], kx[e], s);
-#pragma unroll
-        for (int o = LPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, WAVE);
-        sc[u][g] = s;
-      }
-    }
-
     float mg[GT], lg[GT], og[GT][EPL];
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < RPG; ++u)
-        if (r0 + grp + (long long)u * NG < r1) m = fmaxf(m, sc[u][g]);
-      mg[g] = m;
+      mg[g] = -INFINITY;
       lg[g] = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) og[g][e] = 0.f;
     }
+    for (long long base = r0; base < r1; base += PASS) {
+      uint4 kr[RPG], vr[RPG];
 #pragma unroll
-    for (int u = 0; u < RPG; ++u) {
-      if (r0 + grp + (long long)u * NG < r1) {
-        float vx[EPL];
-        unpack16<T>(vr[u], vx);
+      for (int u = 0; u < RPG; ++u) {
+        const long long row = base + grp + (long long)u * NG;
+        kr[u] = make_uint4(0, 0, 0, 0);
+        vr[u] = make_uint4(0, 0, 0, 0);
+        if (row < r1) {
+          kr[u] = ld16(a.kc + (size_t)row * ROWB + sub * 16);
+          vr[u] = ld16(a.vc + (size_t)row * ROWB + sub * 16);
+        }
+      }
+      float sc[RPG][GT];
+#pragma unroll
+      for (int u = 0; u < RPG; ++u) {
+        float kx[EPL];
+        unpack16<T>(kr[u], kx);
 #pragma unroll
         for (int g = 0; g < GT; ++g) {
-          const float p = fast_exp2(sc[u][g] - mg[g]);
-          lg[g] += p;
+          float s = 0.f;
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) og[g][e] = fmaf(p, vx[e], og[g][e]);
+          for (int e = 0; e < EPL; ++e) s = fmaf(qv[g][e], kx[e], s);
+          sc[u][g] = group_sum<LPR>(s);
+        }
+      }
+      // online merge of this pass into the group's running (max, sum, o)
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        float m = mg[g];
+#pragma unroll
+        for (int u = 0; u < RPG; ++u)
+          if (base + grp + (long long)u * NG < r1) m = fmaxf(m, sc[u][g]);
+        if (m != -INFINITY && m != mg[g]) {
+          const float w = fast_exp2(mg[g] - m);   // 0 when mg was -inf
+          lg[g] *= w;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) og[g][e] *= w;
+          mg[g] = m;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < RPG; ++u) {
+        if (base + grp + (long long)u * NG < r1) {
+          float vx[EPL];
+          unpack16<T>(vr[u], vx);
+#pragma unroll
+          for (int g = 0; g < GT; ++g) {
+            const float p = fast_exp2(sc[u][g] - mg[g]);
+            lg[g] += p;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) og[g][e] = fmaf(p, vx[e], og[g][e]);
+          }
         }
       }
     }
@@ -227,7 +238,7 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
 // are batched so a head's items are fetched a few at a time, not one by one.
 template <int D, int GT>
 __global__ __launch_bounds__(GT * D) void decode_merge(DecodeArgs a) {
-  constexpr int U = 16;
+  constexpr int U = 32;
   const int head = blockIdx.x, qsub = blockIdx.y;
   const int b = head / a.Hkv, h = head % a.Hkv;
   const int i0 = a.item_start[head], i1 = a.item_start[head + 1];
@@ -287,10 +298,23 @@ bool plan_decode(int B, int Hq, int Hkv, int d, int64_t cap, DecodePlan* p) {
   return true;
 }
 
+// Resident workgroups of a kernel on the current device.
+template <typename K>
+int resident_slots(K kernel, int threads, size_t dyn) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dyn) != hipSuccess ||
+      cus < 1 || per_cu < 1)
+    return 8192;
+  return cus * per_cu;
+}
+
 template <typename T, int D, int GT>
 void launch_decode(const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)std::min(a.items_max, 8192), a.n_sub);
   const size_t dyn = (size_t)(a.B * a.Hkv + 1) * (sizeof(long long) + sizeof(int));
+  const int gx = PERSISTENT ? resident_slots(decode_split<T, D, GT>, DT, dyn) : 8192;
+  const dim3 grid((unsigned)std::min(a.items_max, gx), a.n_sub);
   {
     TimedLaunch t("decode_split", st);
     decode_split<T, D, GT><<<grid, DT, dyn, st>>>(a);

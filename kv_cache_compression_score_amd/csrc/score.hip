@@ -39,6 +39,7 @@ constexpr int TOK = 64;          // tokens per LDS tile
 constexpr int TSUB = TOK / 32;   // 32-token MFMA blocks per tile
 constexpr int RBW = 2;           // 32-row blocks per wave
 constexpr int SLOTS_1 = 256 * 2; // pass-1 chunking target: resident workgroups on 256 CUs
+constexpr int NPF = 2;           // K tiles in flight per workgroup (register prefetch depth)
 
 template <typename T> struct FragT;
 template <> struct FragT<__bf16> { using vec = bf16x8; };   // 8 elements = 16 B
@@ -157,6 +158,7 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
   // Pass-1 running state (per row owned by the lane) / pass-2 negated row lse2.
   float m_run[RBW], s_run[RBW];
   float nl2[RBW][16];
+  const float inv_w = 1.0f / (float)a.W;
   if (PASS == 1) {
 #pragma unroll
     for (int i = 0; i < RBW; ++i) { m_run[i] = -INFINITY; s_run[i] = 0.f; }
@@ -168,8 +170,10 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
         const int r = (wave * RBW + i) * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
         float v;
         if (a.lse_in) {   // caller's natural-log LSE of row (j, w), to base 2
+          // rc / W by a float reciprocal: exact for rc < 1024 (error < 0.5/W)
           const int rc = min(r, a.R - 1);
-          const int j = h * a.G + rc / a.W, w = rc % a.W;
+          const int jw = (int)(((float)rc + 0.5f) * inv_w);
+          const int j = h * a.G + jw, w = rc - jw * a.W;
           v = a.lse_in[((size_t)b * a.Hq + j) * a.W + w] * (float)LOG2E_D;
         } else {
           v = a.lse2[(size_t)head * a.R_pad + min(r, a.R_pad - 1)];
@@ -179,25 +183,42 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
     }
   }
 
-  uint4 pre[LPT];
-  auto gload = [&](int tile) {
+  // K tiles in flight: tile t travels in register slot t % NPF (a compile-time
+  // index: the tile loop below is unrolled by NPF) until it is stored to LDS.
+  uint4 pre[NPF][LPT];
+  auto gload = [&](auto slot, int tile) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
     const int tt0 = t0 + tile * TOK;
     const int rows = min(TOK, t1 - tt0);
     const char* base = kh + (size_t)tt0 * ROWB;
+    if (rows == TOK) {   // full tile: fixed per-thread offsets
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int v = tid + i * NT;
-      const int row = v / VPR;
-      pre[i] = (v < TILE_VECS && row < rows) ? ld16(base + (size_t)v * 16) : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < LPT; ++i) {
+        const int v = tid + i * NT;
+        if (v < TILE_VECS) pre[S][i] = ld16(base + (size_t)v * 16);
+      }
+    } else {
+      // rows past the chunk end re-read its last row: their tokens are
+      // masked (pass 1) or never written (pass 2), so no select is needed
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int v = tid + i * NT;
+        if (v < TILE_VECS) {
+          const int row = min(v / VPR, rows - 1);
+          pre[S][i] = ld16(base + ((size_t)row * VPR + v % VPR) * 16);
+        }
+      }
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](auto slot, auto bufc) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
+    constexpr int buf = decltype(bufc)::value;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int v = tid + i * NT;
       if (v < TILE_VECS) {
         const int row = v / VPR, col = v % VPR;
-        *reinterpret_cast<uint4*>(&ktile[buf][row * LDS_STRIDE + col * 16]) = pre[i];
+        *reinterpret_cast<uint4*>(&ktile[buf][row * LDS_STRIDE + col * 16]) = pre[S][i];
       }
     }
   };
@@ -216,7 +237,8 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
   // per-epilogue scratch (pass 1)
   float e_nm = 0.f, e_sum = 0.f, e_mn = 0.f;
 
-  auto load_k = [&](int buf, int sub) __attribute__((always_inline)) {
+  auto load_k = [&](auto bufc, int sub) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
     const unsigned char* krow = &ktile[buf][(sub * 32 + l32) * LDS_STRIDE + 8 * hf * sizeof(T)];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kf[ks] = load_frag<T>(krow + ks * 16 * sizeof(T));
@@ -244,24 +266,27 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
           for (int e = 0; e < 16; ++e)
             acc[i][e] = (8 * (e >> 2) + (e & 3)) > lim ? -INFINITY : acc[i][e];
         }
-        e_mn = fmaxf(fmaxf(acc[i][0], acc[i][1]), fmaxf(acc[i][2], acc[i][3]));
-        e_mn = fmaxf(e_mn, fmaxf(acc[i][4], acc[i][5]));
-        e_mn = fmaxf(e_mn, fmaxf(acc[i][6], acc[i][7]));
+        // three-input maxima (v_max3): 16 values in 8 instructions
+        const float a0 = fmaxf(acc[i][0], fmaxf(acc[i][1], acc[i][2]));
+        const float a1 = fmaxf(acc[i][3], fmaxf(acc[i][4], acc[i][5]));
+        const float a2 = fmaxf(acc[i][6], fmaxf(acc[i][7], acc[i][8]));
+        e_mn = fmaxf(a0, fmaxf(a1, a2));
       } else if (q == 1) {
-        e_mn = fmaxf(e_mn, fmaxf(acc[i][8], acc[i][9]));
-        e_mn = fmaxf(e_mn, fmaxf(acc[i][10], acc[i][11]));
-        e_mn = fmaxf(e_mn, fmaxf(acc[i][12], acc[i][13]));
-        e_mn = fmaxf(e_mn, fmaxf(acc[i][14], acc[i][15]));
+        const float a3 = fmaxf(acc[i][9], fmaxf(acc[i][10], acc[i][11]));
+        const float a4 = fmaxf(acc[i][12], fmaxf(acc[i][13], acc[i][14]));
+        e_mn = fmaxf(acc[i][15], fmaxf(a3, fmaxf(a4, e_mn)));
         e_mn = fmaxf(m_run[i], e_mn * cc);
         // a fully masked row keeps (-inf, 0): exp2(-inf - 0) = 0 everywhere
         e_nm = MASKED && e_mn == -INFINITY ? 0.f : -e_mn;
-        e_sum = 0.f;
       } else {
         // slots 2..7 take 3,3,3,3,2,2 of the 16 exponentials
         constexpr int lo_tab[9] = {0, 0, 0, 3, 6, 9, 12, 14, 16};
         const int lo = lo_tab[q], hi = lo_tab[q + 1];
 #pragma unroll
-        for (int e = lo; e < hi; ++e) e_sum += fast_exp2(fmaf(acc[i][e], cc, e_nm));
+        for (int e = lo; e < hi; ++e) {
+          const float x = fast_exp2(fmaf(acc[i][e], cc, e_nm));
+          e_sum = e == 0 ? x : e_sum + x;
+        }
         if (q == 7) {
           s_run[i] = fmaf(s_run[i], fast_exp2(m_run[i] + e_nm), e_sum);
           m_run[i] = e_mn;
@@ -307,7 +332,11 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
   };
   auto emit_col = [&](int tile, int sub) __attribute__((always_inline)) {   // pass 2: block column sums -> LDS
     if (PASS == 2) {
-      const float c2 = col_cur + __shfl_xor(col_cur, 32, WAVE);   // other half-wave's rows
+      // other half-wave's rows: v_permlane32_swap hands each lane the value
+      // of lane l^32 (both halves of the result sum to col(l) + col(l^32))
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(col_cur),
+                                                       __float_as_uint(col_cur), false, false);
+      const float c2 = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       if (hf == 0) red[tile % 3][wave][sub * 32 + l32] = c2;
       col_cur = 0.f;
     }
@@ -325,35 +354,50 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
   };
   auto masked_tile = [&](int tile) { return tile >= clean_tiles; };
 
-  gload(0);
-  sstore(0);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1 % NPF>;
+  gload(S0{}, 0);
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  sstore(S0{}, B0{});
   __syncthreads();
-  if (ntiles > 1) gload(1);
+  // tiles 1..NPF in flight (tile j in slot j % NPF)
+  if (ntiles > 1) gload(S1{}, 1);
+  if (ntiles > 2) gload(S0{}, 2);
   // tile 0
-  load_k(0, 0);
+  load_k(B0{}, 0);
   step_m(T_{}, I0{}, F_{}, I1{}, 0, false);                     // MMA(0, r0)
   step_m(T_{}, I1{}, T_{}, I0{}, t0, masked_tile(0));           // MMA(0, r1) | epi(0, r0)
-  load_k(0, 1);
+  load_k(B0{}, 1);
   step_m(T_{}, I0{}, T_{}, I1{}, t0, masked_tile(0));           // MMA(1, r0) | epi(0, r1)
   emit_col(0, 0);
   step_m(T_{}, I1{}, T_{}, I0{}, t0 + 32, masked_tile(0));      // MMA(1, r1) | epi(1, r0)
-  if (ntiles > 1) sstore(1);
+  if (ntiles > 1) sstore(S1{}, B1{});
   __syncthreads();
-  for (int tile = 1; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
+  // Tile t: load tile t+NPF into t's (now free) slot, run the tile, store tile
+  // t+1 (slot (t+1) % NPF) to the other LDS buffer.
+  // (bc: this tile's LDS buffer, tile & 1, fixed per call site since NPF is even)
+  auto tile_body = [&](auto ls, auto ss, auto bc, int tile) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bc)::value;
+    using BN = std::integral_constant<int, 1 - buf>;
     const int tt0 = t0 + tile * TOK;
-    if (tile + 1 < ntiles) gload(tile + 1);
-    load_k(buf, 0);
+    if (tile + NPF < ntiles) gload(ls, tile + NPF);
+    load_k(bc, 0);
     step_m(T_{}, I0{}, T_{}, I1{}, tt0 - 32, masked_tile(tile - 1));  // MMA(2t, r0) | epi(2t-1, r1)
     emit_col(tile - 1, 1);
     step_m(T_{}, I1{}, T_{}, I0{}, tt0, masked_tile(tile));           // MMA(2t, r1) | epi(2t, r0)
-    load_k(buf, 1);
+    load_k(bc, 1);
     step_m(T_{}, I0{}, T_{}, I1{}, tt0, masked_tile(tile));           // MMA(2t+1, r0) | epi(2t, r1)
     emit_col(tile, 0);
     step_m(T_{}, I1{}, T_{}, I0{}, tt0 + 32, masked_tile(tile));      // MMA(2t+1, r1) | epi(2t+1, r0)
-    if (tile + 1 < ntiles) sstore((tile + 1) & 1);
+    if (tile + 1 < ntiles) sstore(ss, BN{});
     __syncthreads();
     reduce_tile(tile - 1);
+  };
+  static_assert(NPF == 2, "the unrolled tile loop assumes two slots (and LDS buffer = tile parity)");
+  for (int tile = 1; tile < ntiles; tile += 2) {
+    tile_body(S1{}, S0{}, B1{}, tile);
+    if (tile + 1 < ntiles) tile_body(S0{}, S1{}, B0{}, tile + 1);
   }
   // drain: the last block's second row block
   step_m(F_{}, I0{}, T_{}, I1{}, t0 + (ntiles - 1) * TOK + 32, masked_tile(ntiles - 1));

@@ -138,3 +138,28 @@ def attend(q, k_rows, v_rows, scale: float):
     d = len(v_rows[0])
     out = [math.fsum(e[i] * v_rows[i][c] for i in range(len(e))) / z for c in range(d)]
     return out, m + math.log(z)
+
+
+def rope_rotate(x, pos: int, base: float, sign: float):
+    """Rotate adjacent pairs (2i, 2i+1) of a list by sign * pos * base^(-2i/d)."""
+    d = len(x)
+    out = list(x)
+    if base == 0.0:
+        return out
+    for i in range(d // 2):
+        a = sign * pos * base ** (-2.0 * i / d)
+        c, s_ = math.cos(a), math.sin(a)
+        out[2 * i] = x[2 * i] * c - x[2 * i + 1] * s_
+        out[2 * i + 1] = x[2 * i] * s_ + x[2 * i + 1] * c
+    return out
+
+
+def residual(v_row, k_row, w, pos: int, base: float):
+    """||v - w * rotate(k, -pos)||^2 with explicit loops (w: list of rows)."""
+    kr = rope_rotate(k_row, pos, base, -1.0)
+    d = len(v_row)
+    terms = []
+    for o in range(d):
+        rec = math.fsum(w[o][i] * kr[i] for i in range(d))
+        terms.append((v_row[o] - rec) ** 2)
+    return math.fsum(terms)

@@ -384,3 +384,113 @@ def fidelity(q, k, v, kept_idx, count, ctx_len=None, scale=None):
     dl = l_hat - ell
     return {"out_err2": err2, "out_norm2": (y ** 2).sum(axis=-1), "lse_diff": dl,
             "loss": float(err2.sum() + (dl ** 2).sum())}
+
+
+# ---- VECTOR three-way routing ----------------------------------------------
+#
+# "A Simple Plug-in for Improving Eviction-Based KV Cache Compression"
+# (VECTOR), section "Methodologie: VECTOR" / "Pipeline d'Allocation en Trois
+# Voies": for a target removed fraction p_c and an approximated fraction p_a,
+# the base eviction score picks an enlarged pool of 1 - p_c + p_a of the
+# tokens; each pool token's reconstruction residual eps = ||V - W RoPE^-1(K)||^2
+# is computed with an offline linear map W (keys rotated back to position 0
+# first); keys are kept for the whole pool, the 2 p_a lowest-residual tokens
+# drop their values (rebuilt as W RoPE^-1(K) on use), and the remaining
+# 1 - p_c - p_a keep exact K and V.  Readings: counts are
+# k_pool = clamp(floor((1 - p_c + p_a) n + 1/2), 1, n) and
+# k_apx = min(k_pool, floor(2 p_a n + 1/2)) (p_c, p_a fp32, arithmetic in
+# float64); rotary position encoding rotates adjacent pairs (2i, 2i+1) by
+# pos * base^(-2i/d) (base = 0: no rotation); ties in eps go to the lower
+# token index.
+
+def rope_inverse(x, pos, base: float):
+    """Rotate each adjacent pair (2i, 2i+1) of rows x [m][d] back by
+    pos[m] * base^(-2i/d) (the inverse of rotary position encoding)."""
+    x = _f64(x)
+    if base == 0.0:
+        return x.copy()
+    m, d = x.shape
+    i = np.arange(d // 2, dtype=np.float64)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * base ** (-2.0 * i / d)[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    xe, xo = x[:, 0::2], x[:, 1::2]
+    out = np.empty_like(x)
+    out[:, 0::2] = xe * c + xo * s
+    out[:, 1::2] = -xe * s + xo * c
+    return out
+
+
+def vector_counts(n: int, p_c: float, p_a: float):
+    """(k_pool, k_apx) of a head with n tokens."""
+    pc, pa = float(np.float32(p_c)), float(np.float32(p_a))
+    k_pool = int(min(max(math.floor((1.0 - pc + pa) * n + 0.5), 1), n))
+    k_apx = int(min(k_pool, math.floor(2.0 * pa * n + 0.5)))
+    return k_pool, k_apx
+
+
+def vector_residuals(k, v, w, pool_idx, pool_count, rope_base: float = 0.0):
+    """eps[b][h][j] = ||V_t - W_h RoPE^-1(K_t)||^2 for pool entry j (token
+    t = pool_idx[b,h,j], position t), +inf beyond the pool.  w [Hkv][d][d]
+    maps a de-rotated key to a value (out = w @ in)."""
+    kk, vv, ww = _f64(k), _f64(v), _f64(w)
+    idx, cnt = _ints(pool_idx), _ints(pool_count)
+    B, Hkv, N_max, d = kk.shape
+    eps = np.full((B, Hkv, N_max), np.inf)
+    for b in range(B):
+        for h in range(Hkv):
+            c = int(cnt[b * Hkv + h])
+            t = idx[b, h, :c]
+            kt = rope_inverse(kk[b, h, t], t, rope_base)
+            r = vv[b, h, t] - kt @ ww[h].T
+            eps[b, h, :c] = (r * r).sum(axis=1)
+    return eps
+
+
+def vector_route(scores, k, v, w, ctx_len=None, p_c: float = 0.9, p_a: float = 0.05,
+                 rope_base: float = 0.0):
+    """Pool, residuals and the approximated subset of every head.
+
+    Returns (pool_idx, pool_count, eps, apx) with pool_idx/pool_count as
+    ``select`` at the pool ratio, eps as ``vector_residuals`` and apx
+    [B][Hkv][N_max] bool: True for the pool entries whose value is dropped.
+    """
+    s_all = _f64(scores)
+    B, Hkv, N_max = s_all.shape
+    ctx = _ctx(ctx_len, B, N_max)
+    kp = np.array([vector_counts(int(ctx[b]), p_c, p_a)[0] for b in range(B)
+                   for _ in range(Hkv)], dtype=np.int64)
+    pool_idx, pool_count = select(s_all, ctx, BUDGET_K, k=kp)
+    eps = vector_residuals(k, v, w, pool_idx, pool_count, rope_base)
+    apx = np.zeros((B, Hkv, N_max), dtype=bool)
+    for b in range(B):
+        ka = vector_counts(int(ctx[b]), p_c, p_a)[1]
+        for h in range(Hkv):
+            c = int(pool_count[b * Hkv + h])
+            # lowest residual first, lower token index (= lower pool entry) on ties
+            order = np.lexsort((np.arange(c), eps[b, h, :c]))
+            apx[b, h, order[:ka]] = True
+    return pool_idx, pool_count, eps, apx
+
+
+def vector_decode(q, k, v, w, pool_idx, pool_count, apx, Hkv: int, rope_base: float = 0.0,
+                  scale=None):
+    """Decode over the routed cache: every pool row's key, its exact value or,
+    for approximated entries, W RoPE^-1(K).  Returns (out, lse) as ``decode``."""
+    kk, vv, ww = _f64(k), _f64(v), _f64(w)
+    idx, cnt = _ints(pool_idx), _ints(pool_count)
+    B = kk.shape[0]
+    rows_k, rows_v = [], []
+    offsets = np.zeros(B * Hkv + 1, dtype=np.int64)
+    for b in range(B):
+        for h in range(Hkv):
+            i = b * Hkv + h
+            c = int(cnt[i])
+            t = idx[b, h, :c]
+            val = vv[b, h, t].copy()
+            a = np.asarray(apx[b, h, :c], dtype=bool)
+            if a.any():
+                val[a] = rope_inverse(kk[b, h, t[a]], t[a], rope_base) @ ww[h].T
+            rows_k.append(kk[b, h, t])
+            rows_v.append(val)
+            offsets[i + 1] = offsets[i] + c
+    return decode(q, np.concatenate(rows_k), np.concatenate(rows_v), offsets, Hkv, scale)

@@ -229,6 +229,67 @@ int kv_decode_attn(const void* q, const void* k_c, const void* v_c, const int64_
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------
+ * VECTOR three-way routing: retain, approximate or evict.
+ *
+ * "A Simple Plug-in for Improving Eviction-Based KV Cache Compression"
+ * (VECTOR), section "Methodologie: VECTOR": for a removed fraction p_c and
+ * an approximated fraction p_a, the scores pick an enlarged pool of
+ *   k_pool = clamp(floor((1 - p_c + p_a) n + 1/2), 1, n)
+ * tokens per head (first k_pool of the kv_select order); each pool token t
+ * gets eps_t = ||V_t - W_h RoPE^-1(K_t)||^2, with W_h an offline linear map
+ * (out = W_h in) and RoPE^-1 turning each adjacent pair (2i, 2i+1) back by
+ * t * rope_base^(-2i/d) (rope_base 0: no rotation); the
+ *   k_apx = min(k_pool, floor(2 p_a n + 1/2))
+ * pool tokens of lowest eps (ties: lower token index) keep their key but
+ * drop their value, rebuilt as W_h RoPE^-1(K_t) when decode reads it; the
+ * other pool tokens keep K and V.  Count arithmetic is float64 on the fp32
+ * fractions.
+ * ---------------------------------------------------------------------- */
+
+/* kv_vector_route: pool, residuals and the approximated subset.
+ * scores, ctx_len   as kv_select; k, v [B][Hkv][N_max][d] dtype;
+ * w                 [Hkv][d][d] fp32 device, row-major (out index first)
+ * pool_idx, pool_count  out, as kv_select's kept_idx / kept_count
+ * neg_eps           [B][Hkv][N_max] fp32 out: -eps of pool entry j at j,
+ *                   -inf for j >= pool_count
+ * apx_pos, apx_count    out: per head the ascending pool-entry positions j
+ *                   (indices into that head's pool list) whose value is
+ *                   dropped, and how many (may be 0)
+ * workspace         kv_vector_route_workspace_size(B, Hkv) bytes
+ * Errors: KV_ERR_MODE if p_c, p_a are outside [0, 1] or rope_base < 0. */
+size_t kv_vector_route_workspace_size(int B, int Hkv);
+int kv_vector_route(const float* scores, const int32_t* ctx_len, const void* k, const void* v,
+                    const float* w, int B, int Hkv, int N_max, int d, int dtype, float p_c,
+                    float p_a, float rope_base, int32_t* pool_idx, int32_t* pool_count,
+                    float* neg_eps, int32_t* apx_pos, int32_t* apx_count, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* kv_vector_compact: the routed cache.  Key rows for every pool token, packed
+ * (b, h) row-major as kv_compact (offsets, pos, k_c), value rows only for
+ * the tokens that keep them, packed the same way (voffsets, v_c), and
+ *   vmap[r] = the v_c row of key row r, or -1 when its value is rebuilt.
+ * Key rows past capacity_rows and value rows past v_capacity_rows are not
+ * written; offsets and voffsets always hold the true prefix sums, so the
+ * caller detects overflow after the stream reaches this point. */
+int kv_vector_compact(const void* k, const void* v, int B, int Hkv, int N_max, int d, int dtype,
+                      const int32_t* pool_idx, const int32_t* pool_count, const int32_t* apx_pos,
+                      const int32_t* apx_count, void* k_c, void* v_c, int32_t* pos,
+                      int32_t* vmap, int64_t* offsets, int64_t* voffsets,
+                      int64_t capacity_rows, int64_t v_capacity_rows, void* stream);
+
+/* kv_vector_decode: decode attention over the routed cache, as
+ * kv_decode_attn with each row's value taken from v_c[vmap[r]] or, for
+ * vmap[r] < 0, rebuilt as W_h RoPE^-1(k_c[r]) at position pos[r].  The
+ * rebuilt rows enter as W_h (sum_r p_r RoPE^-1(k_c[r])), one d x d product
+ * per query head.  workspace: kv_vector_decode_workspace_size() bytes. */
+size_t kv_vector_decode_workspace_size(int B, int Hq, int Hkv, int d, int64_t capacity_rows);
+int kv_vector_decode(const void* q, const void* k_c, const void* v_c, const int32_t* vmap,
+                     const int32_t* pos, const int64_t* offsets, const float* w, float rope_base,
+                     int B, int Hq, int Hkv, int d, int dtype, float scale,
+                     int64_t capacity_rows, int64_t v_capacity_rows, float* out, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------------
  * Measurement hook (not part of the method): per-kernel GPU time.
  *
  * kv_timing_enable(1) clears earlier records and makes every kernel the
@@ -239,7 +300,9 @@ int kv_decode_attn(const void* q, const void* k_c, const void* v_c, const int64_
  * kernels (or a negative kv_status).  kv_timing_only(name) restricts the
  * recording to launches of that kernel name (one of "score_rowstats",
  * "score_fold", "score_colsum", "select", "compact", "decode_split",
- * "decode_merge"); NULL or "" records every launch.  The name is copied.
+ * "decode_merge", "vector_counts", "vector_pool", "vector_residual",
+ * "vector_apx", "vector_vmap", "vector_copy", "vector_decode_split",
+ * "vector_decode_merge"); NULL or "" records every launch.  The name is copied.
  * Timing adds event records between launches, so it is meant for
  * measurement runs, not production.
  * ---------------------------------------------------------------------- */

@@ -43,6 +43,20 @@ PROTOTYPES = {
                                c_int, c_int, c_int, c_int, c_int, c_float, c_int64,
                                c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "kv_status_string": (ctypes.c_char_p, [c_int]),
+    "kv_vector_route_workspace_size": (c_size_t, [c_int, c_int]),
+    "kv_vector_route": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                c_int, c_int, c_int, c_int, c_int, c_float, c_float, c_float,
+                                c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                c_void_p, c_size_t, c_void_p]),
+    "kv_vector_compact": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
+                                  c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int64,
+                                  c_void_p]),
+    "kv_vector_decode_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int, c_int64]),
+    "kv_vector_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_float, c_int, c_int, c_int, c_int, c_int, c_float,
+                                 c_int64, c_int64, c_void_p, c_void_p, c_void_p, c_size_t,
+                                 c_void_p]),
     "kv_timing_enable": (c_int, [c_int]),
     "kv_timing_only": (c_int, [ctypes.c_char_p]),
     "kv_timing_read": (c_int, [ctypes.POINTER(KvKernelTime), c_int]),

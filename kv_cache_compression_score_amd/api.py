@@ -182,3 +182,73 @@ def kv_decode_attn(q: torch.Tensor, k_c: torch.Tensor, v_c: torch.Tensor,
         _ptr(q), _ptr(k_c), _ptr(v_c), _ptr(offsets), B, Hq, Hkv, d, _dtype_code(q),
         float(scale), cap, _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))
     return out, lse
+
+
+# ---- VECTOR three-way routing ------------------------------------------------
+
+def kv_vector_route(scores: torch.Tensor, ctx_len: Optional[torch.Tensor], k: torch.Tensor,
+                    v: torch.Tensor, w: torch.Tensor, *, p_c: float, p_a: float,
+                    rope_base: float = 0.0):
+    """(pool_idx, pool_count, neg_eps, apx_pos, apx_count); see kv_vector_route in kvcc.h."""
+    _check(scores, "scores"); _check(k, "k"); _check(v, "v"); _check(w, "w")
+    B, Hkv, N_max, d = k.shape
+    if w.dtype != torch.float32 or tuple(w.shape) != (Hkv, d, d):
+        raise ValueError("w must be fp32 [Hkv][d][d]")
+    dev = k.device
+    pool_idx = torch.empty(B, Hkv, N_max, device=dev, dtype=torch.int32)
+    pool_count = torch.empty(B * Hkv, device=dev, dtype=torch.int32)
+    neg_eps = torch.empty(B, Hkv, N_max, device=dev, dtype=torch.float32)
+    apx_pos = torch.empty(B, Hkv, N_max, device=dev, dtype=torch.int32)
+    apx_count = torch.empty(B * Hkv, device=dev, dtype=torch.int32)
+    need = int(lib().kv_vector_route_workspace_size(B, Hkv))
+    ws = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
+    if ctx_len is not None:
+        _check(ctx_len, "ctx_len")
+    _call("kv_vector_route", lib().kv_vector_route(
+        _ptr(scores), _ptr(ctx_len), _ptr(k), _ptr(v), _ptr(w), B, Hkv, N_max, d, _dtype_code(k),
+        float(p_c), float(p_a), float(rope_base), _ptr(pool_idx), _ptr(pool_count), _ptr(neg_eps),
+        _ptr(apx_pos), _ptr(apx_count), _ptr(ws), ws.numel(), _stream()))
+    return pool_idx, pool_count, neg_eps, apx_pos, apx_count
+
+
+def kv_vector_compact(k: torch.Tensor, v: torch.Tensor, pool_idx: torch.Tensor,
+                      pool_count: torch.Tensor, apx_pos: torch.Tensor, apx_count: torch.Tensor,
+                      capacity_rows: int, v_capacity_rows: int):
+    """(k_c, v_c, pos, vmap, offsets, voffsets) of the routed cache."""
+    _check(k, "k"); _check(v, "v")
+    B, Hkv, N_max, d = k.shape
+    dev = k.device
+    k_c = torch.empty(capacity_rows, d, device=dev, dtype=k.dtype)
+    v_c = torch.empty(max(v_capacity_rows, 1), d, device=dev, dtype=k.dtype)
+    pos = torch.empty(capacity_rows, device=dev, dtype=torch.int32)
+    vmap = torch.empty(capacity_rows, device=dev, dtype=torch.int32)
+    offsets = torch.empty(B * Hkv + 1, device=dev, dtype=torch.int64)
+    voffsets = torch.empty(B * Hkv + 1, device=dev, dtype=torch.int64)
+    _call("kv_vector_compact", lib().kv_vector_compact(
+        _ptr(k), _ptr(v), B, Hkv, N_max, d, _dtype_code(k), _ptr(pool_idx), _ptr(pool_count),
+        _ptr(apx_pos), _ptr(apx_count), _ptr(k_c), _ptr(v_c), _ptr(pos), _ptr(vmap),
+        _ptr(offsets), _ptr(voffsets), int(capacity_rows), int(v_capacity_rows), _stream()))
+    return k_c, v_c, pos, vmap, offsets, voffsets
+
+
+def kv_vector_decode(q: torch.Tensor, k_c: torch.Tensor, v_c: torch.Tensor, vmap: torch.Tensor,
+                     pos: torch.Tensor, offsets: torch.Tensor, w: torch.Tensor, Hkv: int, *,
+                     v_capacity_rows: int, rope_base: float = 0.0, scale: float = 0.0,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None):
+    """Decode (out [B][Hq][d] fp32, lse [B][Hq] fp32) over the routed cache."""
+    _check(q, "q"); _check(k_c, "k_c"); _check(w, "w")
+    B, Hq, d = q.shape
+    cap = k_c.shape[0]
+    if out is None:
+        out = torch.empty(B, Hq, d, device=q.device, dtype=torch.float32)
+    if lse is None:
+        lse = torch.empty(B, Hq, device=q.device, dtype=torch.float32)
+    need = int(lib().kv_vector_decode_workspace_size(B, Hq, Hkv, d, cap))
+    if workspace is None:
+        workspace = torch.zeros(max(need, 1), device=q.device, dtype=torch.uint8)
+    _call("kv_vector_decode", lib().kv_vector_decode(
+        _ptr(q), _ptr(k_c), _ptr(v_c), _ptr(vmap), _ptr(pos), _ptr(offsets), _ptr(w),
+        float(rope_base), B, Hq, Hkv, d, _dtype_code(q), float(scale), cap, int(v_capacity_rows),
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))
+    return out, lse

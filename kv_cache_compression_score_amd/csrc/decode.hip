@@ -41,6 +41,14 @@ struct DecodeArgs {
   int* item_start;         // [B*Hkv+1] first item of every head (written by the split kernel)
   float* out;
   float* lse;
+  // routed cache (VECTOR): value row of key row r is vc[vmap[r]], or, when
+  // vmap[r] < 0, W RoPE^-1(k_c[r]) at position pos[r]
+  const int32_t* vmap;
+  const int32_t* pos;
+  const float* w;          // [Hkv][D][D]
+  float rope_base;
+  int64_t vcap;
+  float* part_u;           // [n_sub][items_max][GT][D]: sum of p * RoPE^-1(k) of rebuilt rows
 };
 
 // Row offsets clipped to the capacity, and the first item of every head.
@@ -95,7 +103,7 @@ __device__ __forceinline__ void unpack16<float>(const uint4 w, float* x) {
   x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
 }
 
-template <typename T, int D, int GT>
+template <typename T, int D, int GT, bool VEC>
 __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
   constexpr int EPL = 16 / (int)sizeof(T);     // elements per lane
   constexpr int LPR = D / EPL;                 // lanes per row (power of two, <= 32)
@@ -117,6 +125,14 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
     for (int i = threadIdx.x; i <= H; i += DT) a.item_start[i] = ist[i];
   const int tid = threadIdx.x, grp = tid / LPR, sub = tid % LPR;
   const int qsub = blockIdx.y;
+  // revolutions per position of this lane's rotary pairs (routed cache only)
+  double rope_g[VEC ? EPL / 2 : 1];
+  if constexpr (VEC) {
+    const double l2b = a.rope_base > 0.f ? log2((double)a.rope_base) : 0.0;
+#pragma unroll
+    for (int m2 = 0; m2 < EPL / 2; ++m2)
+      rope_g[m2] = exp2(-(2.0 * (sub * EPL / 2 + m2) / D) * l2b) * 0.15915494309189535;
+  }
 
   for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
     const int head = find_item_head(ist, H, it);
@@ -143,6 +159,7 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
     }
 
     float mg[GT], lg[GT], og[GT][EPL];
+    float ou[VEC ? GT : 1][EPL];
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
       mg[g] = -INFINITY;
@@ -150,16 +167,28 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) og[g][e] = 0.f;
     }
+#pragma unroll
+    for (int g = 0; g < (VEC ? GT : 1); ++g)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) ou[g][e] = 0.f;
     for (long long base = r0; base < r1; base += PASS) {
       uint4 kr[RPG], vr[RPG];
+      int vm[VEC ? RPG : 1], pp[VEC ? RPG : 1];
 #pragma unroll
       for (int u = 0; u < RPG; ++u) {
         const long long row = base + grp + (long long)u * NG;
         kr[u] = make_uint4(0, 0, 0, 0);
         vr[u] = make_uint4(0, 0, 0, 0);
+        if constexpr (VEC) { vm[u] = -1; pp[u] = 0; }
         if (row < r1) {
           kr[u] = ld16(a.kc + (size_t)row * ROWB + sub * 16);
-          vr[u] = ld16(a.vc + (size_t)row * ROWB + sub * 16);
+          if constexpr (VEC) {
+            vm[u] = a.vmap[row];
+            pp[u] = a.pos[row];
+            if (vm[u] >= 0 && vm[u] < a.vcap) vr[u] = ld16(a.vc + (size_t)vm[u] * ROWB + sub * 16);
+          } else {
+            vr[u] = ld16(a.vc + (size_t)row * ROWB + sub * 16);
+          }
         }
       }
       float sc[RPG][GT];
@@ -187,6 +216,10 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
           lg[g] *= w;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) og[g][e] *= w;
+          if constexpr (VEC) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) ou[g][e] *= w;
+          }
           mg[g] = m;
         }
       }
@@ -194,11 +227,37 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
       for (int u = 0; u < RPG; ++u) {
         if (base + grp + (long long)u * NG < r1) {
           float vx[EPL];
-          unpack16<T>(vr[u], vx);
+          bool rebuilt = false;
+          if constexpr (VEC) rebuilt = vm[u] < 0;
+          if (rebuilt) {
+            // de-rotated key: pairs (2i, 2i+1) of this lane's elements turn back
+            unpack16<T>(kr[u], vx);
+            if (a.rope_base > 0.f) {
+#pragma unroll
+              for (int m2 = 0; m2 < EPL / 2; ++m2) {
+                double r = (double)pp[u] * rope_g[m2];
+                r -= floor(r);
+                const float rv = (float)r;
+                const float s = __builtin_amdgcn_sinf(rv), c = __builtin_amdgcn_cosf(rv);
+                const float x = vx[2 * m2], y = vx[2 * m2 + 1];
+                vx[2 * m2] = x * c + y * s;
+                vx[2 * m2 + 1] = y * c - x * s;
+              }
+            }
+          } else {
+            unpack16<T>(vr[u], vx);
+          }
 #pragma unroll
           for (int g = 0; g < GT; ++g) {
             const float p = fast_exp2(sc[u][g] - mg[g]);
             lg[g] += p;
+            if constexpr (VEC) {
+              if (rebuilt) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) ou[g][e] = fmaf(p, vx[e], ou[g][e]);
+                continue;
+              }
+            }
 #pragma unroll
             for (int e = 0; e < EPL; ++e) og[g][e] = fmaf(p, vx[e], og[g][e]);
           }
@@ -207,56 +266,65 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
     }
 
     // merge the row groups (fixed order) into this item's partial
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      if (sub == 0) { sm_m[grp][g] = mg[g]; sm_l[grp][g] = lg[g]; }
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_o[grp][g][sub * EPL + e] = og[g][e];
-    }
-    __syncthreads();
     const size_t pbase = ((size_t)qsub * a.items_max + it) * GT;
-    for (int x = tid; x < GT * D; x += DT) {
-      const int g = x / D, e = x % D;
-      float M = -INFINITY;
-      for (int r = 0; r < NG; ++r) M = fmaxf(M, sm_m[r][g]);
-      float L = 0.f, O = 0.f;
-      if (M != -INFINITY) {
-        for (int r = 0; r < NG; ++r) {
-          const float w = fast_exp2(sm_m[r][g] - M);
-          L = fmaf(sm_l[r][g], w, L);
-          O = fmaf(sm_o[r][g][e], w, O);
-        }
+#pragma unroll
+    for (int half = 0; half < (VEC ? 2 : 1); ++half) {
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        if (half == 0 && sub == 0) { sm_m[grp][g] = mg[g]; sm_l[grp][g] = lg[g]; }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+          sm_o[grp][g][sub * EPL + e] = half == 0 ? og[g][e] : ou[VEC ? g : 0][e];
       }
-      a.part_o[(pbase + g) * D + e] = O;
-      if (e == 0) a.part_ml[pbase + g] = make_float2(M, L);
+      __syncthreads();
+      for (int x = tid; x < GT * D; x += DT) {
+        const int g = x / D, e = x % D;
+        float M = -INFINITY;
+        for (int r = 0; r < NG; ++r) M = fmaxf(M, sm_m[r][g]);
+        float L = 0.f, O = 0.f;
+        if (M != -INFINITY) {
+          for (int r = 0; r < NG; ++r) {
+            const float w = fast_exp2(sm_m[r][g] - M);
+            L = fmaf(sm_l[r][g], w, L);
+            O = fmaf(sm_o[r][g][e], w, O);
+          }
+        }
+        (half == 0 ? a.part_o : a.part_u)[(pbase + g) * D + e] = O;
+        if (half == 0 && e == 0) a.part_ml[pbase + g] = make_float2(M, L);
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
 // Per (head, query sub-group): merge the head's items in item order.  Loads
 // are batched so a head's items are fetched a few at a time, not one by one.
-template <int D, int GT>
+// Per (head, query sub-group): merge the head's items in item order, loads
+// batched 32 items at a time.  A routed cache also merges the rebuilt-row
+// sums U and adds W U (one d x d product per query head) before dividing.
+template <int D, int GT, bool VEC>
 __global__ __launch_bounds__(GT * D) void decode_merge(DecodeArgs a) {
   constexpr int U = 32;
+  __shared__ float su[VEC ? GT : 1][VEC ? D : 1];
   const int head = blockIdx.x, qsub = blockIdx.y;
   const int b = head / a.Hkv, h = head % a.Hkv;
   const int i0 = a.item_start[head], i1 = a.item_start[head + 1];
   const size_t base = (size_t)qsub * a.items_max;
-  {
-    const int x = threadIdx.x;
-    const int g = x / D, e = x % D, jg = qsub * GT + g;
-    if (jg >= a.G) return;
-    float M = -INFINITY, L = 0.f, O = 0.f;
+  const int x = threadIdx.x;
+  const int g = x / D, e = x % D, jg = qsub * GT + g;
+  const bool live = jg < a.G;
+  float M = -INFINITY, L = 0.f, O = 0.f, Uv = 0.f;
+  if (live) {
     for (int it0 = i0; it0 < i1; it0 += U) {
       float2 ml[U];
-      float ov[U];
+      float ov[U], uv[VEC ? U : 1];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const size_t p = (base + it0 + u) * GT + g;
         const bool ok = it0 + u < i1;
         ml[u] = ok ? a.part_ml[p] : make_float2(-INFINITY, 0.f);
         ov[u] = ok ? a.part_o[p * D + e] : 0.f;
+        if constexpr (VEC) uv[u] = ok ? a.part_u[p * D + e] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -265,22 +333,41 @@ __global__ __launch_bounds__(GT * D) void decode_merge(DecodeArgs a) {
         const float wa = exp2f(M - mn), wb = exp2f(ml[u].x - mn);
         L = L * wa + ml[u].y * wb;
         O = O * wa + ov[u] * wb;
+        if constexpr (VEC) Uv = Uv * wa + uv[u] * wb;
         M = mn;
       }
     }
-    const size_t bj = (size_t)b * a.Hq + h * a.G + jg;
-    const bool any = L > 0.f;
-    a.out[bj * D + e] = any ? O / L : 0.f;
-    if (a.lse && e == 0) a.lse[bj] = any ? (M + log2f(L)) * LN2_F : -INFINITY;
   }
+  if constexpr (VEC) {
+    su[g][e] = Uv;
+    __syncthreads();
+    if (live) {   // O += (W U)[e]: row e of W_h against this query head's U
+      const float4* wr = reinterpret_cast<const float4*>(a.w + ((size_t)h * D + e) * D);
+      float acc = 0.f;
+#pragma unroll 8
+      for (int i = 0; i < D / 4; ++i) {
+        const float4 wv = wr[i];
+        acc = fmaf(wv.x, su[g][4 * i], acc);
+        acc = fmaf(wv.y, su[g][4 * i + 1], acc);
+        acc = fmaf(wv.z, su[g][4 * i + 2], acc);
+        acc = fmaf(wv.w, su[g][4 * i + 3], acc);
+      }
+      O += acc;
+    }
+  }
+  if (!live) return;
+  const size_t bj = (size_t)b * a.Hq + h * a.G + jg;
+  const bool any = L > 0.f;
+  a.out[bj * D + e] = any ? O / L : 0.f;
+  if (a.lse && e == 0) a.lse[bj] = any ? (M + log2f(L)) * LN2_F : -INFINITY;
 }
 
 struct DecodePlan {
   int GT, n_sub, items_max;
-  size_t off_ml, off_ist, bytes;
+  size_t off_ml, off_ist, off_u, bytes;
 };
 
-bool plan_decode(int B, int Hq, int Hkv, int d, int64_t cap, DecodePlan* p) {
+bool plan_decode(int B, int Hq, int Hkv, int d, int64_t cap, DecodePlan* p, bool vec = false) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || (d != 64 && d != 128) || cap < 0 ||
       cap >= (int64_t(1) << 31) || (int64_t)B * Hkv > MAX_HEADS)
     return false;
@@ -295,6 +382,8 @@ bool plan_decode(int B, int Hq, int Hkv, int d, int64_t cap, DecodePlan* p) {
   p->off_ml = (po + 255) & ~size_t(255);
   p->off_ist = (p->off_ml + slots * sizeof(float2) + 255) & ~size_t(255);
   p->bytes = p->off_ist + ((size_t)B * Hkv + 1) * sizeof(int);
+  p->off_u = (p->bytes + 255) & ~size_t(255);
+  if (vec) p->bytes = p->off_u + po;
   return true;
 }
 
@@ -310,28 +399,39 @@ int resident_slots(K kernel, int threads, size_t dyn) {
   return cus * per_cu;
 }
 
-template <typename T, int D, int GT>
+template <typename T, int D, int GT, bool VEC>
 void launch_decode(const DecodeArgs& a, hipStream_t st) {
   const size_t dyn = (size_t)(a.B * a.Hkv + 1) * (sizeof(long long) + sizeof(int));
-  const int gx = PERSISTENT ? resident_slots(decode_split<T, D, GT>, DT, dyn) : 8192;
+  const int gx = PERSISTENT ? resident_slots(decode_split<T, D, GT, VEC>, DT, dyn) : 8192;
   const dim3 grid((unsigned)std::min(a.items_max, gx), a.n_sub);
   {
-    TimedLaunch t("decode_split", st);
-    decode_split<T, D, GT><<<grid, DT, dyn, st>>>(a);
+    TimedLaunch t(VEC ? "vector_decode_split" : "decode_split", st);
+    decode_split<T, D, GT, VEC><<<grid, DT, dyn, st>>>(a);
   }
   {
-    TimedLaunch t("decode_merge", st);
-    decode_merge<D, GT><<<dim3(a.B * a.Hkv, a.n_sub), GT * D, 0, st>>>(a);
+    TimedLaunch t(VEC ? "vector_decode_merge" : "decode_merge", st);
+    decode_merge<D, GT, VEC><<<dim3(a.B * a.Hkv, a.n_sub), GT * D, 0, st>>>(a);
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool VEC>
 void launch_decode_g(const DecodeArgs& a, int GT, hipStream_t st) {
   switch (GT) {
-    case 1: launch_decode<T, D, 1>(a, st); break;
-    case 2: launch_decode<T, D, 2>(a, st); break;
-    case 4: launch_decode<T, D, 4>(a, st); break;
-    default: launch_decode<T, D, 8>(a, st); break;
+    case 1: launch_decode<T, D, 1, VEC>(a, st); break;
+    case 2: launch_decode<T, D, 2, VEC>(a, st); break;
+    case 4: launch_decode<T, D, 4, VEC>(a, st); break;
+    default: launch_decode<T, D, 8, VEC>(a, st); break;
+  }
+}
+
+template <bool VEC>
+void launch_decode_any(const DecodeArgs& a, int dtype, int d, int GT, hipStream_t st) {
+  if (dtype == KV_BF16) {
+    if (d == 128) launch_decode_g<__bf16, 128, VEC>(a, GT, st);
+    else launch_decode_g<__bf16, 64, VEC>(a, GT, st);
+  } else {
+    if (d == 128) launch_decode_g<float, 128, VEC>(a, GT, st);
+    else launch_decode_g<float, 64, VEC>(a, GT, st);
   }
 }
 
@@ -368,14 +468,51 @@ extern "C" int kv_decode_attn(const void* q, const void* k_c, const void* v_c,
   a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + p.off_ml);
   a.item_start = reinterpret_cast<int*>(static_cast<char*>(workspace) + p.off_ist);
   a.out = out; a.lse = lse;
+  a.vmap = nullptr; a.pos = nullptr; a.w = nullptr; a.rope_base = 0.f; a.vcap = 0;
+  a.part_u = nullptr;
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dtype == KV_BF16) {
-    if (d == 128) launch_decode_g<__bf16, 128>(a, p.GT, st);
-    else launch_decode_g<__bf16, 64>(a, p.GT, st);
-  } else {
-    if (d == 128) launch_decode_g<float, 128>(a, p.GT, st);
-    else launch_decode_g<float, 64>(a, p.GT, st);
-  }
+  launch_decode_any<false>(a, dtype, d, p.GT, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+extern "C" size_t kv_vector_decode_workspace_size(int B, int Hq, int Hkv, int d,
+                                                  int64_t capacity_rows) {
+  DecodePlan p;
+  return plan_decode(B, Hq, Hkv, d, capacity_rows, &p, true) ? p.bytes : 0;
+}
+
+extern "C" int kv_vector_decode(const void* q, const void* k_c, const void* v_c,
+                                const int32_t* vmap, const int32_t* pos, const int64_t* offsets,
+                                const float* w, float rope_base, int B, int Hq, int Hkv, int d,
+                                int dtype, float scale, int64_t capacity_rows,
+                                int64_t v_capacity_rows, float* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !offsets || !out || !w) return KV_ERR_NULL;
+  if (capacity_rows > 0 && (!k_c || !vmap || !pos)) return KV_ERR_NULL;
+  if (v_capacity_rows > 0 && !v_c) return KV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_c) || !aligned16(v_c) || !aligned16(vmap) ||
+      !aligned16(pos) || !aligned16(offsets) || !aligned16(w) || !aligned16(out) ||
+      !aligned16(lse) || !aligned16(workspace))
+    return KV_ERR_ALIGN;
+  if (dtype != KV_F32 && dtype != KV_BF16) return KV_ERR_DTYPE;
+  if (!(rope_base >= 0.f) || v_capacity_rows < 0 || v_capacity_rows >= (int64_t(1) << 31))
+    return KV_ERR_SHAPE;
+  DecodePlan p;
+  if (!plan_decode(B, Hq, Hkv, d, capacity_rows, &p, true)) return KV_ERR_SHAPE;
+  if (!workspace || workspace_bytes < p.bytes) return KV_ERR_WORKSPACE;
+
+  DecodeArgs a;
+  a.q = q; a.kc = static_cast<const char*>(k_c); a.vc = static_cast<const char*>(v_c);
+  a.offsets = offsets; a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+  a.n_sub = p.n_sub; a.items_max = p.items_max; a.cap = capacity_rows;
+  a.c = (float)((scale > 0.f ? (double)scale : 1.0 / sqrt((double)d)) * LOG2E_D);
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + p.off_ml);
+  a.item_start = reinterpret_cast<int*>(static_cast<char*>(workspace) + p.off_ist);
+  a.part_u = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_u);
+  a.out = out; a.lse = lse;
+  a.vmap = vmap; a.pos = pos; a.w = w; a.rope_base = rope_base; a.vcap = v_capacity_rows;
+
+  launch_decode_any<true>(a, dtype, d, p.GT, static_cast<hipStream_t>(stream));
   return launch_status();
 }

@@ -34,6 +34,7 @@
 #include <math.h>
 
 #include "common.hpp"
+#include "internal.hpp"
 
 namespace kvcc {
 namespace {
@@ -47,7 +48,9 @@ constexpr int DIGIT = 11;
 struct SelectArgs {
   const float* scores;
   const int32_t* ctx;
+  const int32_t* n_head;   // per-head lengths (overrides ctx), or null
   int B, Hkv, N_max;
+  int k_zero_ok;           // BUDGET_K with k <= 0 keeps nothing (else k >= 1)
   kv_budget bud;
   int32_t* kept_idx;
   int32_t* kept_count;
@@ -206,8 +209,11 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   __shared__ Smem sm;
   const int head = blockIdx.x, b = head / a.Hkv;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
-  const int n = a.ctx ? min(max(a.ctx[b], 0), a.N_max) : a.N_max;
-  if (n == 0) {
+  const int n = a.n_head ? min(max(a.n_head[head], 0), a.N_max)
+                        : (a.ctx ? min(max(a.ctx[b], 0), a.N_max) : a.N_max);
+  const bool none = a.k_zero_ok && a.bud.mode == KV_BUDGET_K &&
+                    (a.bud.k ? a.bud.k[head] : a.bud.k_scalar) <= 0;
+  if (n == 0 || none) {
     if (tid == 0) a.kept_count[head] = 0;
     return;
   }
@@ -473,14 +479,22 @@ extern "C" int kv_select(const float* scores, const int32_t* ctx_len,
   if (bu.mode == KV_BUDGET_THRESHOLD && isnan(bu.tau)) return KV_ERR_MODE;
   if (bu.n_sink < 0 || bu.n_recent < 0) return KV_ERR_MODE;
 
+  select_launch(scores, ctx_len, nullptr, B, Hkv, N_max, bu, false, kept_idx, kept_count,
+                static_cast<hipStream_t>(stream), "select");
+  return launch_status();
+}
+
+void kvcc::select_launch(const float* scores, const int32_t* ctx, const int32_t* n_head, int B,
+                         int Hkv, int N_max, const kv_budget& bud, bool k_zero_ok,
+                         int32_t* kept_idx, int32_t* kept_count, hipStream_t st,
+                         const char* timer_name) {
   SelectArgs a;
-  a.scores = scores; a.ctx = ctx_len; a.B = B; a.Hkv = Hkv; a.N_max = N_max;
-  a.bud = bu; a.kept_idx = kept_idx; a.kept_count = kept_count;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  TimedLaunch t("select", st);
+  a.scores = scores; a.ctx = ctx; a.n_head = n_head; a.B = B; a.Hkv = Hkv; a.N_max = N_max;
+  a.k_zero_ok = k_zero_ok ? 1 : 0;
+  a.bud = bud; a.kept_idx = kept_idx; a.kept_count = kept_count;
+  TimedLaunch t(timer_name, st);
   if (N_max <= LDS_KEYS)
     select_kernel<true><<<B * Hkv, NT, 0, st>>>(a);
   else
     select_kernel<false><<<B * Hkv, NT, 0, st>>>(a);
-  return launch_status();
 }

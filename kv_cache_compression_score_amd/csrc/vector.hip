@@ -1,0 +1,439 @@
+// VECTOR three-way routing: retain, approximate or evict per token.
+//
+// "A Simple Plug-in for Improving Eviction-Based KV Cache Compression"
+// (VECTOR), section "Methodologie: VECTOR": the base eviction score selects
+// an enlarged pool of 1 - p_c + p_a of the tokens; each pool token's
+// reconstruction residual eps = ||V - W RoPE^-1(K)||^2 is computed with an
+// offline linear map W (keys rotated back to position 0 first); keys stay
+// for the whole pool, the 2 p_a lowest-residual tokens drop their values
+// (rebuilt from their keys when read) and the rest keep K and V exactly.
+//
+// kv_vector_route: pool (radix select on the scores), residuals (fp32 MFMA:
+// the 64 pool rows of a workgroup, de-rotated, times W^T, with W, the rows
+// and the values staged in LDS), then a second radix select on -eps inside
+// the pool.  kv_vector_compact: the packed cache keeps a key row per pool
+// token and a value row per exact token, with vmap telling, per key row,
+// where its value is (-1: rebuilt).  The decode side lives with the other
+// decode kernels.
+//
+// Rotary positions: adjacent pairs (2i, 2i+1) turn by pos * base^(-2i/d)
+// (base 0: no rotation).  The angle is reduced to revolutions in float64
+// (exact for any position) before the hardware sine/cosine.
+#include <math.h>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace kvcc {
+namespace {
+
+constexpr int VT = 256;
+constexpr int RPW = 64;          // pool entries per residual workgroup
+constexpr int MAX_HEADS = 4096;
+constexpr double INV_TWO_PI = 0.15915494309189535;
+
+__global__ void vector_counts_kernel(const int32_t* ctx, int B, int Hkv, int N_max, float p_c,
+                                     float p_a, int32_t* k_pool, int32_t* k_apx) {
+  const int head = blockIdx.x * blockDim.x + threadIdx.x;
+  if (head >= B * Hkv) return;
+  const int n = ctx ? min(max(ctx[head / Hkv], 0), N_max) : N_max;
+  const double pc = (double)p_c, pa = (double)p_a;
+  long long kp = (long long)floor((1.0 - pc + pa) * (double)n + 0.5);
+  kp = min(max(kp, 1ll), (long long)n);
+  long long ka = (long long)floor(2.0 * pa * (double)n + 0.5);
+  ka = min(max(ka, 0ll), kp);
+  k_pool[head] = (int)kp;
+  k_apx[head] = (int)ka;
+}
+
+// Revolutions of pair i of a d-wide row at position pos, for base > 0.
+__device__ __forceinline__ float rope_rev(int pos, int i, int d, double log2_base) {
+  const double g = exp2(-(2.0 * i / d) * log2_base) * INV_TWO_PI;
+  double r = (double)pos * g;
+  r -= floor(r);
+  return (float)r;
+}
+
+template <typename T, int N>
+__device__ __forceinline__ void load_elems(const char* row, int e0, float* x) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int c = 0; c < N; c += 8) {
+      const uint4 w = ld16(row + (size_t)(e0 + c) * 2);
+      x[c + 0] = bf16_lo(w.x); x[c + 1] = bf16_hi(w.x);
+      x[c + 2] = bf16_lo(w.y); x[c + 3] = bf16_hi(w.y);
+      x[c + 4] = bf16_lo(w.z); x[c + 5] = bf16_hi(w.z);
+      x[c + 6] = bf16_lo(w.w); x[c + 7] = bf16_hi(w.w);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < N; c += 4) {
+      const uint4 w = ld16(row + (size_t)(e0 + c) * 4);
+      x[c + 0] = __uint_as_float(w.x); x[c + 1] = __uint_as_float(w.y);
+      x[c + 2] = __uint_as_float(w.z); x[c + 3] = __uint_as_float(w.w);
+    }
+  }
+}
+
+struct ResidualArgs {
+  const char* k;
+  const char* v;
+  const float* w;          // [Hkv][d][d], out = w @ in
+  const int32_t* pool_idx;
+  const int32_t* pool_count;
+  float* neg_eps;          // [B][Hkv][N_max]
+  int B, Hkv, N_max;
+  float rope_base;
+};
+
+// Workgroup = 64 pool entries of one head, 4 waves.  Wave w owns row block
+// w/2 and the column blocks of half w%2; each 32x32 output block is
+// K~ W^T over d/2 steps of v_mfma_f32_32x32x2f32, and the squared residual
+// is summed over the columns in-lane, across the 32 lanes of a half-wave
+// (DPP), then over the two halves through LDS.
+template <typename T, int D>
+__global__ __launch_bounds__(VT) void vector_residual_kernel(ResidualArgs a) {
+  constexpr int LD = D + 1;                  // padded LDS rows
+  constexpr int NCB = D / 32, CPW = NCB / 2; // column blocks, per wave
+  constexpr int EQ = D / 4;                  // staged elements per thread
+  constexpr int ROWB = D * (int)sizeof(T);
+  __shared__ float Wl[D][LD];
+  __shared__ float Kt[RPW][LD];
+  __shared__ float Vt[RPW][LD];
+  __shared__ float part[2][RPW];
+
+  const int h = blockIdx.y, b = blockIdx.z, head = b * a.Hkv + h;
+  const int j0 = blockIdx.x * RPW;
+  const int tid = threadIdx.x;
+  const int cnt = min(max(a.pool_count[head], 0), a.N_max);
+  float* ne = a.neg_eps + (size_t)head * a.N_max;
+  const int jend = min(j0 + RPW, a.N_max);
+  if (j0 >= cnt) {
+    for (int j = j0 + tid; j < jend; j += VT) ne[j] = -INFINITY;
+    return;
+  }
+
+  const float4* w4 = reinterpret_cast<const float4*>(a.w + (size_t)h * D * D);
+  for (int i = tid; i < D * D / 4; i += VT) {
+    const float4 x = w4[i];
+    const int o = (4 * i) / D, c = (4 * i) % D;
+    Wl[o][c] = x.x; Wl[o][c + 1] = x.y; Wl[o][c + 2] = x.z; Wl[o][c + 3] = x.w;
+  }
+  {
+    const int r = tid / 4, q4 = tid % 4, j = j0 + r;
+    float kx[EQ], vx[EQ];
+    if (j < cnt) {
+      const int t = a.pool_idx[(size_t)head * a.N_max + j];
+      const size_t roff = ((size_t)head * a.N_max + t) * ROWB;
+      load_elems<T, EQ>(a.k + roff, q4 * EQ, kx);
+      load_elems<T, EQ>(a.v + roff, q4 * EQ, vx);
+      if (a.rope_base > 0.f) {
+        const double l2b = log2((double)a.rope_base);
+#pragma unroll
+        for (int m = 0; m < EQ / 2; ++m) {
+          const float rv = rope_rev(t, q4 * EQ / 2 + m, D, l2b);
+          const float s = __builtin_amdgcn_sinf(rv), c = __builtin_amdgcn_cosf(rv);
+          const float x = kx[2 * m], y = kx[2 * m + 1];
+          kx[2 * m] = x * c + y * s;
+          kx[2 * m + 1] = y * c - x * s;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EQ; ++e) { kx[e] = 0.f; vx[e] = 0.f; }
+    }
+#pragma unroll
+    for (int e = 0; e < EQ; ++e) { Kt[r][q4 * EQ + e] = kx[e]; Vt[r][q4 * EQ + e] = vx[e]; }
+  }
+  __syncthreads();
+
+  const int lane = tid & (WAVE - 1), wave = tid / WAVE, l32 = lane & 31, hf = lane >> 5;
+  const int rb = wave >> 1;
+  float rs[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) rs[e] = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    const int cb = (wave & 1) * CPW + c;
+    f32x16 acc = {};
+#pragma unroll 8
+    for (int ks = 0; ks < D / 2; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Kt[rb * 32 + l32][2 * ks + hf],
+                                                 Wl[cb * 32 + l32][2 * ks + hf], acc, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = rb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+      const float r = Vt[row][cb * 32 + l32] - acc[e];
+      rs[e] = fmaf(r, r, rs[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) rs[e] = group_sum<32>(rs[e]);
+  if (l32 == 0) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) part[wave & 1][rb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3)] = rs[e];
+  }
+  __syncthreads();
+  if (tid < RPW) {
+    const int j = j0 + tid;
+    if (j < jend) ne[j] = j < cnt ? -(part[0][tid] + part[1][tid]) : -INFINITY;
+  }
+}
+
+// ---- compaction -------------------------------------------------------------
+
+struct VCompactArgs {
+  const char* k;
+  const char* v;
+  int B, Hkv, N_max, rowb;
+  const int32_t* pool_idx;
+  const int32_t* pool_count;
+  const int32_t* apx_pos;
+  const int32_t* apx_count;
+  char* kc;
+  char* vc;
+  int32_t* pos;
+  int32_t* vmap;
+  int64_t* offsets;
+  int64_t* voffsets;
+  int64_t cap, vcap;
+};
+
+__device__ __forceinline__ int clamp_cnt(const int32_t* c, int i, int hi) {
+  return min(max(c[i], 0), hi);
+}
+
+// Exclusive scans of the key-row counts (pool) and value-row counts (pool -
+// approximated) over the heads, into LDS.
+__device__ void scan_two(const VCompactArgs& a, int H, long long* off, long long* voff,
+                         long long* wtot) {
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  constexpr int NWV = VT / WAVE;
+  long long carry = 0, vcarry = 0;
+  for (int base = 0; base < H; base += VT) {
+    const int i = base + tid;
+    long long c = 0, vc = 0;
+    if (i < H) {
+      c = clamp_cnt(a.pool_count, i, a.N_max);
+      vc = c - clamp_cnt(a.apx_count, i, (int)c);
+    }
+    const long long inc = wave_incl_scan<long long>(c);
+    const long long vinc = wave_incl_scan<long long>(vc);
+    if (lane == WAVE - 1) { wtot[wave] = inc; wtot[NWV + wave] = vinc; }
+    __syncthreads();
+    long long before = 0, chunk = 0, vbefore = 0, vchunk = 0;
+    for (int w = 0; w < NWV; ++w) {
+      if (w < wave) { before += wtot[w]; vbefore += wtot[NWV + w]; }
+      chunk += wtot[w];
+      vchunk += wtot[NWV + w];
+    }
+    if (i < H) { off[i] = carry + before + inc - c; voff[i] = vcarry + vbefore + vinc - vc; }
+    carry += chunk;
+    vcarry += vchunk;
+    __syncthreads();
+  }
+  if (tid == 0) { off[H] = carry; voff[H] = vcarry; }
+  __syncthreads();
+}
+
+// One workgroup per head: walks the head's pool entries 256 at a time,
+// flags the approximated ones (their sorted positions are a contiguous run
+// of apx_pos) and gives every exact entry its packed value row.
+__global__ __launch_bounds__(VT) void vector_vmap_kernel(VCompactArgs a) {
+  extern __shared__ long long dyn[];   // off[H+1], voff[H+1]
+  __shared__ long long wtot[2 * (VT / WAVE)];
+  __shared__ unsigned char flag[VT];
+  __shared__ int wcnt[2][VT / WAVE];
+  const int H = a.B * a.Hkv;
+  long long* off = dyn;
+  long long* voff = dyn + H + 1;
+  scan_two(a, H, off, voff, wtot);
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  if (blockIdx.x == 0)
+    for (int i = tid; i <= H; i += VT) { a.offsets[i] = off[i]; a.voffsets[i] = voff[i]; }
+  const int head = blockIdx.x;
+  const int cnt = clamp_cnt(a.pool_count, head, a.N_max);
+  const int acnt = clamp_cnt(a.apx_count, head, cnt);
+  const int32_t* ap = a.apx_pos + (size_t)head * a.N_max;
+  const long long base = off[head], vbase = voff[head];
+  int aptr = 0, vrank = 0;
+  for (int J = 0; J < cnt; J += VT) {
+    flag[tid] = 0;
+    __syncthreads();
+    const int x = aptr + tid < acnt ? ap[aptr + tid] : 0x7fffffff;
+    const bool in = x < J + VT;       // sorted and distinct: x >= J
+    if (in && x >= J) flag[x - J] = 1;
+    const uint64_t bin = __ballot(in);
+    if (lane == 0) wcnt[0][wave] = (int)__popcll(bin);
+    __syncthreads();
+    const int j = J + tid;
+    const bool ex = j < cnt && !flag[tid];
+    const uint64_t bex = __ballot(ex);
+    if (lane == 0) wcnt[1][wave] = (int)__popcll(bex);
+    __syncthreads();
+    int before = 0, m = 0, tot = 0;
+    for (int w = 0; w < VT / WAVE; ++w) {
+      if (w < wave) before += wcnt[1][w];
+      m += wcnt[0][w];
+      tot += wcnt[1][w];
+    }
+    if (j < cnt) {
+      const long long row = base + j;
+      if (row < a.cap)
+        a.vmap[row] = ex ? (int32_t)(vbase + vrank + before + (int)mbcnt(bex)) : -1;
+    }
+    vrank += tot;
+    aptr += m;
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ int find_head(const long long* off, int H, long long row) {
+  int lo = 0, hi = H - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Grid-stride over the packed key rows: key row and position always, value
+// row when vmap says the token keeps it (and it fits the value capacity).
+__global__ __launch_bounds__(VT) void vector_copy_kernel(VCompactArgs a) {
+  extern __shared__ long long dyn[];
+  __shared__ long long wtot[2 * (VT / WAVE)];
+  const int H = a.B * a.Hkv;
+  long long* off = dyn;
+  long long* voff = dyn + H + 1;
+  scan_two(a, H, off, voff, wtot);
+  const long long total = min(off[H], (long long)a.cap);
+  const int tid = threadIdx.x;
+  const int lpr = a.rowb / 16, sub = tid % lpr, rloc = tid / lpr, rpi = VT / lpr;
+  for (long long row = (long long)blockIdx.x * rpi + rloc; row < total;
+       row += (long long)gridDim.x * rpi) {
+    const int head = find_head(off, H, row);
+    const long long j = row - off[head];
+    const int t = a.pool_idx[(size_t)head * a.N_max + j];
+    if ((unsigned)t >= (unsigned)a.N_max) continue;
+    const size_t src = ((size_t)head * a.N_max + t) * a.rowb + sub * 16;
+    st16(a.kc + (size_t)row * a.rowb + sub * 16, ld16(a.k + src));
+    const int vm = a.vmap[row];
+    if (vm >= 0 && vm < a.vcap) st16(a.vc + (size_t)vm * a.rowb + sub * 16, ld16(a.v + src));
+    if (sub == 0) a.pos[row] = t;
+  }
+}
+
+}  // namespace
+}  // namespace kvcc
+
+using namespace kvcc;
+
+extern "C" size_t kv_vector_route_workspace_size(int B, int Hkv) {
+  if (B < 1 || Hkv < 1) return 0;
+  return (size_t)2 * B * Hkv * sizeof(int32_t) + 256;
+}
+
+extern "C" int kv_vector_route(const float* scores, const int32_t* ctx_len, const void* k,
+                               const void* v, const float* w, int B, int Hkv, int N_max, int d,
+                               int dtype, float p_c, float p_a, float rope_base,
+                               int32_t* pool_idx, int32_t* pool_count, float* neg_eps,
+                               int32_t* apx_pos, int32_t* apx_count, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (!scores || !k || !v || !w || !pool_idx || !pool_count || !neg_eps || !apx_pos ||
+      !apx_count)
+    return KV_ERR_NULL;
+  if (!aligned16(scores) || !aligned16(ctx_len) || !aligned16(k) || !aligned16(v) ||
+      !aligned16(w) || !aligned16(pool_idx) || !aligned16(pool_count) || !aligned16(neg_eps) ||
+      !aligned16(apx_pos) || !aligned16(apx_count) || !aligned16(workspace))
+    return KV_ERR_ALIGN;
+  if (dtype != KV_F32 && dtype != KV_BF16) return KV_ERR_DTYPE;
+  if (B < 1 || Hkv < 1 || N_max < 1 || (d != 64 && d != 128) ||
+      (int64_t)B * Hkv * N_max >= (int64_t(1) << 31))
+    return KV_ERR_SHAPE;
+  if (!(p_c >= 0.f && p_c <= 1.f && p_a >= 0.f && p_a <= 1.f && rope_base >= 0.f))
+    return KV_ERR_MODE;
+  if (!workspace || workspace_bytes < kv_vector_route_workspace_size(B, Hkv))
+    return KV_ERR_WORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* k_pool = static_cast<int32_t*>(workspace);
+  int32_t* k_apx = k_pool + (size_t)B * Hkv;
+  const int H = B * Hkv;
+  {
+    TimedLaunch t("vector_counts", st);
+    vector_counts_kernel<<<ceil_div(H, 256), 256, 0, st>>>(ctx_len, B, Hkv, N_max, p_c, p_a,
+                                                           k_pool, k_apx);
+  }
+  kv_budget pool{};
+  pool.mode = KV_BUDGET_K;
+  pool.k = k_pool;
+  pool.max_ratio = 1.f;
+  select_launch(scores, ctx_len, nullptr, B, Hkv, N_max, pool, false, pool_idx, pool_count, st,
+                "vector_pool");
+  ResidualArgs r;
+  r.k = static_cast<const char*>(k); r.v = static_cast<const char*>(v); r.w = w;
+  r.pool_idx = pool_idx; r.pool_count = pool_count; r.neg_eps = neg_eps;
+  r.B = B; r.Hkv = Hkv; r.N_max = N_max; r.rope_base = rope_base;
+  {
+    TimedLaunch t("vector_residual", st);
+    const dim3 grid((unsigned)ceil_div(N_max, RPW), Hkv, B);
+    if (dtype == KV_BF16) {
+      if (d == 128) vector_residual_kernel<__bf16, 128><<<grid, VT, 0, st>>>(r);
+      else vector_residual_kernel<__bf16, 64><<<grid, VT, 0, st>>>(r);
+    } else {
+      if (d == 128) vector_residual_kernel<float, 128><<<grid, VT, 0, st>>>(r);
+      else vector_residual_kernel<float, 64><<<grid, VT, 0, st>>>(r);
+    }
+  }
+  kv_budget apx{};
+  apx.mode = KV_BUDGET_K;
+  apx.k = k_apx;
+  apx.max_ratio = 1.f;
+  select_launch(neg_eps, nullptr, pool_count, B, Hkv, N_max, apx, true, apx_pos, apx_count, st,
+                "vector_apx");
+  return launch_status();
+}
+
+extern "C" int kv_vector_compact(const void* k, const void* v, int B, int Hkv, int N_max, int d,
+                                 int dtype, const int32_t* pool_idx, const int32_t* pool_count,
+                                 const int32_t* apx_pos, const int32_t* apx_count, void* k_c,
+                                 void* v_c, int32_t* pos, int32_t* vmap, int64_t* offsets,
+                                 int64_t* voffsets, int64_t capacity_rows,
+                                 int64_t v_capacity_rows, void* stream) {
+  if (!k || !v || !pool_idx || !pool_count || !apx_pos || !apx_count || !offsets || !voffsets)
+    return KV_ERR_NULL;
+  if (capacity_rows > 0 && (!k_c || !pos || !vmap)) return KV_ERR_NULL;
+  if (v_capacity_rows > 0 && !v_c) return KV_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(pool_idx) || !aligned16(pool_count) ||
+      !aligned16(apx_pos) || !aligned16(apx_count) || !aligned16(k_c) || !aligned16(v_c) ||
+      !aligned16(pos) || !aligned16(vmap) || !aligned16(offsets) || !aligned16(voffsets))
+    return KV_ERR_ALIGN;
+  if (dtype != KV_F32 && dtype != KV_BF16) return KV_ERR_DTYPE;
+  if (B < 1 || Hkv < 1 || N_max < 1 || (d != 64 && d != 128) || capacity_rows < 0 ||
+      v_capacity_rows < 0 || (int64_t)B * Hkv > MAX_HEADS ||
+      (int64_t)B * Hkv * N_max >= (int64_t(1) << 31) || v_capacity_rows >= (int64_t(1) << 31))
+    return KV_ERR_SHAPE;
+
+  VCompactArgs a;
+  a.k = static_cast<const char*>(k); a.v = static_cast<const char*>(v);
+  a.B = B; a.Hkv = Hkv; a.N_max = N_max; a.rowb = d * (dtype == KV_BF16 ? 2 : 4);
+  a.pool_idx = pool_idx; a.pool_count = pool_count; a.apx_pos = apx_pos; a.apx_count = apx_count;
+  a.kc = static_cast<char*>(k_c); a.vc = static_cast<char*>(v_c);
+  a.pos = pos; a.vmap = vmap; a.offsets = offsets; a.voffsets = voffsets;
+  a.cap = capacity_rows; a.vcap = v_capacity_rows;
+  const int H = B * Hkv;
+  const size_t dyn = (size_t)2 * (H + 1) * sizeof(long long);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  {
+    TimedLaunch t("vector_vmap", st);
+    vector_vmap_kernel<<<H, VT, dyn, st>>>(a);
+  }
+  {
+    TimedLaunch t("vector_copy", st);
+    const int rpi = VT / (a.rowb / 16);
+    int64_t grid = ceil_div64(std::min<int64_t>(capacity_rows, (int64_t)H * N_max), rpi * 4);
+    grid = std::max<int64_t>(1, std::min<int64_t>(grid, 2048));
+    vector_copy_kernel<<<(unsigned)grid, VT, dyn, st>>>(a);
+  }
+  return launch_status();
+}

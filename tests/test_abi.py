@@ -85,6 +85,35 @@ def test_score_from_lse_validation():
     assert call(d=32) == KV_ERR_SHAPE
 
 
+def test_vector_validation():
+    L = _lib.lib()
+    assert L.kv_vector_route_workspace_size(2, 3) >= 2 * 2 * 3 * 4
+    assert L.kv_vector_decode_workspace_size(1, 8, 2, 128, 1000) > \
+        L.kv_decode_workspace_size(1, 8, 2, 128, 1000)
+
+    def route(**kw):
+        a = dict(s=P, k=P, v=P, w=P, d=64, dtype=1, p_c=0.9, p_a=0.05, base=0.0, ws=P, wsb=4096)
+        a.update(kw)
+        return L.kv_vector_route(a["s"], None, a["k"], a["v"], a["w"], 1, 2, 64, a["d"], a["dtype"],
+                                 a["p_c"], a["p_a"], a["base"], P, P, P, P, P, a["ws"], a["wsb"],
+                                 None)
+    assert route(w=None) == KV_ERR_NULL
+    assert route(k=P + 2) == KV_ERR_ALIGN
+    assert route(dtype=5) == KV_ERR_DTYPE
+    assert route(d=96) == KV_ERR_SHAPE
+    assert route(p_a=1.5) == KV_ERR_MODE
+    assert route(base=-1.0) == KV_ERR_MODE
+    assert route(wsb=4) == KV_ERR_WORKSPACE
+    assert L.kv_vector_compact(P, P, 1, 2, 64, 64, 1, None, P, P, P, P, P, P, P, P, P, 10, 10,
+                               None) == KV_ERR_NULL
+    assert L.kv_vector_compact(P, P, 1, 2, 64, 48, 1, P, P, P, P, P, P, P, P, P, P, 10, 10,
+                               None) == KV_ERR_SHAPE
+    assert L.kv_vector_decode(P, P, P, P, P, P, None, 0.0, 1, 4, 2, 64, 1, 0.0, 10, 10, P, P, P,
+                              1 << 20, None) == KV_ERR_NULL
+    assert L.kv_vector_decode(P, P, P, P, P, P, P, 0.0, 1, 4, 2, 64, 1, 0.0, 10, 10, P, P, P,
+                              16, None) == KV_ERR_WORKSPACE
+
+
 def _select(budget, **kw):
     a = dict(scores=P, ctx=None, B=1, Hkv=2, N=64, idx=P, cnt=P)
     a.update(kw)

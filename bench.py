@@ -20,6 +20,8 @@ in HBM before timing starts.  Prints one JSON line:
   fidelity    output / log-sum-exp loss terms of the compacted cache
               against the full cache for the step's decode queries (and,
               fidelity_window_query, for the last window row of each head)
+  vector_routing  VECTOR three-way routing (route, routed compaction,
+              decode rebuilding dropped values) at the same memory budget
   score_one_pass  kv_score_from_lse (row LSEs given, as a prefill pass
               yields them): one sweep over K instead of two
   cpu_baseline the float64 oracle on a bounded sample on the host cores
@@ -152,6 +154,53 @@ def one_pass_score_ms(pipe: Pipeline, steps: int) -> float:
     if n != 1:
         raise RuntimeError(f"kv_timing_read returned {n}")
     return buf[0].total_ms / buf[0].launches
+
+
+def vector_measure(pipe: Pipeline, steps: int) -> dict:
+    """VECTOR routing at the same memory as the headline's 10% keep (p_c =
+    0.9, p_a = 0.05: keys for 15% of the tokens, values for 5%), with a
+    seeded random linear map W and rotary base 500000, timed per kernel over
+    `steps` route + compact + decode passes."""
+    L = _lib.lib()
+    cfg = pipe.cfg
+    B, Hkv, N, D = pipe.k.shape
+    g = torch.Generator().manual_seed(7)
+    w = (torch.randn(Hkv, D, D, generator=g) / math.sqrt(D)).to("cuda:0")
+    p_c, p_a, base = 0.9, 0.05, 500000.0
+
+    def one():
+        r = api.kv_vector_route(pipe.scores, pipe.c, pipe.k, pipe.v, w, p_c=p_c, p_a=p_a,
+                                rope_base=base)
+        pool_idx, pool_count, _, apx_pos, apx_count = r
+        cap = B * Hkv * N // 4
+        comp = api.kv_vector_compact(pipe.k, pipe.v, pool_idx, pool_count, apx_pos, apx_count,
+                                     cap, cap)
+        k_c, v_c, pos, vmap, off, voff = comp
+        api.kv_vector_decode(pipe.qd, k_c, v_c, vmap, pos, off, w, Hkv, v_capacity_rows=cap,
+                             rope_base=base)
+        return pool_count, apx_count
+
+    pool_count, apx_count = one()
+    torch.cuda.synchronize()
+    L.kv_timing_enable(1)
+    for _ in range(steps):
+        one()
+    torch.cuda.synchronize()
+    buf = (_lib.KvKernelTime * 32)()
+    n = L.kv_timing_read(buf, 32)
+    L.kv_timing_enable(0)
+    kt = {buf[i].name.decode(): buf[i].total_ms / buf[i].launches for i in range(n)}
+    rows = int(pool_count.sum().item())
+    vrows = rows - int(apx_count.sum().item())
+    esz = pipe.k.element_size()
+    t_route = sum(kt[k] for k in ("vector_counts", "vector_pool", "vector_residual", "vector_apx"))
+    t_comp = kt["vector_vmap"] + kt["vector_copy"]
+    t_dec = kt["vector_decode_split"] + kt["vector_decode_merge"]
+    dec_bytes = rows * D * esz + vrows * D * esz + rows * 8 + B * cfg.Hq * D * (esz + 4)
+    return {"p_c": p_c, "p_a": p_a, "key_rows": rows, "value_rows": vrows,
+            "kernels_ms": kt, "route_ms": t_route, "compact_ms": t_comp, "decode_ms": t_dec,
+            "residual_tflops": 2.0 * D * D * rows / (kt["vector_residual"] * 1e-3) / 1e12,
+            "decode_gbps": dec_bytes / (t_dec * 1e-3) / 1e9}
 
 
 COPY_BYTES = 1 << 30
@@ -288,6 +337,7 @@ def main():
     else:
         achieved, peak, unit = amount / t_dom / 1e9, PEAK_HBM_GBPS, "GB/s"
     t_one = one_pass_score_ms(pipe, args.steps) * 1e-3
+    vec = vector_measure(pipe, args.steps)
     t = {k: v[0] * 1e-3 for k, v in kt.items()}
     t_score = t["score_rowstats"] + t["score_fold"] + t["score_colsum"]
     t_dec = t["decode_split"] + t["decode_merge"]
@@ -320,6 +370,7 @@ def main():
         "score_one_pass": {"ms": t_one * 1e3,
                            "algorithmic_tflops": flop_pass / t_one / 1e12,
                            "algorithmic_frac": flop_pass / t_one / 1e12 / peak_f},
+        "vector_routing": vec,
         "select_compact_decode": {"ms": t_scd * 1e3,
                                   "gbps": (bytes_sel + bytes_comp + bytes_dec) / t_scd / 1e9,
                                   "frac": (bytes_sel + bytes_comp + bytes_dec) / t_scd / 1e9

@@ -73,7 +73,7 @@ struct Smem {
   unsigned long long w_fx[NWV];
   unsigned long long f_m[NWV];   // bin search: per-wave totals
   uint32_t f_c[NWV];
-  uint32_t bin, cnt_above;
+  uint32_t bin, cnt_above, bin_cnt;
   unsigned long long mass_above;
 };
 
@@ -132,23 +132,30 @@ __device__ __forceinline__ void for_keys(const Keys<IN_LDS>& key, int n, const F
 template <bool MASS, bool IN_LDS, class FX>
 __device__ uint32_t descend(const Keys<IN_LDS>& key, int n, int cp, uint32_t lo_key,
                             unsigned long long rem, Smem& sm, const FX& fx,
-                            uint32_t* cnt_above_out, unsigned long long* rem_out) {
+                            uint32_t* cnt_above_out, unsigned long long* rem_out,
+                            bool top_ready = false, uint32_t* eq_out = nullptr) {
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  if (top_ready) cp = 0;   // sm.hist already holds the top DIGIT bits of every key
   uint32_t pmask = cp <= 0 ? 0u : (cp >= 32 ? ~0u : ~0u << (32 - cp));
   uint32_t prefix = lo_key & pmask, cnt_above = 0;
   int left = cp >= 32 ? 0 : 32 - cp;
+  bool ready = top_ready;
+  uint32_t pref_cnt = (uint32_t)n;   // keys matching the current prefix
 #pragma unroll 1
   while (left > 0) {
     const int bits = min(DIGIT, left);
     const int shift = left - bits;
     const int nb = 1 << bits;
-    for_keys(key, n, [&](uint32_t kk) {
-      if ((kk & pmask) == prefix) {
-        const int bin = (kk >> shift) & (nb - 1);
-        atomicAdd(&sm.hist[bin], 1u);
-        if (MASS) atomicAdd(&sm.hmass[bin], fx(kk));
-      }
-    });
+    if (!ready) {
+      for_keys(key, n, [&](uint32_t kk) {
+        if ((kk & pmask) == prefix) {
+          const int bin = (kk >> shift) & (nb - 1);
+          atomicAdd(&sm.hist[bin], 1u);
+          if (MASS) atomicAdd(&sm.hmass[bin], fx(kk));
+        }
+      });
+    }
+    ready = false;
     __syncthreads();
     // Thread t owns descending positions 2t and 2t+1 (bins nb-1-2t, nb-2-2t):
     // it reads them, clears them for the next digit, and scans.
@@ -190,16 +197,19 @@ __device__ uint32_t descend(const Keys<IN_LDS>& key, int n, int cp, uint32_t lo_
       sm.bin = (uint32_t)(first ? nb - 1 - p0 : nb - 2 - p0);
       sm.cnt_above = wbc + incl_c - own_c + (first ? 0u : c0);
       sm.mass_above = first ? before : before + m0;
+      sm.bin_cnt = first ? c0 : c1;
     }
     __syncthreads();
     rem -= MASS ? sm.mass_above : (unsigned long long)sm.cnt_above;
     cnt_above += sm.cnt_above;
+    pref_cnt = sm.bin_cnt;
     prefix |= sm.bin << shift;
     pmask |= (uint32_t)(nb - 1) << shift;
     left -= bits;
   }
   *cnt_above_out = cnt_above;
   *rem_out = rem;
+  if (eq_out) *eq_out = cp >= 32 ? (uint32_t)n : pref_cnt;   // keys equal to the result
   return prefix;
 }
 
@@ -231,12 +241,15 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   // of the real scores.
   uint32_t mn = 0xffffffffu, mx = 0u, cnt = 0u;
   double tot = 0.0;
+  // Count budgets also histogram the top DIGIT key bits here (the first digit
+  // of the descent), which saves one sweep over the keys.
   auto visit = [&](uint32_t kr, bool prot) -> uint32_t {
     const uint32_t kk = prot ? PROTECTED_KEY : kr;
     mn = min(mn, kk);
     mx = max(mx, kk);
     cnt += kk >= tk ? 1u : 0u;
     if (mass) tot += (double)from_key(kr);
+    else atomicAdd(&sm.hist[kk >> (32 - DIGIT)], 1u);
     return kk;
   };
   for (int i = tid; i < NBINS; i += NT) { sm.hist[i] = 0; sm.hmass[i] = 0; }
@@ -250,6 +263,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       const int i = tid + u * NT;
       v[u] = i < n4 ? src4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    __syncthreads();   // histogram cleared before the first count (loads in flight)
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int i = tid + u * NT;
@@ -264,6 +278,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     }
     for (int t = 4 * n4 + tid; t < n; t += NT) keys_lds[t] = visit(to_key(src[t]), is_prot(t));
   } else {
+    __syncthreads();
     for (int t = tid; t < n; t += NT) visit(to_key(src[t]), is_prot(t));
   }
   mn = last_lane(wave_scan_u32(mn, 0xffffffffu, OpMin()));
@@ -341,12 +356,13 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   k = min(max(k, n_prot), n);
 
   // The k-th key and the tie quota.
-  uint32_t T, quota;
+  uint32_t T, quota, eq_total = 0;
   {
     uint32_t above;
     unsigned long long rem;
     auto nofx = [](uint32_t) { return 0ull; };
-    T = descend<false>(key, n, cp, mn, (unsigned long long)k, sm, nofx, &above, &rem);
+    T = descend<false>(key, n, cp, mn, (unsigned long long)k, sm, nofx, &above, &rem, !mass,
+                       &eq_total);
     quota = (uint32_t)rem;
   }
 
@@ -414,21 +430,85 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       const int t = s0 + j * 4 * WAVE + 4 * lane;
       ek[j] = t < s1 ? *reinterpret_cast<const uint4*>(&keys_lds[t]) : make_uint4(0u, 0u, 0u, 0u);
     }
+    // Every wave holds its segment's keys in registers, so after one barrier
+    // the key area of LDS is free: each wave compacts its kept indices into
+    // its own key range [s0, s1), then copies them out contiguously.
+    // When every key equal to T is kept (no tie to rank) the keep rule is
+    // key >= T; otherwise waves first count their equal keys for the ranks.
+    const bool all_ties = quota >= eq_total;
+    if (!all_ties) {
+      uint32_t eqw = 0;
+#pragma unroll
+      for (int j = 0; j < EPI; ++j) {
+        if (s0 + j * 4 * WAVE < s1) {
+          const int t = s0 + j * 4 * WAVE + 4 * lane;
+          const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            eqw += (uint32_t)__popcll(__ballot(t + u < s1 && kk[u] == T));
+        }
+      }
+      if (lane == 0) sm.w_eq[wave] = eqw;
+    }
+    __syncthreads();   // also: every wave holds its keys in registers now
+    if (!all_ties)
+      for (int w = 0; w < wave; ++w) eqr += sm.w_eq[w];   // ties before this wave
+    uint32_t* stage = keys_lds + s0;
+    uint32_t nk = 0;
 #pragma unroll
     for (int j = 0; j < EPI; ++j) {
-      if (s0 + j * 4 * WAVE < s1) {
+      if (all_ties && s0 + j * 4 * WAVE < s1) {
+        const int t = s0 + j * 4 * WAVE + 4 * lane;
         const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
-        count4(s0 + j * 4 * WAVE + 4 * lane, kk);
-      }
-    }
-    prefix_of_waves();
+        uint32_t at = nk;
+        bool keep[4];
+        uint64_t bk[4];
 #pragma unroll
-    for (int j = 0; j < EPI; ++j) {
-      if (s0 + j * 4 * WAVE < s1) {
+        for (int u = 0; u < 4; ++u) {
+          keep[u] = t + u < s1 && kk[u] >= T;
+          bk[u] = __ballot(keep[u]);
+          at += mbcnt(bk[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (keep[u]) stage[at++] = (uint32_t)(t + u);
+          nk += (uint32_t)__popcll(bk[u]);
+        }
+      } else if (s0 + j * 4 * WAVE < s1) {
+        const int t = s0 + j * 4 * WAVE + 4 * lane;
         const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
-        write4(s0 + j * 4 * WAVE + 4 * lane, kk);
+        bool is_gt[4], is_eq[4], keep[4];
+        uint64_t be[4], bk[4];
+        uint32_t r = eqr;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bool valid = t + u < s1;
+          is_gt[u] = valid && kk[u] > T;
+          is_eq[u] = valid && kk[u] == T;
+          be[u] = __ballot(is_eq[u]);
+          r += mbcnt(be[u]);
+        }
+        uint32_t at = nk;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          keep[u] = is_gt[u] || (is_eq[u] && r < quota);
+          r += is_eq[u] ? 1u : 0u;
+          bk[u] = __ballot(keep[u]);
+          at += mbcnt(bk[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (keep[u]) stage[at++] = (uint32_t)(t + u);
+          nk += (uint32_t)__popcll(bk[u]);
+          eqr += (uint32_t)__popcll(be[u]);
+        }
       }
     }
+    if (lane == 0) sm.w_gt[wave] = nk;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) slot += sm.w_gt[w];
+    for (uint32_t i = lane; i < nk; i += WAVE)
+      if (slot + i < (uint32_t)n) dst[slot + i] = (int32_t)stage[i];
   } else {
     auto four = [&](int t, uint32_t* kk) __attribute__((always_inline)) {
 #pragma unroll

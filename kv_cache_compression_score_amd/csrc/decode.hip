@@ -300,7 +300,7 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
 // Per (head, query sub-group): merge the head's items in item order.  Loads
 // are batched so a head's items are fetched a few at a time, not one by one.
 // Per (head, query sub-group): merge the head's items in item order, loads
-// batched 32 items at a time.  A routed cache also merges the rebuilt-row
+// batched 32 items at a time (the batch maximum first, then the weights).  A routed cache also merges the rebuilt-row
 // sums U and adds W U (one d x d product per query head) before dividing.
 template <int D, int GT, bool VEC>
 __global__ __launch_bounds__(GT * D) void decode_merge(DecodeArgs a) {
@@ -326,16 +326,23 @@ __global__ __launch_bounds__(GT * D) void decode_merge(DecodeArgs a) {
         ov[u] = ok ? a.part_o[p * D + e] : 0.f;
         if constexpr (VEC) uv[u] = ok ? a.part_u[p * D + e] : 0.f;
       }
+      // batch maximum first, then independent weights (hardware exp2)
+      float mb = M;
+#pragma unroll
+      for (int u = 0; u < U; ++u) mb = fmaxf(mb, ml[u].x);
+      if (mb == -INFINITY) continue;
+      const float wa = fast_exp2(M - mb);   // 0 while M is -inf
+      L *= wa;
+      O *= wa;
+      if constexpr (VEC) Uv *= wa;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float mn = fmaxf(M, ml[u].x);
-        if (mn == -INFINITY) continue;
-        const float wa = exp2f(M - mn), wb = exp2f(ml[u].x - mn);
-        L = L * wa + ml[u].y * wb;
-        O = O * wa + ov[u] * wb;
-        if constexpr (VEC) Uv = Uv * wa + uv[u] * wb;
-        M = mn;
+        const float wb = fast_exp2(ml[u].x - mb);   // 0 for empty items (-inf)
+        L = fmaf(ml[u].y, wb, L);
+        O = fmaf(ov[u], wb, O);
+        if constexpr (VEC) Uv = fmaf(uv[u], wb, Uv);
       }
+      M = mb;
     }
   }
   if constexpr (VEC) {

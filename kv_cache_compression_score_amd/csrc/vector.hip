@@ -86,8 +86,9 @@ struct ResidualArgs {
   float rope_base;
 };
 
-// Workgroup = 64 pool entries of one head, 4 waves.  Wave w owns row block
-// w/2 and the column blocks of half w%2; each 32x32 output block is
+// A few workgroups per head stage W_h once, then walk the head's pool in
+// tiles of 64 entries, 4 waves each.  Wave w owns row block w/2 and the
+// column blocks of half w%2; each 32x32 output block is
 // K~ W^T over d/2 steps of v_mfma_f32_32x32x2f32, and the squared residual
 // is summed over the columns in-lane, across the 32 lanes of a half-wave
 // (DPP), then over the two halves through LDS.
@@ -103,22 +104,25 @@ __global__ __launch_bounds__(VT) void vector_residual_kernel(ResidualArgs a) {
   __shared__ float part[2][RPW];
 
   const int h = blockIdx.y, b = blockIdx.z, head = b * a.Hkv + h;
-  const int j0 = blockIdx.x * RPW;
   const int tid = threadIdx.x;
   const int cnt = min(max(a.pool_count[head], 0), a.N_max);
   float* ne = a.neg_eps + (size_t)head * a.N_max;
-  const int jend = min(j0 + RPW, a.N_max);
-  if (j0 >= cnt) {
-    for (int j = j0 + tid; j < jend; j += VT) ne[j] = -INFINITY;
-    return;
-  }
+  // entries past the pool
+  for (int j = cnt + (int)blockIdx.x * VT + tid; j < a.N_max; j += (int)gridDim.x * VT)
+    ne[j] = -INFINITY;
+  if ((int)blockIdx.x * RPW >= cnt) return;
 
+  // W_h once per workgroup; the workgroup then walks its tiles of 64 entries
   const float4* w4 = reinterpret_cast<const float4*>(a.w + (size_t)h * D * D);
   for (int i = tid; i < D * D / 4; i += VT) {
     const float4 x = w4[i];
     const int o = (4 * i) / D, c = (4 * i) % D;
     Wl[o][c] = x.x; Wl[o][c + 1] = x.y; Wl[o][c + 2] = x.z; Wl[o][c + 3] = x.w;
   }
+#pragma unroll 1
+  for (int j0 = (int)blockIdx.x * RPW; j0 < cnt; j0 += (int)gridDim.x * RPW) {
+  const int jend = min(j0 + RPW, a.N_max);
+  __syncthreads();   // the previous tile's rows are no longer read
   {
     const int r = tid / 4, q4 = tid % 4, j = j0 + r;
     float kx[EQ], vx[EQ];
@@ -152,18 +156,25 @@ __global__ __launch_bounds__(VT) void vector_residual_kernel(ResidualArgs a) {
   float rs[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) rs[e] = 0.f;
+  // the wave's column blocks are independent accumulator chains: interleave them
+  f32x16 acc[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) acc[c] = f32x16{};
+#pragma unroll 8
+  for (int ks = 0; ks < D / 2; ++ks) {
+    const float av = Kt[rb * 32 + l32][2 * ks + hf];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+          av, Wl[((wave & 1) * CPW + c) * 32 + l32][2 * ks + hf], acc[c], 0, 0, 0);
+  }
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {
     const int cb = (wave & 1) * CPW + c;
-    f32x16 acc = {};
-#pragma unroll 8
-    for (int ks = 0; ks < D / 2; ++ks)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Kt[rb * 32 + l32][2 * ks + hf],
-                                                 Wl[cb * 32 + l32][2 * ks + hf], acc, 0, 0, 0);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int row = rb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
-      const float r = Vt[row][cb * 32 + l32] - acc[e];
+      const float r = Vt[row][cb * 32 + l32] - acc[c][e];
       rs[e] = fmaf(r, r, rs[e]);
     }
   }
@@ -176,7 +187,8 @@ __global__ __launch_bounds__(VT) void vector_residual_kernel(ResidualArgs a) {
   __syncthreads();
   if (tid < RPW) {
     const int j = j0 + tid;
-    if (j < jend) ne[j] = j < cnt ? -(part[0][tid] + part[1][tid]) : -INFINITY;
+    if (j < min(jend, cnt)) ne[j] = -(part[0][tid] + part[1][tid]);
+  }
   }
 }
 
@@ -376,7 +388,8 @@ extern "C" int kv_vector_route(const float* scores, const int32_t* ctx_len, cons
   r.B = B; r.Hkv = Hkv; r.N_max = N_max; r.rope_base = rope_base;
   {
     TimedLaunch t("vector_residual", st);
-    const dim3 grid((unsigned)ceil_div(N_max, RPW), Hkv, B);
+    // a few workgroups per head (W staged once each), walking 64-entry tiles
+    const dim3 grid((unsigned)std::max(1, std::min(ceil_div(N_max, RPW), 8)), Hkv, B);
     if (dtype == KV_BF16) {
       if (d == 128) vector_residual_kernel<__bf16, 128><<<grid, VT, 0, st>>>(r);
       else vector_residual_kernel<__bf16, 64><<<grid, VT, 0, st>>>(r);

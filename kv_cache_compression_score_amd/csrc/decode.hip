@@ -23,7 +23,7 @@ namespace kvcc {
 namespace {
 
 constexpr int DT = 256;
-constexpr int CH = 128;          // rows per work item
+constexpr int CH = 256;          // rows per work item (two passes of NG*RPG rows)
 constexpr int RPG = 8;           // rows per lane group per pass over an item
 constexpr bool PERSISTENT = false;   // grid = resident workgroups, items walked grid-stride
 constexpr int MAX_HEADS = 4096;

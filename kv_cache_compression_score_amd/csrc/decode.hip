@@ -25,7 +25,6 @@ namespace {
 constexpr int DT = 256;
 constexpr int CH = 256;          // rows per work item (two passes of NG*RPG rows)
 constexpr int RPG = 8;           // rows per lane group per pass over an item
-constexpr bool PERSISTENT = false;   // grid = resident workgroups, items walked grid-stride
 constexpr int MAX_HEADS = 4096;
 
 struct DecodeArgs {
@@ -103,13 +102,149 @@ __device__ __forceinline__ void unpack16<float>(const uint4 w, float* x) {
   x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
 }
 
-template <typename T, int D, int GT, bool VEC>
+// One lane's slice (EPL elements) of the query of each of the GT heads of a
+// group.  bf16 slices stay packed: the lane's 16 bytes of a key row enter
+// v_dot2 against them directly (a bf16 product is exact in fp32) and the
+// scale multiplies the reduced sum.  fp32 slices are scaled up front.
+template <typename T, int GT> struct QSlices;
+
+template <int GT> struct QSlices<__bf16, GT> {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  uint4 q[GT];
+  template <int D>
+  __device__ void load(const DecodeArgs& a, int b, int h, int qsub, int sub) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      const int jg = qsub * GT + g;
+      q[g] = make_uint4(0, 0, 0, 0);
+      if (jg < a.G)
+        q[g] = ld16(static_cast<const char*>(a.q) +
+                    (((size_t)b * a.Hq + h * a.G + jg) * D + (size_t)sub * 8) * sizeof(__bf16));
+    }
+  }
+  static __device__ __forceinline__ float d2(uint32_t x, uint32_t y, float s) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, x), __builtin_bit_cast(bf2, y), s,
+                                           false);
+  }
+  __device__ __forceinline__ float score(int g, const uint4 k, float c) const {
+    return d2(q[g].w, k.w, d2(q[g].z, k.z, d2(q[g].y, k.y, d2(q[g].x, k.x, 0.f))));
+  }
+  static constexpr bool kScaled = false;
+};
+
+template <int GT> struct QSlices<float, GT> {
+  float q[GT][4];
+  template <int D>
+  __device__ void load(const DecodeArgs& a, int b, int h, int qsub, int sub) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      const int jg = qsub * GT + g;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (jg < a.G)
+        w = ld16(static_cast<const char*>(a.q) +
+                 (((size_t)b * a.Hq + h * a.G + jg) * D + (size_t)sub * 4) * sizeof(float));
+      q[g][0] = __uint_as_float(w.x) * a.c; q[g][1] = __uint_as_float(w.y) * a.c;
+      q[g][2] = __uint_as_float(w.z) * a.c; q[g][3] = __uint_as_float(w.w) * a.c;
+    }
+  }
+  __device__ __forceinline__ float score(int g, const uint4 k, float) const {
+    float s = q[g][0] * __uint_as_float(k.x);
+    s = fmaf(q[g][1], __uint_as_float(k.y), s);
+    s = fmaf(q[g][2], __uint_as_float(k.z), s);
+    return fmaf(q[g][3], __uint_as_float(k.w), s);
+  }
+  static constexpr bool kScaled = true;
+};
+
+// A lane group's running base-2 softmax state for the GT query heads over
+// the rows it has seen: maximum m, sum l, and o = sum of weight * row.
+template <int GT, int EPL> struct RowState {
+  float m[GT], l[GT], o[GT][EPL];
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      m[g] = -INFINITY;
+      l[g] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[g][e] = 0.f;
+    }
+  }
+  // raise the maximum to cover a pass's scores (rows with ok[u]), rescaling
+  template <int R>
+  __device__ __forceinline__ void cover(const float (&sc)[R][GT], const bool (&ok)[R]) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      float mm = m[g];
+#pragma unroll
+      for (int u = 0; u < R; ++u)
+        if (ok[u]) mm = fmaxf(mm, sc[u][g]);
+      if (mm != -INFINITY && mm != m[g]) {
+        const float w = fast_exp2(m[g] - mm);   // 0 when m was -inf
+        l[g] *= w;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[g][e] *= w;
+        m[g] = mm;
+      }
+    }
+  }
+  __device__ __forceinline__ void add(const float (&sc)[GT], const float (&x)[EPL]) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      const float p = fast_exp2(sc[g] - m[g]);
+      l[g] += p;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[g][e] = fmaf(p, x[e], o[g][e]);
+    }
+  }
+  // park this lane group's state in LDS for the group merge
+  template <int NG, int D>
+  __device__ __forceinline__ void park(float (&sm)[NG][GT][D], float (&sm_m)[NG][GT],
+                                       float (&sm_l)[NG][GT], int grp, int sub) const {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      if (sub == 0) { sm_m[grp][g] = m[g]; sm_l[grp][g] = l[g]; }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sm[grp][g][sub * EPL + e] = o[g][e];
+    }
+  }
+};
+
+// Fixed-order merge of the NG parked lane-group states.  Slot k of this
+// thread is x = tid + k * DT, i.e. (g, e) = (x / D, x % D), when x < GT * D.
+template <int NG, int GT, int D>
+struct GroupMerge {
+  static constexpr int S = (GT * D + DT - 1) / DT;
+  float M[S], L[S], O[S];
+  __device__ __forceinline__ void run(const float (&sm)[NG][GT][D], const float (&sm_m)[NG][GT],
+                                      const float (&sm_l)[NG][GT], int tid) {
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      const int x = tid + k * DT;
+      M[k] = -INFINITY; L[k] = 0.f; O[k] = 0.f;
+      if (GT * D % DT != 0 && x >= GT * D) continue;
+      const int g = x / D, e = x % D;
+      float mx = -INFINITY;
+      for (int r = 0; r < NG; ++r) mx = fmaxf(mx, sm_m[r][g]);
+      if (mx == -INFINITY) continue;
+      float l = 0.f, o = 0.f;
+      for (int r = 0; r < NG; ++r) {
+        const float w = fast_exp2(sm_m[r][g] - mx);
+        l = fmaf(sm_l[r][g], w, l);
+        o = fmaf(sm[r][g][e], w, o);
+      }
+      M[k] = mx; L[k] = l; O[k] = o;
+    }
+  }
+};
+
+template <typename T, int D, int GT>
 __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
   constexpr int EPL = 16 / (int)sizeof(T);     // elements per lane
   constexpr int LPR = D / EPL;                 // lanes per row (power of two, <= 32)
   constexpr int NG = DT / LPR;                 // row groups per workgroup
   constexpr int PASS = NG * RPG;               // rows per pass over an item
   constexpr int ROWB = D * (int)sizeof(T);
+  typedef GroupMerge<NG, GT, D> Merge;
 
   __shared__ int wtot[DT / WAVE];
   __shared__ float sm_m[NG][GT], sm_l[NG][GT];
@@ -125,9 +260,106 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
     for (int i = threadIdx.x; i <= H; i += DT) a.item_start[i] = ist[i];
   const int tid = threadIdx.x, grp = tid / LPR, sub = tid % LPR;
   const int qsub = blockIdx.y;
-  // revolutions per position of this lane's rotary pairs (routed cache only)
-  double rope_g[VEC ? EPL / 2 : 1];
-  if constexpr (VEC) {
+
+  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const int head = find_item_head(ist, H, it);
+    const int b = head / a.Hkv, h = head % a.Hkv;
+    const long long r0 = off[head] + (long long)(it - ist[head]) * CH;
+    const long long r1 = min(r0 + CH, off[head + 1]);
+
+    QSlices<T, GT> qs;
+    qs.template load<D>(a, b, h, qsub, sub);
+    RowState<GT, EPL> st;
+    st.reset();
+    for (long long base = r0; base < r1; base += PASS) {
+      uint4 kr[RPG], vr[RPG];
+      bool ok[RPG];
+#pragma unroll
+      for (int u = 0; u < RPG; ++u) {
+        const long long row = base + grp + (long long)u * NG;
+        ok[u] = row < r1;
+        kr[u] = make_uint4(0, 0, 0, 0);
+        vr[u] = make_uint4(0, 0, 0, 0);
+        if (ok[u]) {
+          kr[u] = ld16(a.kc + (size_t)row * ROWB + sub * 16);
+          vr[u] = ld16(a.vc + (size_t)row * ROWB + sub * 16);
+        }
+      }
+      float sc[RPG][GT];
+#pragma unroll
+      for (int u = 0; u < RPG; ++u)
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+          sc[u][g] = group_sum<LPR>(qs.score(g, kr[u], a.c));
+          if (!QSlices<T, GT>::kScaled) sc[u][g] *= a.c;
+        }
+      st.cover(sc, ok);
+#pragma unroll
+      for (int u = 0; u < RPG; ++u) {
+        if (ok[u]) {
+          float vx[EPL];
+          unpack16<T>(vr[u], vx);
+          st.add(sc[u], vx);
+        }
+      }
+    }
+
+    // merge the row groups (fixed order) into this item's partial
+    st.park(sm_o, sm_m, sm_l, grp, sub);
+    __syncthreads();
+    Merge mg;
+    mg.run(sm_o, sm_m, sm_l, tid);
+    const size_t pbase = ((size_t)qsub * a.items_max + it) * GT;
+#pragma unroll
+    for (int k = 0; k < Merge::S; ++k) {
+      const int x = tid + k * DT;
+      if (GT * D % DT != 0 && x >= GT * D) continue;
+      const int g = x / D, e = x % D;
+      a.part_o[(pbase + g) * D + e] = mg.O[k];
+      if (e == 0) a.part_ml[pbase + g] = make_float2(mg.M[k], mg.L[k]);
+    }
+    __syncthreads();
+  }
+}
+
+// Split kernel over a routed cache.  Each item first sorts its rows into two
+// lists in LDS, in row order within each: exact rows (value row vmap[r]) and
+// rebuilt rows (position pos[r]).  The lane groups walk the exact rows (key
+// and value loads, no per-row branch), merge, then walk the rebuilt rows:
+// the key row is turned back by RoPE^-1 and accumulated as U, the sum that
+// the merge kernel multiplies by W_h once per query head.  The two phases'
+// states meet in the item's partial under one maximum.
+template <typename T, int D, int GT>
+__global__ __launch_bounds__(DT) void vector_decode_split(DecodeArgs a) {
+  constexpr int EPL = 16 / (int)sizeof(T);
+  constexpr int LPR = D / EPL;
+  constexpr int NG = DT / LPR;
+  constexpr int PASS = NG * RPG;
+  constexpr int ROWB = D * (int)sizeof(T);
+  constexpr int NWV = DT / WAVE;
+  static_assert(CH == DT, "one row of an item per thread when routing it");
+  typedef GroupMerge<NG, GT, D> Merge;
+
+  __shared__ int wtot[NWV];
+  __shared__ int wcnt[2][NWV];
+  __shared__ int2 lst[CH];
+  __shared__ float sm_m[NG][GT], sm_l[NG][GT];
+  __shared__ float sm_o[NG][GT][D];
+  extern __shared__ long long dyn[];
+  const int H = a.B * a.Hkv;
+  long long* off = dyn;
+  int* ist = reinterpret_cast<int*>(dyn + H + 1);
+
+  build_items(a, off, ist, wtot);
+  const int n_items = ist[H];
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i <= H; i += DT) a.item_start[i] = ist[i];
+  const int tid = threadIdx.x, grp = tid / LPR, sub = tid % LPR;
+  const int lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int qsub = blockIdx.y;
+  // revolutions per position of this lane's rotary pairs
+  double rope_g[EPL / 2];
+  {
     const double l2b = a.rope_base > 0.f ? log2((double)a.rope_base) : 0.0;
 #pragma unroll
     for (int m2 = 0; m2 < EPL / 2; ++m2)
@@ -140,168 +372,155 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
     const long long r0 = off[head] + (long long)(it - ist[head]) * CH;
     const long long r1 = min(r0 + CH, off[head + 1]);
 
-    // query slices (this lane's EPL elements) of the GT query heads, in base 2
-    float qv[GT][EPL];
+    // route the item's rows: lst = [exact (row, vmap) ... | rebuilt (row, pos) ...]
+    {
+      const bool in = r0 + tid < r1;
+      int vm = 0, ps = 0;
+      if (in) { vm = a.vmap[r0 + tid]; ps = a.pos[r0 + tid]; }
+      const bool ex = in && vm >= 0, rb = in && vm < 0;
+      const uint64_t be = __ballot(ex), bb = __ballot(rb);
+      if (lane == 0) { wcnt[0][wave] = __popcll(be); wcnt[1][wave] = __popcll(bb); }
+      __syncthreads();
+      int ne = 0, pe = 0, pb = 0;
 #pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      const int jg = qsub * GT + g;
-      if (jg < a.G) {
-        const int j = h * a.G + jg;
-        const char* qp = static_cast<const char*>(a.q) +
-                         (((size_t)b * a.Hq + j) * D + sub * EPL) * sizeof(T);
-        unpack16<T>(ld16(qp), qv[g]);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) qv[g][e] *= a.c;
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) qv[g][e] = 0.f;
+      for (int w = 0; w < NWV; ++w) {
+        ne += wcnt[0][w];
+        if (w < wave) { pe += wcnt[0][w]; pb += wcnt[1][w]; }
       }
+      if (ex) lst[pe + (int)mbcnt(be)] = make_int2(tid, vm);
+      if (rb) lst[ne + pb + (int)mbcnt(bb)] = make_int2(tid, ps);
+      __syncthreads();
     }
+    int n_ex = 0, n_all = 0;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) { n_ex += wcnt[0][w]; n_all += wcnt[0][w] + wcnt[1][w]; }
 
-    float mg[GT], lg[GT], og[GT][EPL];
-    float ou[VEC ? GT : 1][EPL];
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      mg[g] = -INFINITY;
-      lg[g] = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) og[g][e] = 0.f;
-    }
-#pragma unroll
-    for (int g = 0; g < (VEC ? GT : 1); ++g)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) ou[g][e] = 0.f;
-    for (long long base = r0; base < r1; base += PASS) {
+    QSlices<T, GT> qs;
+    qs.template load<D>(a, b, h, qsub, sub);
+    RowState<GT, EPL> st;
+    st.reset();
+    // exact rows
+    for (int base = 0; base < n_ex; base += PASS) {
       uint4 kr[RPG], vr[RPG];
-      int vm[VEC ? RPG : 1], pp[VEC ? RPG : 1];
+      bool ok[RPG];
 #pragma unroll
       for (int u = 0; u < RPG; ++u) {
-        const long long row = base + grp + (long long)u * NG;
+        const int idx = base + grp + u * NG;
+        ok[u] = idx < n_ex;
         kr[u] = make_uint4(0, 0, 0, 0);
         vr[u] = make_uint4(0, 0, 0, 0);
-        if constexpr (VEC) { vm[u] = -1; pp[u] = 0; }
-        if (row < r1) {
-          kr[u] = ld16(a.kc + (size_t)row * ROWB + sub * 16);
-          if constexpr (VEC) {
-            vm[u] = a.vmap[row];
-            pp[u] = a.pos[row];
-            if (vm[u] >= 0 && vm[u] < a.vcap) vr[u] = ld16(a.vc + (size_t)vm[u] * ROWB + sub * 16);
-          } else {
-            vr[u] = ld16(a.vc + (size_t)row * ROWB + sub * 16);
-          }
+        if (ok[u]) {
+          const int2 e = lst[idx];
+          kr[u] = ld16(a.kc + (size_t)(r0 + e.x) * ROWB + sub * 16);
+          if (e.y < a.vcap) vr[u] = ld16(a.vc + (size_t)e.y * ROWB + sub * 16);
         }
       }
       float sc[RPG][GT];
 #pragma unroll
-      for (int u = 0; u < RPG; ++u) {
-        float kx[EPL];
-        unpack16<T>(kr[u], kx);
+      for (int u = 0; u < RPG; ++u)
 #pragma unroll
         for (int g = 0; g < GT; ++g) {
-          float s = 0.f;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) s = fmaf(qv[g][e], kx[e], s);
-          sc[u][g] = group_sum<LPR>(s);
+          sc[u][g] = group_sum<LPR>(qs.score(g, kr[u], a.c));
+          if (!QSlices<T, GT>::kScaled) sc[u][g] *= a.c;
         }
-      }
-      // online merge of this pass into the group's running (max, sum, o)
-#pragma unroll
-      for (int g = 0; g < GT; ++g) {
-        float m = mg[g];
-#pragma unroll
-        for (int u = 0; u < RPG; ++u)
-          if (base + grp + (long long)u * NG < r1) m = fmaxf(m, sc[u][g]);
-        if (m != -INFINITY && m != mg[g]) {
-          const float w = fast_exp2(mg[g] - m);   // 0 when mg was -inf
-          lg[g] *= w;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) og[g][e] *= w;
-          if constexpr (VEC) {
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) ou[g][e] *= w;
-          }
-          mg[g] = m;
-        }
-      }
+      st.cover(sc, ok);
 #pragma unroll
       for (int u = 0; u < RPG; ++u) {
-        if (base + grp + (long long)u * NG < r1) {
+        if (ok[u]) {
           float vx[EPL];
-          bool rebuilt = false;
-          if constexpr (VEC) rebuilt = vm[u] < 0;
-          if (rebuilt) {
-            // de-rotated key: pairs (2i, 2i+1) of this lane's elements turn back
-            unpack16<T>(kr[u], vx);
-            if (a.rope_base > 0.f) {
-#pragma unroll
-              for (int m2 = 0; m2 < EPL / 2; ++m2) {
-                double r = (double)pp[u] * rope_g[m2];
-                r -= floor(r);
-                const float rv = (float)r;
-                const float s = __builtin_amdgcn_sinf(rv), c = __builtin_amdgcn_cosf(rv);
-                const float x = vx[2 * m2], y = vx[2 * m2 + 1];
-                vx[2 * m2] = x * c + y * s;
-                vx[2 * m2 + 1] = y * c - x * s;
-              }
-            }
-          } else {
-            unpack16<T>(vr[u], vx);
-          }
-#pragma unroll
-          for (int g = 0; g < GT; ++g) {
-            const float p = fast_exp2(sc[u][g] - mg[g]);
-            lg[g] += p;
-            if constexpr (VEC) {
-              if (rebuilt) {
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) ou[g][e] = fmaf(p, vx[e], ou[g][e]);
-                continue;
-              }
-            }
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) og[g][e] = fmaf(p, vx[e], og[g][e]);
-          }
+          unpack16<T>(vr[u], vx);
+          st.add(sc[u], vx);
         }
       }
     }
+    st.park(sm_o, sm_m, sm_l, grp, sub);
+    __syncthreads();
+    Merge ex;
+    ex.run(sm_o, sm_m, sm_l, tid);
+    __syncthreads();
 
-    // merge the row groups (fixed order) into this item's partial
+    // rebuilt rows
+    st.reset();
+    for (int base = n_ex; base < n_all; base += PASS) {
+      uint4 kr[RPG];
+      int pp[RPG];
+      bool ok[RPG];
+#pragma unroll
+      for (int u = 0; u < RPG; ++u) {
+        const int idx = base + grp + u * NG;
+        ok[u] = idx < n_all;
+        kr[u] = make_uint4(0, 0, 0, 0);
+        pp[u] = 0;
+        if (ok[u]) {
+          const int2 e = lst[idx];
+          kr[u] = ld16(a.kc + (size_t)(r0 + e.x) * ROWB + sub * 16);
+          pp[u] = e.y;
+        }
+      }
+      float sc[RPG][GT];
+#pragma unroll
+      for (int u = 0; u < RPG; ++u)
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+          sc[u][g] = group_sum<LPR>(qs.score(g, kr[u], a.c));
+          if (!QSlices<T, GT>::kScaled) sc[u][g] *= a.c;
+        }
+      st.cover(sc, ok);
+#pragma unroll
+      for (int u = 0; u < RPG; ++u) {
+        if (ok[u]) {
+          // RoPE^-1: pairs (2i, 2i+1) of this lane's elements turn back by
+          // the angle of position pp (revolutions reduced in double)
+          float kx[EPL];
+          unpack16<T>(kr[u], kx);
+          if (a.rope_base > 0.f) {
+#pragma unroll
+            for (int m2 = 0; m2 < EPL / 2; ++m2) {
+              double r = (double)pp[u] * rope_g[m2];
+              r -= floor(r);
+              const float rv = (float)r;
+              const float s = __builtin_amdgcn_sinf(rv), c = __builtin_amdgcn_cosf(rv);
+              const float x = kx[2 * m2], y = kx[2 * m2 + 1];
+              kx[2 * m2] = x * c + y * s;
+              kx[2 * m2 + 1] = y * c - x * s;
+            }
+          }
+          st.add(sc[u], kx);
+        }
+      }
+    }
+    st.park(sm_o, sm_m, sm_l, grp, sub);
+    __syncthreads();
+    Merge rb;
+    rb.run(sm_o, sm_m, sm_l, tid);
+
+    // the item's partial: both phases under one maximum
     const size_t pbase = ((size_t)qsub * a.items_max + it) * GT;
 #pragma unroll
-    for (int half = 0; half < (VEC ? 2 : 1); ++half) {
-#pragma unroll
-      for (int g = 0; g < GT; ++g) {
-        if (half == 0 && sub == 0) { sm_m[grp][g] = mg[g]; sm_l[grp][g] = lg[g]; }
-#pragma unroll
-        for (int e = 0; e < EPL; ++e)
-          sm_o[grp][g][sub * EPL + e] = half == 0 ? og[g][e] : ou[VEC ? g : 0][e];
+    for (int k = 0; k < Merge::S; ++k) {
+      const int x = tid + k * DT;
+      if (GT * D % DT != 0 && x >= GT * D) continue;
+      const int g = x / D, e = x % D;
+      const float M = fmaxf(ex.M[k], rb.M[k]);
+      float L = 0.f, O = 0.f, U = 0.f;
+      if (M != -INFINITY) {
+        const float we = fast_exp2(ex.M[k] - M), wr = fast_exp2(rb.M[k] - M);
+        L = fmaf(ex.L[k], we, rb.L[k] * wr);
+        O = ex.O[k] * we;
+        U = rb.O[k] * wr;
       }
-      __syncthreads();
-      for (int x = tid; x < GT * D; x += DT) {
-        const int g = x / D, e = x % D;
-        float M = -INFINITY;
-        for (int r = 0; r < NG; ++r) M = fmaxf(M, sm_m[r][g]);
-        float L = 0.f, O = 0.f;
-        if (M != -INFINITY) {
-          for (int r = 0; r < NG; ++r) {
-            const float w = fast_exp2(sm_m[r][g] - M);
-            L = fmaf(sm_l[r][g], w, L);
-            O = fmaf(sm_o[r][g][e], w, O);
-          }
-        }
-        (half == 0 ? a.part_o : a.part_u)[(pbase + g) * D + e] = O;
-        if (half == 0 && e == 0) a.part_ml[pbase + g] = make_float2(M, L);
-      }
-      __syncthreads();
+      a.part_o[(pbase + g) * D + e] = O;
+      a.part_u[(pbase + g) * D + e] = U;
+      if (e == 0) a.part_ml[pbase + g] = make_float2(M, L);
     }
+    __syncthreads();
   }
 }
 
-// Per (head, query sub-group): merge the head's items in item order.  Loads
-// are batched so a head's items are fetched a few at a time, not one by one.
 // Per (head, query sub-group): merge the head's items in item order, loads
-// batched 32 items at a time (the batch maximum first, then the weights).  A routed cache also merges the rebuilt-row
-// sums U and adds W U (one d x d product per query head) before dividing.
+// batched 32 items at a time (the batch maximum first, then the weights).  A
+// routed cache also merges the rebuilt-row sums U and adds W U (one d x d
+// product per query head) before dividing.
 template <int D, int GT, bool VEC>
 __global__ __launch_bounds__(GT * D) void decode_merge(DecodeArgs a) {
   constexpr int U = 32;
@@ -394,26 +613,16 @@ bool plan_decode(int B, int Hq, int Hkv, int d, int64_t cap, DecodePlan* p, bool
   return true;
 }
 
-// Resident workgroups of a kernel on the current device.
-template <typename K>
-int resident_slots(K kernel, int threads, size_t dyn) {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dyn) != hipSuccess ||
-      cus < 1 || per_cu < 1)
-    return 8192;
-  return cus * per_cu;
-}
-
 template <typename T, int D, int GT, bool VEC>
 void launch_decode(const DecodeArgs& a, hipStream_t st) {
   const size_t dyn = (size_t)(a.B * a.Hkv + 1) * (sizeof(long long) + sizeof(int));
-  const int gx = PERSISTENT ? resident_slots(decode_split<T, D, GT, VEC>, DT, dyn) : 8192;
-  const dim3 grid((unsigned)std::min(a.items_max, gx), a.n_sub);
-  {
-    TimedLaunch t(VEC ? "vector_decode_split" : "decode_split", st);
-    decode_split<T, D, GT, VEC><<<grid, DT, dyn, st>>>(a);
+  const dim3 grid((unsigned)std::min(a.items_max, 8192), a.n_sub);
+  if constexpr (VEC) {
+    TimedLaunch t("vector_decode_split", st);
+    vector_decode_split<T, D, GT><<<grid, DT, dyn, st>>>(a);
+  } else {
+    TimedLaunch t("decode_split", st);
+    decode_split<T, D, GT><<<grid, DT, dyn, st>>>(a);
   }
   {
     TimedLaunch t(VEC ? "vector_decode_merge" : "decode_merge", st);

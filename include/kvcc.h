@@ -281,7 +281,9 @@ int kv_vector_compact(const void* k, const void* v, int B, int Hkv, int N_max, i
  * kv_decode_attn with each row's value taken from v_c[vmap[r]] or, for
  * vmap[r] < 0, rebuilt as W_h RoPE^-1(k_c[r]) at position pos[r].  The
  * rebuilt rows enter as W_h (sum_r p_r RoPE^-1(k_c[r])), one d x d product
- * per query head.  workspace: kv_vector_decode_workspace_size() bytes. */
+ * per query head.  A vmap entry at or beyond v_capacity_rows reads as a zero
+ * value row.  A head with no rows gives out = 0 and lse = -inf.
+ * workspace: kv_vector_decode_workspace_size() bytes. */
 size_t kv_vector_decode_workspace_size(int B, int Hq, int Hkv, int d, int64_t capacity_rows);
 int kv_vector_decode(const void* q, const void* k_c, const void* v_c, const int32_t* vmap,
                      const int32_t* pos, const int64_t* offsets, const float* w, float rope_base,

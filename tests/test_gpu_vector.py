@@ -148,3 +148,88 @@ def test_vector_without_approximation_matches_plain_decode():
     assert int(apx_count.sum().item()) == 0
     np.testing.assert_allclose(out.cpu().numpy(), out2.cpu().numpy(), atol=1e-5, rtol=0)
     np.testing.assert_allclose(lse.cpu().numpy(), lse2.cpu().numpy(), atol=1e-5, rtol=0)
+
+
+DEC_CASES = [
+    # B, Hq, Hkv, N, d, dtype, ctx, rope_base, pattern of approximated entries
+    (2, 16, 2, 700, 128, torch.bfloat16, [700, 0], 10000.0, "mixed"),
+    (1, 8, 2, 600, 64, torch.float32, None, 0.0, "rebuilt"),
+    (2, 4, 1, 900, 128, torch.bfloat16, [900, 513], 500000.0, "exact"),
+    (1, 4, 2, 1500, 128, torch.bfloat16, None, 10000.0, "alternate"),
+    (1, 8, 1, 2000, 64, torch.bfloat16, None, 10000.0, "runs"),
+]
+
+
+def routed_cache(lay, v, pattern, rng):
+    """A routed cache laid out on the host: per head a random ascending pool
+    of about half the tokens, approximated entries by `pattern`, key rows,
+    positions and the value map in head order, value rows of the exact
+    entries packed in the same order."""
+    B, Hkv, N, d = lay.k.shape
+    n_b = lay.ctx_len.numpy()
+    pool_idx = np.zeros((B, Hkv, N), np.int32)
+    pool_count = np.zeros(B * Hkv, np.int32)
+    apx = np.zeros((B, Hkv, N), bool)
+    krows, vrows, pos, vmap, off = [], [], [], [], [0]
+    nv = 0
+    for b in range(B):
+        for h in range(Hkv):
+            n = int(n_b[b])
+            c = n // 2
+            t = np.sort(rng.choice(n, size=c, replace=False)) if c else np.zeros(0, np.int64)
+            j = np.arange(c)
+            a = {"mixed": rng.random(c) < 0.6, "rebuilt": np.ones(c, bool),
+                 "exact": np.zeros(c, bool), "alternate": j % 2 == 1,
+                 "runs": (j // 300) % 2 == 0}[pattern]
+            i = b * Hkv + h
+            pool_idx[b, h, :c] = t
+            pool_count[i] = c
+            apx[b, h, :c] = a
+            krows.append(lay.k[b, h, torch.from_numpy(t)])
+            vrows.append(v[b, h, torch.from_numpy(t[~a])])
+            pos.append(t.astype(np.int32))
+            vm = np.full(c, -1, np.int32)
+            vm[~a] = nv + np.arange(int((~a).sum()), dtype=np.int32)
+            nv += int((~a).sum())
+            vmap.append(vm)
+            off.append(off[-1] + c)
+    return (torch.cat(krows), torch.cat(vrows), np.concatenate(pos), np.concatenate(vmap),
+            np.array(off, np.int64), pool_idx, pool_count, apx)
+
+
+@pytest.mark.parametrize("c", DEC_CASES, ids=lambda c: f"G{c[1] // c[2]}d{c[4]}"
+                         f"{'f32' if c[5] == torch.float32 else 'bf16'}-{c[8]}")
+def test_vector_decode_routed_layouts(c):
+    """kv_vector_decode on host-built routed caches: every item exact, every
+    item rebuilt, alternating rows, long runs, G = 8, an empty sequence, and
+    (mixed) an exact row whose value row lies beyond v_capacity_rows, which
+    reads as zeros."""
+    B, Hq, Hkv, N, d, dt, ctx, base, pattern = c
+    log(f"vector decode layout {c}")
+    rng = np.random.default_rng(11)
+    lay = wl.random_case(13, B=B, Hq=Hq, Hkv=Hkv, d=d, N_max=N, W=8, dtype=dt, ctx=ctx)
+    v = (torch.randn(B, Hkv, N, d, generator=torch.Generator().manual_seed(17))).to(dt)
+    w = torch.from_numpy((rng.standard_normal((Hkv, d, d)) / math.sqrt(d)).astype(np.float32))
+    k_c, v_c, pos, vmap, off, pool_idx, pool_count, apx = routed_cache(lay, v, pattern, rng)
+    vcap = v_c.shape[0]
+    v_ref = v.double().numpy().copy()
+    if pattern == "mixed":   # first exact row of head 0 points past the value rows
+        r = int(np.flatnonzero(vmap[:off[1]] >= 0)[0])
+        vmap[r] = vcap + 3
+        v_ref[0, 0, pos[r]] = 0.0
+    out, lse = api.kv_vector_decode(dev(lay.q_dec[0]), dev(k_c), dev(v_c) if vcap else None,
+                                    torch.from_numpy(vmap).cuda(), torch.from_numpy(pos).cuda(),
+                                    torch.from_numpy(off).cuda(), dev(w), Hkv,
+                                    v_capacity_rows=vcap, rope_base=base)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    live = [b for b in range(B) if lay.ctx_len[b] > 1]
+    sl = slice(live[0], live[-1] + 1)
+    assert live == list(range(sl.start, sl.stop))
+    o_ref, l_ref = orc.vector_decode(lay.q_dec[0][sl], lay.k[sl], v_ref[sl], w, pool_idx[sl],
+                                     pool_count.reshape(B, Hkv)[sl].reshape(-1), apx[sl], Hkv,
+                                     base)
+    np.testing.assert_allclose(out[sl], o_ref, atol=1e-2, rtol=0)
+    np.testing.assert_allclose(lse[sl], l_ref, atol=1e-3, rtol=0)
+    for b in set(range(B)) - set(live):   # a sequence with no rows: out 0, lse -inf
+        assert np.all(out[b] == 0) and np.all(np.isneginf(lse[b]))

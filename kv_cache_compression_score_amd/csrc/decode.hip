@@ -523,8 +523,9 @@ __global__ __launch_bounds__(DT) void vector_decode_split(DecodeArgs a) {
 // product per query head) before dividing.
 template <int D, int GT, bool VEC>
 __global__ __launch_bounds__(GT * D) void decode_merge(DecodeArgs a) {
-  constexpr int U = 32;
-  __shared__ float su[VEC ? GT : 1][VEC ? D : 1];
+  constexpr int U = VEC && GT * D > 512 ? 16 : 32;   // partials per batch (registers)
+  __shared__ __attribute__((aligned(16))) float su[VEC ? GT : 1][VEC ? D : 1];
+  __shared__ float wu[VEC ? GT : 1][VEC ? D : 1];
   const int head = blockIdx.x, qsub = blockIdx.y;
   const int b = head / a.Hkv, h = head % a.Hkv;
   const int i0 = a.item_start[head], i1 = a.item_start[head + 1];
@@ -533,6 +534,17 @@ __global__ __launch_bounds__(GT * D) void decode_merge(DecodeArgs a) {
   const int g = x / D, e = x % D, jg = qsub * GT + g;
   const bool live = jg < a.G;
   float M = -INFINITY, L = 0.f, O = 0.f, Uv = 0.f;
+  // Routed cache: O += (W_h U)[e] at the end.  A group of D/4 lanes takes one
+  // row of W_h at a time (16 bytes per lane, so a wave reads whole rows
+  // contiguously), dots it with every query head's U from LDS and sums over
+  // the group.  The rows are requested here, ahead of the partials.
+  constexpr int LW = D / 4, RPP = GT * D / LW, NP = D / RPP;   // lanes per row, rows per pass
+  float4 wv[VEC ? NP : 1];
+  if constexpr (VEC) {
+#pragma unroll
+    for (int pz = 0; pz < NP; ++pz)
+      wv[pz] = reinterpret_cast<const float4*>(a.w + ((size_t)h * D + x / LW + pz * RPP) * D)[x % LW];
+  }
   if (live) {
     for (int it0 = i0; it0 < i1; it0 += U) {
       float2 ml[U];
@@ -567,19 +579,23 @@ __global__ __launch_bounds__(GT * D) void decode_merge(DecodeArgs a) {
   if constexpr (VEC) {
     su[g][e] = Uv;
     __syncthreads();
-    if (live) {   // O += (W U)[e]: row e of W_h against this query head's U
-      const float4* wr = reinterpret_cast<const float4*>(a.w + ((size_t)h * D + e) * D);
-      float acc = 0.f;
-#pragma unroll 8
-      for (int i = 0; i < D / 4; ++i) {
-        const float4 wv = wr[i];
-        acc = fmaf(wv.x, su[g][4 * i], acc);
-        acc = fmaf(wv.y, su[g][4 * i + 1], acc);
-        acc = fmaf(wv.z, su[g][4 * i + 2], acc);
-        acc = fmaf(wv.w, su[g][4 * i + 3], acc);
+    const int j = x % LW;
+#pragma unroll
+    for (int pz = 0; pz < NP; ++pz) {
+      const int r = x / LW + pz * RPP;
+#pragma unroll
+      for (int g2 = 0; g2 < GT; ++g2) {
+        const float4 uv4 = *reinterpret_cast<const float4*>(&su[g2][4 * j]);
+        float t = wv[pz].x * uv4.x;
+        t = fmaf(wv[pz].y, uv4.y, t);
+        t = fmaf(wv[pz].z, uv4.z, t);
+        t = fmaf(wv[pz].w, uv4.w, t);
+        t = group_sum<LW>(t);
+        if (j == 0) wu[g2][r] = t;
       }
-      O += acc;
     }
+    __syncthreads();
+    O += wu[g][e];
   }
   if (!live) return;
   const size_t bj = (size_t)b * a.Hq + h * a.G + jg;

@@ -46,31 +46,38 @@ __global__ void vector_counts_kernel(const int32_t* ctx, int B, int Hkv, int N_m
   k_apx[head] = (int)ka;
 }
 
-// Revolutions of pair i of a d-wide row at position pos, for base > 0.
-__device__ __forceinline__ float rope_rev(int pos, int i, int d, double log2_base) {
-  const double g = exp2(-(2.0 * i / d) * log2_base) * INV_TWO_PI;
+// Revolutions per position of pair i of a d-wide row, for base > 0.
+__device__ __forceinline__ double rope_freq(int i, int d, double log2_base) {
+  return exp2(-(2.0 * i / d) * log2_base) * INV_TWO_PI;
+}
+
+// The angle of position pos at frequency g, reduced to [0, 1) revolutions.
+__device__ __forceinline__ float rope_rev(int pos, double g) {
   double r = (double)pos * g;
   r -= floor(r);
   return (float)r;
 }
 
+// N elements of a row as raw 16-byte words (converted later by unpack_elems).
+template <typename T, int N> struct RawElems { uint4 w[N * (int)sizeof(T) / 16]; };
 template <typename T, int N>
-__device__ __forceinline__ void load_elems(const char* row, int e0, float* x) {
-  if constexpr (sizeof(T) == 2) {
+__device__ __forceinline__ void raw_load(const char* row, int e0, RawElems<T, N>& r) {
 #pragma unroll
-    for (int c = 0; c < N; c += 8) {
-      const uint4 w = ld16(row + (size_t)(e0 + c) * 2);
-      x[c + 0] = bf16_lo(w.x); x[c + 1] = bf16_hi(w.x);
-      x[c + 2] = bf16_lo(w.y); x[c + 3] = bf16_hi(w.y);
-      x[c + 4] = bf16_lo(w.z); x[c + 5] = bf16_hi(w.z);
-      x[c + 6] = bf16_lo(w.w); x[c + 7] = bf16_hi(w.w);
-    }
-  } else {
+  for (int c = 0; c < N * (int)sizeof(T) / 16; ++c) r.w[c] = ld16(row + (size_t)e0 * sizeof(T) + 16 * c);
+}
+template <typename T, int N>
+__device__ __forceinline__ void unpack_elems(const RawElems<T, N>& r, float* x) {
 #pragma unroll
-    for (int c = 0; c < N; c += 4) {
-      const uint4 w = ld16(row + (size_t)(e0 + c) * 4);
-      x[c + 0] = __uint_as_float(w.x); x[c + 1] = __uint_as_float(w.y);
-      x[c + 2] = __uint_as_float(w.z); x[c + 3] = __uint_as_float(w.w);
+  for (int c = 0; c < N * (int)sizeof(T) / 16; ++c) {
+    const uint4 w = r.w[c];
+    if constexpr (sizeof(T) == 2) {
+      x[8 * c + 0] = bf16_lo(w.x); x[8 * c + 1] = bf16_hi(w.x);
+      x[8 * c + 2] = bf16_lo(w.y); x[8 * c + 3] = bf16_hi(w.y);
+      x[8 * c + 4] = bf16_lo(w.z); x[8 * c + 5] = bf16_hi(w.z);
+      x[8 * c + 6] = bf16_lo(w.w); x[8 * c + 7] = bf16_hi(w.w);
+    } else {
+      x[4 * c + 0] = __uint_as_float(w.x); x[4 * c + 1] = __uint_as_float(w.y);
+      x[4 * c + 2] = __uint_as_float(w.z); x[4 * c + 3] = __uint_as_float(w.w);
     }
   }
 }
@@ -102,6 +109,7 @@ __global__ __launch_bounds__(VT) void vector_residual_kernel(ResidualArgs a) {
   __shared__ float Kt[RPW][LD];
   __shared__ float Vt[RPW][LD];
   __shared__ float part[2][RPW];
+  __shared__ double gfreq[D / 2];   // revolutions per position of every rotary pair
 
   const int h = blockIdx.y, b = blockIdx.z, head = b * a.Hkv + h;
   const int tid = threadIdx.x;
@@ -119,23 +127,37 @@ __global__ __launch_bounds__(VT) void vector_residual_kernel(ResidualArgs a) {
     const int o = (4 * i) / D, c = (4 * i) % D;
     Wl[o][c] = x.x; Wl[o][c + 1] = x.y; Wl[o][c + 2] = x.z; Wl[o][c + 3] = x.w;
   }
+  // Thread tid stages quarter tid%4 of row tid/4 of a tile.  The next tile's
+  // rows are requested before this tile's MFMAs, so their gather overlaps
+  // the matrix work; only the unpacking and RoPE^-1 sit between barriers.
+  const int sr = tid / 4, q4 = tid % 4;
+  RawElems<T, EQ> pk, pv;
+  int pt = -1;
+  auto fetch = [&](int jt) __attribute__((always_inline)) {
+    const int j = jt + sr;
+    pt = -1;
+    if (j < cnt) {
+      pt = a.pool_idx[(size_t)head * a.N_max + j];
+      const size_t roff = ((size_t)head * a.N_max + pt) * ROWB;
+      raw_load<T, EQ>(a.k + roff, q4 * EQ, pk);
+      raw_load<T, EQ>(a.v + roff, q4 * EQ, pv);
+    }
+  };
+  fetch((int)blockIdx.x * RPW);
+  if (a.rope_base > 0.f && tid < D / 2) gfreq[tid] = rope_freq(tid, D, log2((double)a.rope_base));
 #pragma unroll 1
   for (int j0 = (int)blockIdx.x * RPW; j0 < cnt; j0 += (int)gridDim.x * RPW) {
   const int jend = min(j0 + RPW, a.N_max);
   __syncthreads();   // the previous tile's rows are no longer read
   {
-    const int r = tid / 4, q4 = tid % 4, j = j0 + r;
     float kx[EQ], vx[EQ];
-    if (j < cnt) {
-      const int t = a.pool_idx[(size_t)head * a.N_max + j];
-      const size_t roff = ((size_t)head * a.N_max + t) * ROWB;
-      load_elems<T, EQ>(a.k + roff, q4 * EQ, kx);
-      load_elems<T, EQ>(a.v + roff, q4 * EQ, vx);
+    if (pt >= 0) {
+      unpack_elems<T, EQ>(pk, kx);
+      unpack_elems<T, EQ>(pv, vx);
       if (a.rope_base > 0.f) {
-        const double l2b = log2((double)a.rope_base);
 #pragma unroll
         for (int m = 0; m < EQ / 2; ++m) {
-          const float rv = rope_rev(t, q4 * EQ / 2 + m, D, l2b);
+          const float rv = rope_rev(pt, gfreq[q4 * EQ / 2 + m]);
           const float s = __builtin_amdgcn_sinf(rv), c = __builtin_amdgcn_cosf(rv);
           const float x = kx[2 * m], y = kx[2 * m + 1];
           kx[2 * m] = x * c + y * s;
@@ -147,9 +169,10 @@ __global__ __launch_bounds__(VT) void vector_residual_kernel(ResidualArgs a) {
       for (int e = 0; e < EQ; ++e) { kx[e] = 0.f; vx[e] = 0.f; }
     }
 #pragma unroll
-    for (int e = 0; e < EQ; ++e) { Kt[r][q4 * EQ + e] = kx[e]; Vt[r][q4 * EQ + e] = vx[e]; }
+    for (int e = 0; e < EQ; ++e) { Kt[sr][q4 * EQ + e] = kx[e]; Vt[sr][q4 * EQ + e] = vx[e]; }
   }
   __syncthreads();
+  if (j0 + (int)gridDim.x * RPW < cnt) fetch(j0 + (int)gridDim.x * RPW);
 
   const int lane = tid & (WAVE - 1), wave = tid / WAVE, l32 = lane & 31, hf = lane >> 5;
   const int rb = wave >> 1;
@@ -160,13 +183,28 @@ __global__ __launch_bounds__(VT) void vector_residual_kernel(ResidualArgs a) {
   f32x16 acc[CPW];
 #pragma unroll
   for (int c = 0; c < CPW; ++c) acc[c] = f32x16{};
-#pragma unroll 8
-  for (int ks = 0; ks < D / 2; ++ks) {
-    const float av = Kt[rb * 32 + l32][2 * ks + hf];
+  // operands of KB k-steps are read from LDS one batch ahead of their MFMAs
+  constexpr int KB = 4, NKB = D / 2 / KB;
+  float av[2][KB], bv[2][CPW][KB];
+  auto ld_ops = [&](int buf, int ks0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < CPW; ++c)
-      acc[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-          av, Wl[((wave & 1) * CPW + c) * 32 + l32][2 * ks + hf], acc[c], 0, 0, 0);
+    for (int kk = 0; kk < KB; ++kk) {
+      av[buf][kk] = Kt[rb * 32 + l32][2 * (ks0 + kk) + hf];
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+        bv[buf][c][kk] = Wl[((wave & 1) * CPW + c) * 32 + l32][2 * (ks0 + kk) + hf];
+    }
+  };
+  ld_ops(0, 0);
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    if (kb + 1 < NKB) ld_ops((kb + 1) & 1, (kb + 1) * KB);
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[kb & 1][kk], bv[kb & 1][c][kk], acc[c],
+                                                      0, 0, 0);
   }
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {

@@ -1,0 +1,112 @@
+"""One score -> select -> compact -> decode step captured in a HIP graph.
+
+The library allocates nothing and records no memset, so the four calls can
+be captured with static buffers.  Every replay, with eager steps and
+synchronisations in between, must reproduce the eager step bit for bit
+(every kernel sums in a fixed order, so repeated runs are bit-identical).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_compression_score_amd import api
+from kv_cache_compression_score_amd import workloads as wl
+from oracle import oracle as orc
+
+from gpu_helpers import dev, log
+
+pytestmark = pytest.mark.gpu
+
+
+def static_step(cfg, lay):
+    """Inputs, outputs and workspaces allocated once; returns (step, buffers)."""
+    q, k, v, c, qd = dev(lay.q_win), dev(lay.k), dev(lay.v), dev(lay.ctx_len), dev(lay.q_dec[0])
+    B, Hkv, N, d = lay.k.shape
+    if cfg.budget_mode == wl.BUDGET_MASS:
+        bud = api.Budget(api.BUDGET_MASS, mass=cfg.ratio, min_ratio=cfg.min_ratio,
+                         max_ratio=cfg.max_ratio)
+        cap = int(math.ceil(B * Hkv * N * cfg.max_ratio))
+    else:
+        bud = api.Budget(api.BUDGET_RATIO, ratio_scalar=cfg.ratio)
+        cap = B * Hkv * orc.budget_count(np.zeros(N), orc.BUDGET_RATIO, ratio=cfg.ratio)
+    f32, i32 = torch.float32, torch.int32
+    buf = dict(
+        scores=torch.empty(B, Hkv, N, device="cuda", dtype=f32),
+        ws_s=torch.zeros(api.kv_score_workspace_size(B, cfg.Hq, Hkv, N, cfg.W, d),
+                         device="cuda", dtype=torch.uint8),
+        idx=torch.empty(B, Hkv, N, device="cuda", dtype=i32),
+        cnt=torch.empty(B * Hkv, device="cuda", dtype=i32),
+        k_c=torch.empty(cap, d, device="cuda", dtype=lay.k.dtype),
+        v_c=torch.empty(cap, d, device="cuda", dtype=lay.k.dtype),
+        pos=torch.empty(cap, device="cuda", dtype=i32),
+        off=torch.empty(B * Hkv + 1, device="cuda", dtype=torch.int64),
+        out=torch.empty(B, cfg.Hq, d, device="cuda", dtype=f32),
+        lse=torch.empty(B, cfg.Hq, device="cuda", dtype=f32),
+        ws_d=torch.zeros(api.kv_decode_workspace_size(B, cfg.Hq, Hkv, d, cap),
+                         device="cuda", dtype=torch.uint8))
+
+    def step():
+        api.kv_score(q, k, c, scores=buf["scores"], workspace=buf["ws_s"])
+        api.kv_select(buf["scores"], c, bud, kept_idx=buf["idx"], kept_count=buf["cnt"])
+        api.kv_compact(k, v, buf["idx"], buf["cnt"], cap,
+                       out=(buf["k_c"], buf["v_c"], buf["pos"], buf["off"]))
+        api.kv_decode_attn(qd, buf["k_c"], buf["v_c"], buf["off"], Hkv, out=buf["out"],
+                           lse=buf["lse"], workspace=buf["ws_d"])
+    return step, buf
+
+
+def snapshot(buf, ctx):
+    """The defined part of every output: scores of tokens t < n_b, kept rows
+    up to offsets[-1], kept indices up to each head's count."""
+    n = int(buf["off"][-1])
+    cnt = buf["cnt"].cpu().numpy()
+    idx = buf["idx"].cpu().numpy().reshape(len(cnt), -1)
+    sc = buf["scores"].cpu()
+    return dict(scores=[sc[b, :, :int(ctx[b])].clone() for b in range(sc.shape[0])],
+                cnt=buf["cnt"].cpu(), off=buf["off"].cpu(),
+                idx=[idx[i, :cnt[i]].copy() for i in range(len(cnt))],
+                k_c=buf["k_c"][:n].cpu(), v_c=buf["v_c"][:n].cpu(), pos=buf["pos"][:n].cpu(),
+                out=buf["out"].cpu(), lse=buf["lse"].cpu())
+
+
+def assert_same(a, b):
+    for key in a:
+        if key == "idx":
+            assert all(np.array_equal(x, y) for x, y in zip(a[key], b[key])), key
+        elif key == "scores":
+            assert all(torch.equal(x, y) for x, y in zip(a[key], b[key])), key
+        else:
+            assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama8b_layer", "ragged_adaptive"])
+def test_graph_replay_matches_eager(name):
+    cfg = wl.CONFIGS[name]
+    log(f"graph capture: {name}")
+    lay = wl.make_layer(cfg)
+    step, buf = static_step(cfg, lay)
+    step()
+    torch.cuda.synchronize()
+    ref = snapshot(buf, lay.ctx_len)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step()
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for key in ("scores", "out", "lse"):
+            buf[key].fill_(-7.0)
+        for key in ("cnt", "off"):
+            buf[key].fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert_same(snapshot(buf, lay.ctx_len), ref)
+        step()   # eager work between the replays
+        torch.cuda.synchronize()
+        assert_same(snapshot(buf, lay.ctx_len), ref)

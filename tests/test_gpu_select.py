@@ -49,8 +49,10 @@ def compare_sets(idx_g, cnt_g, idx_r, cnt_r):
 
 
 KINDS = ["ties", "zeros", "heavy", "uniform"]
+# 12001: a ragged batch whose row length is not a multiple of 4 (the
+# scalar staging path), with a head of 4097 tokens and one of a single token.
 SHAPES = [(2, 3, 1000, [1000, 517]), (1, 2, 32768, [32768]), (1, 2, 40000, [40000]),
-          (3, 1, 64, [64, 1, 63])]
+          (3, 1, 64, [64, 1, 63]), (3, 2, 12001, [12001, 4097, 1])]
 
 
 @pytest.mark.parametrize("kind", ["ties", "zeros", "heavy", "uniform"])

@@ -29,6 +29,7 @@ namespace {
 
 constexpr int VT = 256;
 constexpr int RPW = 64;          // pool entries per residual workgroup
+constexpr int VMC = 8192;        // pool entries per window of the value-map kernel
 constexpr int MAX_HEADS = 4096;
 constexpr double INV_TWO_PI = 0.15915494309189535;
 
@@ -286,14 +287,17 @@ __device__ void scan_two(const VCompactArgs& a, int H, long long* off, long long
   __syncthreads();
 }
 
-// One workgroup per head: walks the head's pool entries 256 at a time,
-// flags the approximated ones (their sorted positions are a contiguous run
-// of apx_pos) and gives every exact entry its packed value row.
+// One workgroup per head, over windows of VMC pool entries: the window's
+// approximated entries (the next run of the ascending apx_pos list, read in
+// parallel) are flagged in LDS, every thread counts the exact entries among
+// its 32 consecutive ones, and one block scan gives each exact entry its
+// packed value row.
 __global__ __launch_bounds__(VT) void vector_vmap_kernel(VCompactArgs a) {
+  constexpr int E = VMC / VT;          // pool entries per thread in a window
   extern __shared__ long long dyn[];   // off[H+1], voff[H+1]
   __shared__ long long wtot[2 * (VT / WAVE)];
-  __shared__ unsigned char flag[VT];
-  __shared__ int wcnt[2][VT / WAVE];
+  __shared__ __attribute__((aligned(16))) unsigned char flag[VMC];
+  __shared__ int wsum[VT / WAVE];
   const int H = a.B * a.Hkv;
   long long* off = dyn;
   long long* voff = dyn + H + 1;
@@ -307,34 +311,61 @@ __global__ __launch_bounds__(VT) void vector_vmap_kernel(VCompactArgs a) {
   const int32_t* ap = a.apx_pos + (size_t)head * a.N_max;
   const long long base = off[head], vbase = voff[head];
   int aptr = 0, vrank = 0;
-  for (int J = 0; J < cnt; J += VT) {
-    flag[tid] = 0;
+  for (int J = 0; J < cnt; J += VMC) {
+    // flag the approximated entries of the window [J, J + VMC): they are the
+    // next entries of the ascending list (at most VMC of them)
+    for (int i = tid; i < VMC / 16; i += VT) reinterpret_cast<uint4*>(flag)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
-    const int x = aptr + tid < acnt ? ap[aptr + tid] : 0x7fffffff;
-    const bool in = x < J + VT;       // sorted and distinct: x >= J
-    if (in && x >= J) flag[x - J] = 1;
-    const uint64_t bin = __ballot(in);
-    if (lane == 0) wcnt[0][wave] = (int)__popcll(bin);
-    __syncthreads();
-    const int j = J + tid;
-    const bool ex = j < cnt && !flag[tid];
-    const uint64_t bex = __ballot(ex);
-    if (lane == 0) wcnt[1][wave] = (int)__popcll(bex);
-    __syncthreads();
-    int before = 0, m = 0, tot = 0;
-    for (int w = 0; w < VT / WAVE; ++w) {
-      if (w < wave) before += wcnt[1][w];
-      m += wcnt[0][w];
-      tot += wcnt[1][w];
+    const int lim = min(acnt, aptr + VMC);
+    int inwin = 0;
+#pragma unroll 8
+    for (int i = aptr + tid; i < lim; i += VT) {
+      const int x = ap[i];
+      if (x >= J && x < J + VMC) { flag[x - J] = 1; ++inwin; }
     }
-    if (j < cnt) {
-      const long long row = base + j;
-      if (row < a.cap)
-        a.vmap[row] = ex ? (int32_t)(vbase + vrank + before + (int)mbcnt(bex)) : -1;
+    inwin = wave_incl_scan<int>(inwin);
+    if (lane == WAVE - 1) wsum[wave] = inwin;
+    __syncthreads();
+    inwin = 0;
+#pragma unroll
+    for (int w = 0; w < VT / WAVE; ++w) inwin += wsum[w];
+    __syncthreads();
+    // exact entries among this thread's E consecutive ones, ranked by a block scan
+    const int j0 = J + E * tid;
+    const uint4* f4 = reinterpret_cast<const uint4*>(flag + E * tid);
+    uint32_t fw[E / 4];
+#pragma unroll
+    for (int q = 0; q < E / 16; ++q) {
+      const uint4 v = f4[q];
+      fw[4 * q] = v.x; fw[4 * q + 1] = v.y; fw[4 * q + 2] = v.z; fw[4 * q + 3] = v.w;
+    }
+    int ex = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      ex += (j0 + e < cnt && ((fw[e / 4] >> (8 * (e % 4))) & 0xffu) == 0) ? 1 : 0;
+    const int inc = wave_incl_scan<int>(ex);
+    if (lane == WAVE - 1) wsum[wave] = inc;
+    __syncthreads();
+    int before = inc - ex, tot = 0;
+#pragma unroll
+    for (int w = 0; w < VT / WAVE; ++w) {
+      if (w < wave) before += wsum[w];
+      tot += wsum[w];
+    }
+    int r = vrank + before;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = j0 + e;
+      if (j < cnt) {
+        const bool apx = ((fw[e / 4] >> (8 * (e % 4))) & 0xffu) != 0;
+        const long long row = base + j;
+        if (row < a.cap) a.vmap[row] = apx ? -1 : (int32_t)(vbase + r);
+        r += apx ? 0 : 1;
+      }
     }
     vrank += tot;
-    aptr += m;
-    __syncthreads();
+    aptr += inwin;
+    __syncthreads();   // flags and wsum are reused by the next window
   }
 }
 

@@ -10,11 +10,13 @@
 // rebuilds the item list from the offsets in LDS and walks it grid-stride,
 // so ragged heads balance by rows, not by head count.  Inside an item a group
 // of d*sizeof(T)/16 lanes owns one row at a time (16 bytes of K and of V per
-// lane, RPG rows in flight), forms the G dot products with a DPP reduction
-// inside the group, and keeps a base-2 (max, sum, o) per query
-// head.  Groups merge through LDS in a fixed order into one partial per item;
-// a second kernel merges each head's items in item order, so the result is
-// deterministic.
+// lane, RPG rows in flight), forms the G dot products (bf16: v_dot2 against
+// the packed query) with a DPP reduction inside the group, and keeps a
+// base-2 (max, sum, o) per query head.  Groups merge through LDS in a fixed
+// order into one partial per item; a second kernel merges each head's items
+// in item order, so the result is deterministic.  A routed (VECTOR) cache has
+// its own split kernel, which first sorts an item's rows into an exact and a
+// rebuilt list, and the merge adds W_h times the rebuilt rows' sum.
 #include <math.h>
 
 #include "common.hpp"

@@ -233,3 +233,79 @@ def test_vector_decode_routed_layouts(c):
     np.testing.assert_allclose(lse[sl], l_ref, atol=1e-3, rtol=0)
     for b in set(range(B)) - set(live):   # a sequence with no rows: out 0, lse -inf
         assert np.all(out[b] == 0) and np.all(np.isneginf(lse[b]))
+
+
+def test_vector_full_size_needle32k():
+    """The routing bench.py times, at its size: needle32k (4 x 8 heads x 32K
+    tokens, window scores from kv_score), p_c = 0.9, p_a = 0.05, rotary base
+    500000, V = W RoPE^-1(K) + noise.  Pool and approximated subset on every
+    head; residuals, compaction and decode on sampled heads and sequences."""
+    cfg = wl.CONFIGS["needle32k"]
+    p_c, p_a, base = 0.9, 0.05, 500000.0
+    log("vector full size: needle32k")
+    lay = wl.make_layer(cfg, with_v=False)
+    B, Hkv, N, d = lay.k.shape
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal((Hkv, d, d)) / math.sqrt(d)).astype(np.float32)
+    k64 = lay.k.double().numpy()
+    v = np.empty((B, Hkv, N, d), np.float32)
+    for b in range(B):
+        for h in range(Hkv):
+            kt = orc.rope_inverse(k64[b, h], np.arange(N), base)
+            noise = rng.standard_normal((N, d)) * rng.choice([0.02, 0.3, 1.0], size=(N, 1))
+            v[b, h] = (kt @ w[h].astype(np.float64).T + noise).astype(np.float32)
+    del k64
+    v_t = torch.from_numpy(v).to(lay.k.dtype)
+    del v
+    k_d, v_d, w_d, c_d = dev(lay.k), dev(v_t), dev(torch.from_numpy(w)), dev(lay.ctx_len)
+    s_d, _ = api.kv_score(dev(lay.q_win), k_d, c_d)
+    pool_idx, pool_count, neg_eps, apx_pos, apx_count = api.kv_vector_route(
+        s_d, c_d, k_d, v_d, w_d, p_c=p_c, p_a=p_a, rope_base=base)
+    torch.cuda.synchronize()
+    s = s_d.cpu().numpy()
+    pi, pc = pool_idx.cpu().numpy(), pool_count.cpu().numpy()
+    ne, ap, ac = neg_eps.cpu().numpy(), apx_pos.cpu().numpy(), apx_count.cpu().numpy()
+    kp, ka = orc.vector_counts(N, p_c, p_a)
+    ri, rc = orc.select(s, lay.ctx_len, orc.BUDGET_K, k=np.full(B * Hkv, kp))
+    assert np.array_equal(pc, rc) and np.all(pc == kp)
+    for b in range(B):
+        for h in range(Hkv):
+            assert np.array_equal(pi[b, h, :kp], ri[b, h, :kp]), (b, h)
+            order = np.lexsort((np.arange(kp), -ne[b, h, :kp].astype(np.float64)))
+            assert ac[b * Hkv + h] == ka
+            assert np.array_equal(ap[b, h, :ka], np.sort(order[:ka])), (b, h)
+    for b, h in [(0, 0), (3, 7)]:
+        eps_ref = orc.vector_residuals(lay.k[b:b + 1, h:h + 1], v_t[b:b + 1, h:h + 1], w[h:h + 1],
+                                       pi[b:b + 1, h:h + 1], pc[b * Hkv + h:b * Hkv + h + 1], base)
+        np.testing.assert_allclose(-ne[b, h, :kp], eps_ref[0, 0, :kp], rtol=1e-3, atol=1e-4 * d)
+
+    cap = int(pc.sum())
+    vcap = int(cap - ac.sum())
+    k_c, v_c, pos, vmap, off, voff = api.kv_vector_compact(k_d, v_d, pool_idx, pool_count,
+                                                           apx_pos, apx_count, cap, vcap)
+    out, lse = api.kv_vector_decode(dev(lay.q_dec[0]), k_c, v_c, vmap, pos, off, w_d, Hkv,
+                                    v_capacity_rows=vcap, rope_base=base)
+    torch.cuda.synchronize()
+    of, vo, vm, ps = off.cpu().numpy(), voff.cpu().numpy(), vmap.cpu().numpy(), pos.cpu().numpy()
+    assert of[-1] == cap and vo[-1] == vcap
+    apx_mask = np.zeros((B, Hkv, N), dtype=bool)
+    for b in range(B):
+        for h in range(Hkv):
+            apx_mask[b, h, ap[b, h, :ka]] = True
+    kb, vb = bits(lay.k), bits(v_t)
+    k_cb, v_cb = bits(k_c.cpu()), bits(v_c.cpu())
+    for b, h in [(0, 0), (1, 5), (3, 7)]:
+        i = b * Hkv + h
+        toks = pi[b, h, :kp]
+        a_m = apx_mask[b, h, :kp]
+        assert np.array_equal(ps[of[i]:of[i + 1]], toks)
+        assert np.array_equal(k_cb[of[i]:of[i + 1]], kb[b, h, toks])
+        assert np.array_equal(vm[of[i]:of[i + 1]][~a_m], np.arange(vo[i], vo[i + 1]))
+        assert np.all(vm[of[i]:of[i + 1]][a_m] == -1)
+        assert np.array_equal(v_cb[vo[i]:vo[i + 1]], vb[b, h, toks[~a_m]])
+    for b in (0, 3):
+        o_ref, l_ref = orc.vector_decode(lay.q_dec[0][b:b + 1], lay.k[b:b + 1], v_t[b:b + 1], w,
+                                         pi[b:b + 1], pc[b * Hkv:(b + 1) * Hkv],
+                                         apx_mask[b:b + 1], Hkv, base)
+        np.testing.assert_allclose(out.cpu().numpy()[b], o_ref[0], atol=1e-2, rtol=0)
+        np.testing.assert_allclose(lse.cpu().numpy()[b], l_ref[0], atol=1e-3, rtol=0)

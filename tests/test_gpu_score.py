@@ -130,3 +130,27 @@ def test_score_from_own_lse_equals_two_pass():
     assert rel.max() < 1e-4, rel.max()
     s_ref, _ = orc.window_scores(lay.q_win, lay.k, lay.ctx_len)
     check_scores(s1.cpu().numpy(), s_ref, lay.ctx_len.numpy(), cfg.W, cfg.G)
+
+
+def test_score_from_lse_needle32k_full():
+    # The one-pass entry point at the size bench.py times (4 x 8 heads x 32K,
+    # W = 64): fed the two-pass call's row LSE it must reproduce the two-pass
+    # scores on every head, and the oracle on sampled heads.
+    cfg = wl.CONFIGS["needle32k"]
+    lay = wl.make_layer(cfg, with_v=False)
+    log("score from lse needle32k")
+    q, k, c = dev(lay.q_win), dev(lay.k), dev(lay.ctx_len)
+    s2, lse = api.kv_score(q, k, c, with_row_lse=True)
+    s1 = api.kv_score_from_lse(q, k, c, lse)
+    torch.cuda.synchronize()
+    a, b = s1.double().cpu().numpy(), s2.double().cpu().numpy()
+    big = b > 2.0 ** -92 * cfg.W * cfg.G
+    rel = np.abs(a - b)[big] / b[big]
+    assert rel.max() < 1e-4, rel.max()
+    np.testing.assert_allclose(a.sum(axis=2), cfg.W * cfg.G, rtol=1e-4)
+    for bb, h in [(0, 2), (3, 6)]:
+        s_ref, _ = orc.window_scores(lay.q_win[bb:bb + 1, h * cfg.G:(h + 1) * cfg.G],
+                                     lay.k[bb:bb + 1, h:h + 1], lay.ctx_len[bb:bb + 1])
+        err = check_scores(s1[bb:bb + 1, h:h + 1].cpu().numpy(), s_ref,
+                           lay.ctx_len[bb:bb + 1].numpy(), cfg.W, cfg.G)
+        log(f"  ({bb}, {h}) max rel score err {err:.3e}")

@@ -12,7 +12,8 @@ from gpu_helpers import dev, log
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,steps", [("llama8b_layer", 2), ("ragged_adaptive", 1)])
+@pytest.mark.parametrize("name,steps", [("llama8b_layer", 2), ("ragged_adaptive", 1),
+                                        ("needle32k", 1)])
 def test_fidelity_matches_oracle(name, steps):
     cfg = wl.CONFIGS[name]
     B = 2 if name == "ragged_adaptive" else None

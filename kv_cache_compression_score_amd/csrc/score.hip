@@ -10,7 +10,9 @@
 //
 // Both sweeps over K tile the logit matrix into 32x32 MFMA blocks with the
 // K tile staged once per workgroup in LDS and each wave holding the Q
-// fragments of two 32-row blocks in registers:
+// fragments of two 32-row blocks in registers.  K tiles of 64 tokens go from
+// HBM to LDS directly (no registers), three tiles ahead of the MFMAs, into
+// four buffers with XOR-swizzled 16-byte columns:
 //   pass 1: C[token,row] = K * Q^T, so one lane owns one row and 16 tokens
 //           per block and keeps a running (max, sum of exp2) per row in
 //           registers; the two half-waves are merged by a lane swizzle and
@@ -22,9 +24,8 @@
 //           half-waves and waves through LDS in a fixed order.
 // All logits are kept in base-2 units: c = scale*log2(e) is applied to the
 // fp32 dot product after the MFMA (bf16 inputs are never rescaled).  The
-// exp2 of every logit runs on the VALU's transcendental unit, which sets the
-// pace next to the MFMA, so the per-logit epilogue is kept to one FMA, one
-// exp2 and one add (plus a max in pass 1); masks only exist in tail tiles.
+// per-logit epilogue is kept to one FMA, one exp2 and one add (plus a max in
+// pass 1); masks only exist in tail tiles.
 #include <math.h>
 #include <stdint.h>
 
@@ -36,10 +37,8 @@ namespace kvcc {
 namespace {
 
 constexpr int TOK = 64;          // tokens per LDS tile
-constexpr int TSUB = TOK / 32;   // 32-token MFMA blocks per tile
 constexpr int RBW = 2;           // 32-row blocks per wave
 constexpr int SLOTS_1 = 256 * 2; // pass-1 chunking target: resident workgroups on 256 CUs
-constexpr int NPF = 2;           // K tiles in flight per workgroup (register prefetch depth)
 
 template <typename T> struct FragT;
 template <> struct FragT<__bf16> { using vec = bf16x8; };   // 8 elements = 16 B
@@ -74,6 +73,50 @@ __device__ __forceinline__ f32x8 load_frag<float>(const void* p) {
   return v;
 }
 
+// A K fragment from a swizzled LDS row: logical 16-byte piece c of the row
+// sits at piece c ^ sw.  bf16: one piece; fp32: pieces c and c + 1.
+template <typename T>
+__device__ __forceinline__ typename FragT<T>::vec load_frag_sw(const unsigned char* row, int c, int sw);
+template <>
+__device__ __forceinline__ bf16x8 load_frag_sw<__bf16>(const unsigned char* row, int c, int sw) {
+  return __builtin_bit_cast(bf16x8, ld16(row + 16 * (c ^ sw)));
+}
+template <>
+__device__ __forceinline__ f32x8 load_frag_sw<float>(const unsigned char* row, int c, int sw) {
+  const uint4 a = ld16(row + 16 * (c ^ sw)), b = ld16(row + 16 * ((c + 1) ^ sw));
+  f32x8 v;
+  v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+  v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+  v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+  v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+  return v;
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land
+// at lds + 16 i (the LDS base goes in M0, which the block restores).  Issued
+// from asm so that the compiler does not answer the pending LDS write with a
+// full vector-memory wait before every later LDS read; the kernel orders them
+// itself (vm_wait, then a barrier).  The load writes no register; its
+// address operands are read at issue.
+__device__ __forceinline__ void lds_dma16(const void* g, unsigned char* lds) {
+  const uint32_t l = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(l)
+      : "memory");
+  (void)saved;
+}
+
+// s_waitcnt on the vector-memory counter only (at most N outstanding).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 struct ScoreArgs {
   const void* q;
   const void* k;
@@ -94,13 +137,15 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
   using V = typename FragT<T>::vec;
   constexpr int KS = D / 16;
   constexpr int ROWB = D * (int)sizeof(T);
-  constexpr int LDS_STRIDE = ROWB + 16;          // pad rows against bank conflicts
-  constexpr int VPR = ROWB / 16;
+  constexpr int VPR = ROWB / 16;                 // 16-byte pieces per K row
   constexpr int TILE_VECS = TOK * VPR;
+  // K tiles travel HBM -> LDS directly (no registers): NB buffers, tile t in
+  // buffer t % NB, requested NB - 1 tiles ahead.
+  constexpr int NB = TOK * ROWB <= 16384 ? 4 : 2;
   constexpr int NT = NW * WAVE;
   constexpr int LPT = (TILE_VECS + NT - 1) / NT;
 
-  __shared__ __attribute__((aligned(16))) unsigned char ktile[2][TOK * LDS_STRIDE];
+  __shared__ __attribute__((aligned(16))) unsigned char ktile[NB][TOK * ROWB];
   __shared__ float red[3][PASS == 2 ? NW : 1][TOK];
   __shared__ __attribute__((aligned(8))) int rowpos[PASS == 2 ? NW * RBW * 32 : 2];
 
@@ -183,43 +228,40 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
     }
   }
 
-  // K tiles in flight: tile t travels in register slot t % NPF (a compile-time
-  // index: the tile loop below is unrolled by NPF) until it is stored to LDS.
-  uint4 pre[NPF][LPT];
-  auto gload = [&](auto slot, int tile) __attribute__((always_inline)) {
-    constexpr int S = decltype(slot)::value;
+  // K tile staging.  Piece v of a tile (16 bytes) sits at LDS slot v: row
+  // v / VPR, column v % VPR, and holds the row's global column
+  // (v % VPR) ^ (row % VPR), so the 32 rows a fragment read touches spread
+  // over the banks without padding.  A wave's load instruction fills 64
+  // consecutive slots (lane i -> slot base + i).
+  // (a wave either loads all 64 of its pieces in a round or none of them)
+  static_assert(TILE_VECS % WAVE == 0 && (TILE_VECS % NT == 0 || TILE_VECS < NT), "load rounds");
+  auto gload_lds = [&](int buf, int tile) __attribute__((always_inline)) {
     const int tt0 = t0 + tile * TOK;
     const int rows = min(TOK, t1 - tt0);
     const char* base = kh + (size_t)tt0 * ROWB;
-    if (rows == TOK) {   // full tile: fixed per-thread offsets
-#pragma unroll
-      for (int i = 0; i < LPT; ++i) {
-        const int v = tid + i * NT;
-        if (v < TILE_VECS) pre[S][i] = ld16(base + (size_t)v * 16);
-      }
-    } else {
-      // rows past the chunk end re-read its last row: their tokens are
-      // masked (pass 1) or never written (pass 2), so no select is needed
-#pragma unroll
-      for (int i = 0; i < LPT; ++i) {
-        const int v = tid + i * NT;
-        if (v < TILE_VECS) {
-          const int row = min(v / VPR, rows - 1);
-          pre[S][i] = ld16(base + ((size_t)row * VPR + v % VPR) * 16);
-        }
-      }
-    }
-  };
-  auto sstore = [&](auto slot, auto bufc) __attribute__((always_inline)) {
-    constexpr int S = decltype(slot)::value;
-    constexpr int buf = decltype(bufc)::value;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int v = tid + i * NT;
-      if (v < TILE_VECS) {
-        const int row = v / VPR, col = v % VPR;
-        *reinterpret_cast<uint4*>(&ktile[buf][row * LDS_STRIDE + col * 16]) = pre[S][i];
-      }
+      if (v >= TILE_VECS) break;   // uniform over the wave
+      // rows past the chunk end re-read its last row: their tokens are
+      // masked (pass 1) or never written (pass 2)
+      const int row = min(v / VPR, rows - 1);
+      const int col = (v % VPR) ^ ((v / VPR) & (VPR - 1));
+      const int slot0 = __builtin_amdgcn_readfirstlane(v - lane);   // the wave's first slot
+      lds_dma16(base + ((size_t)row * VPR + col) * 16, &ktile[buf][slot0 * 16]);
+    }
+  };
+  // Wait for this thread's pieces of tile t; the NB - 2 tiles requested
+  // after it (fewer near the end) may stay in flight.
+  auto wait_tile = [&](int tile) __attribute__((always_inline)) {
+    static_assert(NB == 2 || NB == 4, "buffers");
+    if constexpr (NB == 4) {
+      const int later = min(NB - 2, ntiles - 1 - tile);
+      if (later >= 2) vm_wait<2 * LPT>();
+      else if (later == 1) vm_wait<LPT>();
+      else vm_wait<0>();
+    } else {
+      vm_wait<0>();
     }
   };
 
@@ -237,11 +279,14 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
   // per-epilogue scratch (pass 1)
   float e_nm = 0.f, e_sum = 0.f, e_mn = 0.f;
 
-  auto load_k = [&](auto bufc, int sub) __attribute__((always_inline)) {
-    constexpr int buf = decltype(bufc)::value;
-    const unsigned char* krow = &ktile[buf][(sub * 32 + l32) * LDS_STRIDE + 8 * hf * sizeof(T)];
+  auto load_k = [&](int buf, int sub) __attribute__((always_inline)) {
+    const int r = sub * 32 + l32, sw = r & (VPR - 1);
+    const unsigned char* krow = &ktile[buf][r * ROWB];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[ks] = load_frag<T>(krow + ks * 16 * sizeof(T));
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = (8 * hf + 16 * ks) * (int)sizeof(T) / 16;   // first 16-byte piece
+      kf[ks] = load_frag_sw<T>(krow, c, sw);
+    }
   };
   auto mma_step = [&](int i, int q) __attribute__((always_inline)) {
     // q-th of 8 MFMA slots of row block i: k-steps [q*KS/8, (q+1)*KS/8)
@@ -354,56 +399,43 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
   };
   auto masked_tile = [&](int tile) { return tile >= clean_tiles; };
 
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1 % NPF>;
-  gload(S0{}, 0);
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  sstore(S0{}, B0{});
-  __syncthreads();
-  // tiles 1..NPF in flight (tile j in slot j % NPF)
-  if (ntiles > 1) gload(S1{}, 1);
-  if (ntiles > 2) gload(S0{}, 2);
+  // Tiles 0 .. NB-2 requested up front; at tile t (after its barrier, which
+  // also tells that every wave is done with tile t-1) tile t + NB - 1 goes
+  // into the buffer tile t-1 used.
+  for (int p = 0; p < NB - 1; ++p)
+    if (p < ntiles) gload_lds(p, p);
   // tile 0
-  load_k(B0{}, 0);
+  wait_tile(0);
+  __syncthreads();
+  if (NB - 1 < ntiles) gload_lds(NB - 1, NB - 1);
+  load_k(0, 0);
   step_m(T_{}, I0{}, F_{}, I1{}, 0, false);                     // MMA(0, r0)
   step_m(T_{}, I1{}, T_{}, I0{}, t0, masked_tile(0));           // MMA(0, r1) | epi(0, r0)
-  load_k(B0{}, 1);
+  load_k(0, 1);
   step_m(T_{}, I0{}, T_{}, I1{}, t0, masked_tile(0));           // MMA(1, r0) | epi(0, r1)
   emit_col(0, 0);
   step_m(T_{}, I1{}, T_{}, I0{}, t0 + 32, masked_tile(0));      // MMA(1, r1) | epi(1, r0)
-  if (ntiles > 1) sstore(S1{}, B1{});
-  __syncthreads();
-  // Tile t: load tile t+NPF into t's (now free) slot, run the tile, store tile
-  // t+1 (slot (t+1) % NPF) to the other LDS buffer.
-  // (bc: this tile's LDS buffer, tile & 1, fixed per call site since NPF is even)
-  auto tile_body = [&](auto ls, auto ss, auto bc, int tile) __attribute__((always_inline)) {
-    constexpr int buf = decltype(bc)::value;
-    using BN = std::integral_constant<int, 1 - buf>;
-    const int tt0 = t0 + tile * TOK;
-    if (tile + NPF < ntiles) gload(ls, tile + NPF);
-    load_k(bc, 0);
+  for (int tile = 1; tile < ntiles; ++tile) {
+    const int tt0 = t0 + tile * TOK, buf = tile % NB;
+    wait_tile(tile);
+    __syncthreads();
+    if (tile >= 2) reduce_tile(tile - 2);
+    if (tile + NB - 1 < ntiles) gload_lds((tile + NB - 1) % NB, tile + NB - 1);
+    load_k(buf, 0);
     step_m(T_{}, I0{}, T_{}, I1{}, tt0 - 32, masked_tile(tile - 1));  // MMA(2t, r0) | epi(2t-1, r1)
     emit_col(tile - 1, 1);
     step_m(T_{}, I1{}, T_{}, I0{}, tt0, masked_tile(tile));           // MMA(2t, r1) | epi(2t, r0)
-    load_k(bc, 1);
+    load_k(buf, 1);
     step_m(T_{}, I0{}, T_{}, I1{}, tt0, masked_tile(tile));           // MMA(2t+1, r0) | epi(2t, r1)
     emit_col(tile, 0);
     step_m(T_{}, I1{}, T_{}, I0{}, tt0 + 32, masked_tile(tile));      // MMA(2t+1, r1) | epi(2t+1, r0)
-    if (tile + 1 < ntiles) sstore(ss, BN{});
-    __syncthreads();
-    reduce_tile(tile - 1);
-  };
-  static_assert(NPF == 2, "the unrolled tile loop assumes two slots (and LDS buffer = tile parity)");
-  for (int tile = 1; tile < ntiles; tile += 2) {
-    tile_body(S1{}, S0{}, B1{}, tile);
-    if (tile + 1 < ntiles) tile_body(S0{}, S1{}, B0{}, tile + 1);
   }
   // drain: the last block's second row block
   step_m(F_{}, I0{}, T_{}, I1{}, t0 + (ntiles - 1) * TOK + 32, masked_tile(ntiles - 1));
   emit_col(ntiles - 1, 1);
   if (PASS == 2) {
     __syncthreads();
+    if (ntiles >= 2) reduce_tile(ntiles - 2);
     reduce_tile(ntiles - 1);
   }
 

@@ -110,6 +110,20 @@ __device__ __forceinline__ void lds_dma16(const void* g, unsigned char* lds) {
   (void)saved;
 }
 
+// As lds_dma16, from a wave-uniform base (SGPRs) plus a 32-bit per-lane
+// byte offset: no per-load address arithmetic on the VALU.
+__device__ __forceinline__ void lds_dma16_sv(const void* base, uint32_t off, unsigned char* lds) {
+  const uint32_t l = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(l)
+      : "memory");
+  (void)saved;
+}
+
 // s_waitcnt on the vector-memory counter only (at most N outstanding).
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -235,20 +249,36 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
   // consecutive slots (lane i -> slot base + i).
   // (a wave either loads all 64 of its pieces in a round or none of them)
   static_assert(TILE_VECS % WAVE == 0 && (TILE_VECS % NT == 0 || TILE_VECS < NT), "load rounds");
+  // A whole tile's loads take the byte offsets computed here once, from the
+  // tile's base address in SGPRs; a partial (last) tile clamps its rows.
+  uint32_t poff[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int v = tid + i * NT;
+    poff[i] = (uint32_t)(((v / VPR) * VPR + ((v % VPR) ^ ((v / VPR) & (VPR - 1)))) * 16);
+  }
+  const int wslot = __builtin_amdgcn_readfirstlane(tid - lane);   // the wave's first slot
   auto gload_lds = [&](int buf, int tile) __attribute__((always_inline)) {
     const int tt0 = t0 + tile * TOK;
     const int rows = min(TOK, t1 - tt0);
     const char* base = kh + (size_t)tt0 * ROWB;
+    if (rows == TOK) {
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int v = tid + i * NT;
-      if (v >= TILE_VECS) break;   // uniform over the wave
-      // rows past the chunk end re-read its last row: their tokens are
-      // masked (pass 1) or never written (pass 2)
-      const int row = min(v / VPR, rows - 1);
-      const int col = (v % VPR) ^ ((v / VPR) & (VPR - 1));
-      const int slot0 = __builtin_amdgcn_readfirstlane(v - lane);   // the wave's first slot
-      lds_dma16(base + ((size_t)row * VPR + col) * 16, &ktile[buf][slot0 * 16]);
+      for (int i = 0; i < LPT; ++i) {
+        if (tid + i * NT >= TILE_VECS) break;   // uniform over the wave
+        lds_dma16_sv(base, poff[i], &ktile[buf][(wslot + i * NT) * 16]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int v = tid + i * NT;
+        if (v >= TILE_VECS) break;   // uniform over the wave
+        // rows past the chunk end re-read its last row: their tokens are
+        // masked (pass 1) or never written (pass 2)
+        const int row = min(v / VPR, rows - 1);
+        const int col = (v % VPR) ^ ((v / VPR) & (VPR - 1));
+        lds_dma16(base + ((size_t)row * VPR + col) * 16, &ktile[buf][(wslot + i * NT) * 16]);
+      }
     }
   };
   // Wait for this thread's pieces of tile t; the NB - 2 tiles requested

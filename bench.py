@@ -110,6 +110,21 @@ class Pipeline:
                            workspace=self.ws_d)
 
 
+def settle_clocks(pipe: Pipeline, seconds: float = 0.1) -> int:
+    """Run the step untimed for about `seconds` of wall time.  From a cold
+    start the GPU needs a few tens of ms of sustained load before its clocks
+    settle (the first steps run up to 20% slower), so the warmup steps alone
+    would leave the timed region on the ramp.  Returns the steps run."""
+    n = 0
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            pipe.step()
+        n += 10
+        torch.cuda.synchronize()
+    return n
+
+
 def timed_steps(pipe: Pipeline, steps: int, only=None):
     """Wall-clock ms per step and the event timings of the same steps: every
     kernel, or (only=name) one kernel, so that the timed region carries two
@@ -303,14 +318,14 @@ def main():
     log("bench: device copy bandwidth")
     copy_bw = copy_gbps()
     log(f"bench: {torch.cuda.get_device_name(0)}; copy {copy_bw:.0f} GB/s; warmup {args.warmup}")
-    for _ in range(args.warmup):
-        pipe.step()
-    torch.cuda.synchronize()
+    settle = settle_clocks(pipe)
+    log(f"bench: {settle} untimed steps while the clocks settle")
 
-    # Per-kernel breakdown (all kernels bracketed), then the timed region with
-    # events around the roofline kernel only.
-    _, kt = timed_steps(pipe, args.steps)
-    log("bench: per-kernel mean ms " + ", ".join(f"{k}={v[0]:.4f}" for k, v in kt.items()))
+    # Per-kernel breakdown (every launch timed), then the timed region with
+    # events on the roofline kernel only.
+    ms_all, kt = timed_steps(pipe, args.steps)
+    log(f"bench: {ms_all:.4f} ms per step with every launch timed; per-kernel mean ms "
+        + ", ".join(f"{k}={v[0]:.4f}" for k, v in kt.items()))
 
     B, Hkv, N, D = lay.k.shape
     G, W = cfg.G, cfg.W
@@ -328,7 +343,13 @@ def main():
             "select": ("hbm", bytes_sel), "compact": ("hbm", bytes_comp),
             "decode_split": ("hbm", bytes_dec)}
     dom = max(work, key=lambda k: kt.get(k, (0.0,))[0])
-    log(f"bench: timing {args.steps} steps (events around {dom})")
+    # the host work since the last step leaves the GPU idle long enough for
+    # its clocks to drop: settle them again, right before the warmup steps
+    settle_clocks(pipe)
+    for _ in range(args.warmup):
+        pipe.step()
+    torch.cuda.synchronize()
+    log(f"bench: {args.warmup} warmup steps, timing {args.steps} steps (events on {dom})")
     ms, kt_dom = timed_steps(pipe, args.steps, only=dom)
     bound, amount = work[dom]
     t_dom = kt_dom[dom][0] * 1e-3

@@ -1,6 +1,7 @@
 // Shared device/host helpers for the kvcc HIP library (gfx950, wave64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,20 +34,27 @@ inline float default_scale(float scale, int d) {
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Brackets one kernel launch with hipEvents on its stream while timing is
-// enabled (kv_timing_enable); a no-op otherwise.
-class TimedLaunch {
- public:
-  TimedLaunch(const char* name, hipStream_t st);
-  ~TimedLaunch();
-  TimedLaunch(const TimedLaunch&) = delete;
-  TimedLaunch& operator=(const TimedLaunch&) = delete;
+// Per-kernel timing (kv_timing_enable): while it is on for `name`,
+// timing_events hands out a start/stop event pair for one launch, and
+// timing_done files the pair under `name`.
+bool timing_events(const char* name, hipEvent_t* start, hipEvent_t* stop);
+void timing_done(const char* name, hipEvent_t start, hipEvent_t stop);
 
- private:
-  const char* name_;
-  hipStream_t st_;
-  hipEvent_t start_ = nullptr, stop_ = nullptr;
-};
+// kernel<<<grid, block, shmem, st>>>(args...).  While timing is on for
+// `name`, the launch carries an event pair that the dispatch itself stamps at
+// kernel start and end (hipExtLaunchKernelGGL), so timing adds no packets of
+// its own to the stream.
+template <typename K, typename... A>
+inline void launch(const char* name, K kernel, dim3 grid, dim3 block, uint32_t shmem,
+                   hipStream_t st, A... args) {
+  hipEvent_t e0, e1;
+  if (timing_events(name, &e0, &e1)) {
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, e0, e1, 0, args...);
+    timing_done(name, e0, e1);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, st, args...);
+  }
+}
 
 // Device-side helpers ------------------------------------------------------
 

@@ -146,7 +146,6 @@ extern "C" int kv_compact(const void* k, const void* v, int B, int Hkv, int N_ma
   grid = std::max<int64_t>(1, std::min<int64_t>(grid, 2048));
   const size_t dyn = ((size_t)B * Hkv + 1) * sizeof(long long);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  TimedLaunch t("compact", st);
-  compact_kernel<<<(unsigned)grid, CT, dyn, st>>>(a);
+  launch("compact", compact_kernel, dim3((unsigned)grid), dim3(CT), (uint32_t)dyn, st, a);
   return launch_status();
 }

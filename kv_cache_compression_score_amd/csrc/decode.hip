@@ -636,16 +636,12 @@ void launch_decode(const DecodeArgs& a, hipStream_t st) {
   const size_t dyn = (size_t)(a.B * a.Hkv + 1) * (sizeof(long long) + sizeof(int));
   const dim3 grid((unsigned)std::min(a.items_max, 8192), a.n_sub);
   if constexpr (VEC) {
-    TimedLaunch t("vector_decode_split", st);
-    vector_decode_split<T, D, GT><<<grid, DT, dyn, st>>>(a);
+    launch("vector_decode_split", vector_decode_split<T, D, GT>, grid, dim3(DT), (uint32_t)dyn, st, a);
   } else {
-    TimedLaunch t("decode_split", st);
-    decode_split<T, D, GT><<<grid, DT, dyn, st>>>(a);
+    launch("decode_split", decode_split<T, D, GT>, grid, dim3(DT), (uint32_t)dyn, st, a);
   }
-  {
-    TimedLaunch t(VEC ? "vector_decode_merge" : "decode_merge", st);
-    decode_merge<D, GT, VEC><<<dim3(a.B * a.Hkv, a.n_sub), GT * D, 0, st>>>(a);
-  }
+  launch(VEC ? "vector_decode_merge" : "decode_merge", decode_merge<D, GT, VEC>,
+         dim3(a.B * a.Hkv, a.n_sub), dim3(GT * D), 0, st, a);
 }
 
 template <typename T, int D, bool VEC>

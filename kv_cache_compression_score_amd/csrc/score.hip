@@ -590,24 +590,15 @@ void launch_score(ScoreArgs a, hipStream_t st) {
   a.TC2 = chunk_tokens((int64_t)a.B * a.Hkv, a.N_max,
                        resident_slots(score_pass<T, D, NW, 2>, NW * WAVE, &slots2), 4);
   a.n_chunks2 = ceil_div(a.N_max, a.TC2);
+  const dim3 grid1(a.n_chunks, a.Hkv, a.B), grid2(a.n_chunks2, a.Hkv, a.B);
   if (a.lse_in) {   // row LSEs given: the column-sum pass alone
-    TimedLaunch t("score_colsum", st);
-    score_pass<T, D, NW, 2><<<dim3(a.n_chunks2, a.Hkv, a.B), NW * WAVE, 0, st>>>(a);
+    launch("score_colsum", score_pass<T, D, NW, 2>, grid2, dim3(NW * WAVE), 0, st, a);
     return;
   }
-  {
-    TimedLaunch t("score_rowstats", st);
-    score_pass<T, D, NW, 1><<<dim3(a.n_chunks, a.Hkv, a.B), NW * WAVE, 0, st>>>(a);
-  }
-  {
-    TimedLaunch t("score_fold", st);
-    const int rows = a.B * a.Hkv * a.R_pad;
-    score_fold<<<ceil_div(rows, 4), 256, 0, st>>>(a);
-  }
-  {
-    TimedLaunch t("score_colsum", st);
-    score_pass<T, D, NW, 2><<<dim3(a.n_chunks2, a.Hkv, a.B), NW * WAVE, 0, st>>>(a);
-  }
+  launch("score_rowstats", score_pass<T, D, NW, 1>, grid1, dim3(NW * WAVE), 0, st, a);
+  const int rows = a.B * a.Hkv * a.R_pad;
+  launch("score_fold", score_fold, dim3(ceil_div(rows, 4)), dim3(256), 0, st, a);
+  launch("score_colsum", score_pass<T, D, NW, 2>, grid2, dim3(NW * WAVE), 0, st, a);
 }
 
 template <typename T, int D>

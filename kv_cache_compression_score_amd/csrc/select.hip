@@ -572,9 +572,8 @@ void kvcc::select_launch(const float* scores, const int32_t* ctx, const int32_t*
   a.scores = scores; a.ctx = ctx; a.n_head = n_head; a.B = B; a.Hkv = Hkv; a.N_max = N_max;
   a.k_zero_ok = k_zero_ok ? 1 : 0;
   a.bud = bud; a.kept_idx = kept_idx; a.kept_count = kept_count;
-  TimedLaunch t(timer_name, st);
   if (N_max <= LDS_KEYS)
-    select_kernel<true><<<B * Hkv, NT, 0, st>>>(a);
+    launch(timer_name, select_kernel<true>, dim3(B * Hkv), dim3(NT), 0, st, a);
   else
-    select_kernel<false><<<B * Hkv, NT, 0, st>>>(a);
+    launch(timer_name, select_kernel<false>, dim3(B * Hkv), dim3(NT), 0, st, a);
 }

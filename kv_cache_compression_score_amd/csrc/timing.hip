@@ -1,6 +1,6 @@
 // Opt-in per-kernel timing: when enabled, every kernel the library launches
-// (or only those of one name) is bracketed by hipEvents recorded on the
-// launch's own stream.
+// (or only those of one name) carries a start/stop hipEvent pair that its
+// dispatch stamps (see launch() in common.hpp).
 #include <string.h>
 
 #include <mutex>
@@ -36,19 +36,23 @@ hipEvent_t take_event() {
 
 }  // namespace
 
-TimedLaunch::TimedLaunch(const char* name, hipStream_t st) : name_(name), st_(st) {
+bool timing_events(const char* name, hipEvent_t* start, hipEvent_t* stop) {
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_enabled || (!g_only.empty() && g_only != name)) return;
-  start_ = take_event();
-  stop_ = take_event();
-  if (start_ && stop_) (void)hipEventRecord(start_, st_);
+  if (!g_enabled || (!g_only.empty() && g_only != name)) return false;
+  hipEvent_t a = take_event(), b = take_event();
+  if (!a || !b) {
+    if (a) g_pool.push_back(a);
+    if (b) g_pool.push_back(b);
+    return false;
+  }
+  *start = a;
+  *stop = b;
+  return true;
 }
 
-TimedLaunch::~TimedLaunch() {
-  if (!start_ || !stop_) return;
-  (void)hipEventRecord(stop_, st_);
+void timing_done(const char* name, hipEvent_t start, hipEvent_t stop) {
   std::lock_guard<std::mutex> lk(g_mu);
-  g_records.push_back(Record{name_, start_, stop_});
+  g_records.push_back(Record{name, start, stop});
 }
 
 }  // namespace kvcc

@@ -440,11 +440,8 @@ extern "C" int kv_vector_route(const float* scores, const int32_t* ctx_len, cons
   int32_t* k_pool = static_cast<int32_t*>(workspace);
   int32_t* k_apx = k_pool + (size_t)B * Hkv;
   const int H = B * Hkv;
-  {
-    TimedLaunch t("vector_counts", st);
-    vector_counts_kernel<<<ceil_div(H, 256), 256, 0, st>>>(ctx_len, B, Hkv, N_max, p_c, p_a,
-                                                           k_pool, k_apx);
-  }
+  launch("vector_counts", vector_counts_kernel, dim3(ceil_div(H, 256)), dim3(256), 0, st, ctx_len,
+         B, Hkv, N_max, p_c, p_a, k_pool, k_apx);
   kv_budget pool{};
   pool.mode = KV_BUDGET_K;
   pool.k = k_pool;
@@ -456,15 +453,15 @@ extern "C" int kv_vector_route(const float* scores, const int32_t* ctx_len, cons
   r.pool_idx = pool_idx; r.pool_count = pool_count; r.neg_eps = neg_eps;
   r.B = B; r.Hkv = Hkv; r.N_max = N_max; r.rope_base = rope_base;
   {
-    TimedLaunch t("vector_residual", st);
     // a few workgroups per head (W staged once each), walking 64-entry tiles
     const dim3 grid((unsigned)std::max(1, std::min(ceil_div(N_max, RPW), 8)), Hkv, B);
+    const char* nm = "vector_residual";
     if (dtype == KV_BF16) {
-      if (d == 128) vector_residual_kernel<__bf16, 128><<<grid, VT, 0, st>>>(r);
-      else vector_residual_kernel<__bf16, 64><<<grid, VT, 0, st>>>(r);
+      if (d == 128) launch(nm, vector_residual_kernel<__bf16, 128>, grid, dim3(VT), 0, st, r);
+      else launch(nm, vector_residual_kernel<__bf16, 64>, grid, dim3(VT), 0, st, r);
     } else {
-      if (d == 128) vector_residual_kernel<float, 128><<<grid, VT, 0, st>>>(r);
-      else vector_residual_kernel<float, 64><<<grid, VT, 0, st>>>(r);
+      if (d == 128) launch(nm, vector_residual_kernel<float, 128>, grid, dim3(VT), 0, st, r);
+      else launch(nm, vector_residual_kernel<float, 64>, grid, dim3(VT), 0, st, r);
     }
   }
   kv_budget apx{};
@@ -506,16 +503,12 @@ extern "C" int kv_vector_compact(const void* k, const void* v, int B, int Hkv, i
   const int H = B * Hkv;
   const size_t dyn = (size_t)2 * (H + 1) * sizeof(long long);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  launch("vector_vmap", vector_vmap_kernel, dim3(H), dim3(VT), (uint32_t)dyn, st, a);
   {
-    TimedLaunch t("vector_vmap", st);
-    vector_vmap_kernel<<<H, VT, dyn, st>>>(a);
-  }
-  {
-    TimedLaunch t("vector_copy", st);
     const int rpi = VT / (a.rowb / 16);
     int64_t grid = ceil_div64(std::min<int64_t>(capacity_rows, (int64_t)H * N_max), rpi * 4);
     grid = std::max<int64_t>(1, std::min<int64_t>(grid, 2048));
-    vector_copy_kernel<<<(unsigned)grid, VT, dyn, st>>>(a);
+    launch("vector_copy", vector_copy_kernel, dim3((unsigned)grid), dim3(VT), (uint32_t)dyn, st, a);
   }
   return launch_status();
 }

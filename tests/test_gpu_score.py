@@ -20,6 +20,8 @@ CASES = [
     (1, 32, 8, 64, 2048, 128, torch.bfloat16, False, None),       # Llama head shape
     (1, 64, 4, 32, 700, 128, torch.bfloat16, False, None),        # G*W = 512 rows
     (1, 4, 1, 256, 300, 64, torch.bfloat16, True, None),          # G*W = 1024 rows
+    (1, 4, 2, 40, 40, 64, torch.bfloat16, True, None),            # W = N, one partial tile
+    (2, 4, 1, 8, 130, 128, torch.bfloat16, False, [130, 8]),      # a sequence of only W tokens
 ]
 
 

@@ -295,8 +295,9 @@ int kv_vector_decode(const void* q, const void* k_c, const void* v_c, const int3
  * Measurement hook (not part of the method): per-kernel GPU time.
  *
  * kv_timing_enable(1) clears earlier records and makes every kernel the
- * library launches afterwards be bracketed by two hipEvents recorded on that
- * launch's own stream; kv_timing_enable(0) stops recording.  kv_timing_read
+ * library launches afterwards carry a start/stop hipEvent pair that its
+ * dispatch stamps at kernel start and end, on that launch's own stream;
+ * kv_timing_enable(0) stops recording.  kv_timing_read
  * waits for the recorded events and writes up to max_entries per-kernel
  * totals (host array, caller-owned), returning the number of distinct
  * kernels (or a negative kv_status).  kv_timing_only(name) restricts the
@@ -305,7 +306,8 @@ int kv_vector_decode(const void* q, const void* k_c, const void* v_c, const int3
  * "decode_merge", "vector_counts", "vector_pool", "vector_residual",
  * "vector_apx", "vector_vmap", "vector_copy", "vector_decode_split",
  * "vector_decode_merge"); NULL or "" records every launch.  The name is copied.
- * Timing adds event records between launches, so it is meant for
+ * Timed dispatches run a little slower (about 4 us per timed launch
+ * within a step of back-to-back launches), so timing is meant for
  * measurement runs, not production.
  * ---------------------------------------------------------------------- */
 typedef struct kv_kernel_time {

@@ -341,15 +341,26 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
           for (int e = 0; e < 16; ++e)
             acc[i][e] = (8 * (e >> 2) + (e & 3)) > lim ? -INFINITY : acc[i][e];
         }
-        // three-input maxima (v_max3): 16 values in 8 instructions
-        const float a0 = fmaxf(acc[i][0], fmaxf(acc[i][1], acc[i][2]));
-        const float a1 = fmaxf(acc[i][3], fmaxf(acc[i][4], acc[i][5]));
-        const float a2 = fmaxf(acc[i][6], fmaxf(acc[i][7], acc[i][8]));
-        e_mn = fmaxf(a0, fmaxf(a1, a2));
+        if (MASKED) {
+          // three-input maxima (v_max3): 16 values in 8 instructions
+          const float a0 = fmaxf(acc[i][0], fmaxf(acc[i][1], acc[i][2]));
+          const float a1 = fmaxf(acc[i][3], fmaxf(acc[i][4], acc[i][5]));
+          const float a2 = fmaxf(acc[i][6], fmaxf(acc[i][7], acc[i][8]));
+          e_mn = fmaxf(a0, fmaxf(a1, a2));
+        } else {
+          // The reference m of a running (m, sum of 2^(x - m)) pair need not
+          // be the maximum: any m at or below it gives the same m + log2(sum)
+          // while no term overflows.  Whole tiles take it from three of the
+          // lane's sixteen logits; a block whose sum comes out above 2^64 is
+          // redone from its exact maximum below.
+          e_mn = fmaxf(acc[i][0], fmaxf(acc[i][7], acc[i][13]));
+        }
       } else if (q == 1) {
-        const float a3 = fmaxf(acc[i][9], fmaxf(acc[i][10], acc[i][11]));
-        const float a4 = fmaxf(acc[i][12], fmaxf(acc[i][13], acc[i][14]));
-        e_mn = fmaxf(acc[i][15], fmaxf(a3, fmaxf(a4, e_mn)));
+        if (MASKED) {
+          const float a3 = fmaxf(acc[i][9], fmaxf(acc[i][10], acc[i][11]));
+          const float a4 = fmaxf(acc[i][12], fmaxf(acc[i][13], acc[i][14]));
+          e_mn = fmaxf(acc[i][15], fmaxf(a3, fmaxf(a4, e_mn)));
+        }
         e_mn = fmaxf(m_run[i], e_mn * cc);
         // a fully masked row keeps (-inf, 0): exp2(-inf - 0) = 0 everywhere
         e_nm = MASKED && e_mn == -INFINITY ? 0.f : -e_mn;
@@ -363,6 +374,16 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
           e_sum = e == 0 ? x : e_sum + x;
         }
         if (q == 7) {
+          if (!MASKED && !(e_sum <= 0x1p64f)) {   // a logit far above the sampled ones
+            float mx = acc[i][0];
+#pragma unroll
+            for (int e = 1; e < 16; ++e) mx = fmaxf(mx, acc[i][e]);
+            e_mn = fmaxf(m_run[i], mx * cc);
+            e_nm = -e_mn;
+            e_sum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) e_sum += fast_exp2(fmaf(acc[i][e], cc, e_nm));
+          }
           s_run[i] = fmaf(s_run[i], fast_exp2(m_run[i] + e_nm), e_sum);
           m_run[i] = e_mn;
         }

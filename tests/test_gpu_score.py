@@ -67,6 +67,32 @@ def test_score_zero_queries_uniform():
     np.testing.assert_allclose(s.cpu().numpy(), 64 / 640, rtol=1e-5)
 
 
+@pytest.mark.parametrize("spread", [40.0, 100.0])
+def test_score_far_outlier_logit(spread):
+    # One token whose logit (base 2) sits about `spread` above every other
+    # one, at a position the row-statistics pass does not sample for its
+    # running reference: 40 leaves that reference far below the maximum,
+    # 100 makes the block's sum overflow 2^64 and be redone exactly.
+    d, W, N = 64, 16, 1024
+    lay = wl.random_case(21, B=1, Hq=4, Hkv=1, d=d, N_max=N, W=W)
+    rng = np.random.Generator(np.random.PCG64(22))
+    base = rng.standard_normal(d).astype(np.float32)
+    q = base + 0.1 * rng.standard_normal((1, 4, W, d)).astype(np.float32)
+    u = base / np.linalg.norm(base)
+    c = np.log2(np.e) / np.sqrt(d)
+    t_star = 64 * 5 + 2          # offset 2 of a 32-token block
+    k = lay.k.float().numpy().copy()
+    k[0, 0, t_star] = u * spread / (c * np.linalg.norm(base))
+    q_t = torch.from_numpy(q).to(lay.q_win.dtype)
+    k_t = torch.from_numpy(k).to(lay.k.dtype)
+    s_gpu, lse_gpu = api.kv_score(dev(q_t), dev(k_t), None, with_row_lse=True)
+    torch.cuda.synchronize()
+    s_ref, lse_ref = orc.window_scores(q_t, k_t, None)
+    assert s_ref[0, 0, t_star] > 0.99 * W * 4
+    check_scores(s_gpu.cpu().numpy(), s_ref, [N], W, 4)
+    np.testing.assert_allclose(lse_gpu.cpu().numpy(), lse_ref, atol=1e-3, rtol=0)
+
+
 def test_score_llama8b_layer_full():
     cfg = wl.CONFIGS["llama8b_layer"]
     lay = wl.make_layer(cfg, with_v=False)

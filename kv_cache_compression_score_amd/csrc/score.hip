@@ -17,7 +17,7 @@
 //           per block and keeps a running (max, sum of exp2) per row in
 //           registers; the two half-waves are merged by a lane swizzle and
 //           the chunk partials published.
-//   fold:   one wave per row merges the row's chunk partials (lanes over
+//   fold:   16 lanes per row merge the row's chunk partials (lanes over
 //           chunks, then a fixed butterfly) into a base-2 log-sum-exp.
 //   pass 2: C[row,token] = Q * K^T, so one lane owns one token and 16 rows
 //           per block; exp2(l*c - lse2[row]) is summed in-lane, then over
@@ -513,33 +513,38 @@ __device__ __forceinline__ void merge(float& m, float& s, float pm, float ps) {
   m = mn;
 }
 
-// One wave per row: lanes merge chunks c = lane, lane+64, ... in order, then a
-// fixed butterfly merges the lanes; deterministic for fixed sizes.
+// FOLD_LANES lanes per row (four rows per wave): the lanes merge chunks
+// c = l, l + FOLD_LANES, ... in order, then a fixed butterfly merges the
+// lanes; deterministic for fixed sizes.
+constexpr int FOLD_LANES = 16;
+
 __global__ __launch_bounds__(256) void score_fold(ScoreArgs a) {
-  const int lane = threadIdx.x & (WAVE - 1);
-  const int row_id = blockIdx.x * 4 + threadIdx.x / WAVE;
-  if (row_id >= a.B * a.Hkv * a.R_pad) return;
+  const int l = threadIdx.x & (FOLD_LANES - 1);
+  const int row_id = blockIdx.x * (256 / FOLD_LANES) + threadIdx.x / FOLD_LANES;
+  const bool live = row_id < a.B * a.Hkv * a.R_pad;   // the butterfly needs every lane
   const int head = row_id / a.R_pad, r = row_id % a.R_pad;
-  if (r >= a.R) {
-    if (lane == 0) a.lse2[row_id] = INFINITY;
-    return;
-  }
-  const float2* src = a.part + (size_t)row_id * a.n_chunks;
   float m = -INFINITY, s = 0.f;
-  for (int c = lane; c < a.n_chunks; c += WAVE) {
-    const float2 p = src[c];
-    merge(m, s, p.x, p.y);
+  if (live && r < a.R) {
+    const float2* src = a.part + (size_t)row_id * a.n_chunks;
+    for (int c = l; c < a.n_chunks; c += FOLD_LANES) {
+      const float2 p = src[c];
+      merge(m, s, p.x, p.y);
+    }
   }
 #pragma unroll
-  for (int o = 1; o < WAVE; o <<= 1) {
+  for (int o = 1; o < FOLD_LANES; o <<= 1) {
     const float pm = __shfl_xor(m, o, WAVE), ps = __shfl_xor(s, o, WAVE);
     // both partners compute the same merge in the same operand order
-    const bool lower = (lane & o) == 0;
+    const bool lower = (l & o) == 0;
     float m1 = lower ? m : pm, s1 = lower ? s : ps;
     merge(m1, s1, lower ? pm : m, lower ? ps : s);
     m = m1; s = s1;
   }
-  if (lane != 0) return;
+  if (!live || l != 0) return;
+  if (r >= a.R) {
+    a.lse2[row_id] = INFINITY;
+    return;
+  }
   const bool seen = s > 0.f;
   const float l2v = seen ? m + log2f(s) : INFINITY;
   a.lse2[row_id] = l2v;
@@ -618,7 +623,7 @@ void launch_score(ScoreArgs a, hipStream_t st) {
   }
   launch("score_rowstats", score_pass<T, D, NW, 1>, grid1, dim3(NW * WAVE), 0, st, a);
   const int rows = a.B * a.Hkv * a.R_pad;
-  launch("score_fold", score_fold, dim3(ceil_div(rows, 4)), dim3(256), 0, st, a);
+  launch("score_fold", score_fold, dim3(ceil_div(rows, 256 / FOLD_LANES)), dim3(256), 0, st, a);
   launch("score_colsum", score_pass<T, D, NW, 2>, grid2, dim3(NW * WAVE), 0, st, a);
 }
 

@@ -127,8 +127,9 @@ def settle_clocks(pipe: Pipeline, seconds: float = 0.1) -> int:
 
 def timed_steps(pipe: Pipeline, steps: int, only=None):
     """Wall-clock ms per step and the event timings of the same steps: every
-    kernel, or (only=name) one kernel, so that the timed region carries two
-    event records per step instead of two per launch."""
+    kernel, or (only=name) one kernel, so that only one launch per step is a
+    timed dispatch (the events are stamped by the dispatch itself, which still
+    slows a timed launch by a few us)."""
     L = _lib.lib()
     torch.cuda.synchronize()
     L.kv_timing_only(only.encode() if only else None)

@@ -274,6 +274,26 @@ def measured_traffic(kernel: str, workload: str):
     return None
 
 
+def step_distribution(pipe: Pipeline, steps: int, flush=None) -> dict:
+    """Per-step times (ms) from torch events around each step on the stream the
+    library launches on: median, p10 and p90.  `flush`, if given, runs before
+    every step, outside the timed interval."""
+    st = torch.cuda.current_stream()
+    ev = []
+    for _ in range(steps):
+        if flush is not None:
+            flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        pipe.step()
+        e1.record(st)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = np.sort(np.array([a.elapsed_time(b) for a, b in ev]))
+    return {"median": float(np.median(ms)), "p10": float(np.percentile(ms, 10)),
+            "p90": float(np.percentile(ms, 90)), "steps": steps}
+
+
 def cpu_baseline(lay: wl.Layer, nseq: int):
     """The float64 oracle, as it stands, on the first nseq sequences."""
     from oracle import oracle as orc
@@ -285,22 +305,29 @@ def cpu_baseline(lay: wl.Layer, nseq: int):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
-    t0 = time.perf_counter()
+    t = [time.perf_counter()]
     s, _ = orc.window_scores(lay.q_win[sl], lay.k[sl], ctx)
+    t.append(time.perf_counter())
     if cfg.budget_mode == wl.BUDGET_MASS:
         idx, cnt = orc.select(s, ctx, orc.BUDGET_MASS, mass=cfg.ratio,
                               min_ratio=cfg.min_ratio, max_ratio=cfg.max_ratio)
     else:
         idx, cnt = orc.select(s, ctx, orc.BUDGET_RATIO, ratio=cfg.ratio)
+    t.append(time.perf_counter())
     k_c, v_c, pos, off = orc.compact(lay.k[sl], lay.v[sl], idx, cnt)
+    t.append(time.perf_counter())
     kc = torch.from_numpy(k_c).view(lay.k.dtype) if lay.k.dtype == torch.bfloat16 else k_c
     vc = torch.from_numpy(v_c).view(lay.k.dtype) if lay.k.dtype == torch.bfloat16 else v_c
     orc.decode(lay.q_dec[0][sl], kc, vc, off, cfg.Hkv)
-    dt = time.perf_counter() - t0
+    t.append(time.perf_counter())
+    dt = t[-1] - t[0]
     tokens = int(ctx.sum())
+    stages = dict(zip(("score", "select", "compact", "decode"),
+                      (t[i + 1] - t[i] for i in range(4))))
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"sequences 0..{nseq - 1} of the batch ({tokens} cached tokens, all "
-                      f"{cfg.Hkv} KV heads): float64 score+select+compact+decode, {dt:.2f} s"}
+                      f"{cfg.Hkv} KV heads): float64 score+select+compact+decode, {dt:.2f} s",
+            "stage_s": stages, "fraction_of_batch": nseq / lay.cfg.B}
 
 
 def main():
@@ -360,6 +387,18 @@ def main():
         achieved, peak, unit = amount / t_dom / 1e9, PEAK_HBM_GBPS, "GB/s"
     t_one = one_pass_score_ms(pipe, args.steps) * 1e-3
     vec = vector_measure(pipe, args.steps)
+    # per-step spread, back to back and from cold caches (a 1 GiB buffer
+    # overwritten before every step, outside the timed interval)
+    # Cold: a 1 GiB buffer is read before every step, so that the L2 and the
+    # 256 MB Infinity Cache hold nothing of the step's data, and nothing
+    # dirty.  (Overwriting the buffer instead leaves up to 256 MB of dirty
+    # lines whose write-back lands inside the next step: reported apart.)
+    settle_clocks(pipe)
+    warm = step_distribution(pipe, args.steps)
+    buf = torch.ones(1 << 28, device="cuda", dtype=torch.float32)
+    cold = step_distribution(pipe, args.steps, lambda: buf.sum())
+    cold_w = step_distribution(pipe, args.steps, lambda: buf.fill_(1.0))
+    del buf
     t = {k: v[0] * 1e-3 for k, v in kt.items()}
     t_score = t["score_rowstats"] + t["score_fold"] + t["score_colsum"]
     t_dec = t["decode_split"] + t["decode_merge"]
@@ -398,6 +437,9 @@ def main():
                                   "frac": (bytes_sel + bytes_comp + bytes_dec) / t_scd / 1e9
                                   / PEAK_HBM_GBPS},
         "kernels_ms": {k: v[0] for k, v in kt.items()},
+        "step_ms_warm": warm,
+        "step_ms_cold": cold,
+        "step_ms_after_1gib_write": cold_w,
         "cpu_baseline": None,
     }
     # Quality beside throughput: loss terms of the step's compacted cache
@@ -415,7 +457,11 @@ def main():
     del out_f, lse_f, out_w, lse_w
     if not args.no_cpu_baseline:
         log("bench: oracle baseline on the host")
-        res["cpu_baseline"] = cpu_baseline(lay, min(args.cpu_seqs, B))
+        cb = cpu_baseline(lay, min(args.cpu_seqs, B))
+        gpu_s = {"score": t_score, "select": t["select"], "compact": t["compact"], "decode": t_dec}
+        cb["stage_speedup"] = {k: cb["stage_s"][k] / cb["fraction_of_batch"] / gpu_s[k]
+                               for k in gpu_s}
+        res["cpu_baseline"] = cb
     print(json.dumps(res), flush=True)
 
 

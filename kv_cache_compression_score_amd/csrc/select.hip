@@ -84,11 +84,45 @@ struct Keys {
   const uint32_t* lds;
   const float* g;
   int p_end, r_begin;   // protected: t < p_end or t >= r_begin
+  __device__ __forceinline__ uint32_t of(float x, int t) const {
+    return (t < p_end || t >= r_begin) ? PROTECTED_KEY : to_key(x);
+  }
   __device__ __forceinline__ uint32_t operator()(int t) const {
     if (IN_LDS) return lds[t];
-    return (t < p_end || t >= r_begin) ? PROTECTED_KEY : to_key(g[t]);
+    return of(g[t], t);
+  }
+  // keys of tokens t .. t+3 from their four scores
+  __device__ __forceinline__ uint4 four(const float4& v, int t) const {
+    return make_uint4(of(v.x, t), of(v.y, t + 1), of(v.z, t + 2), of(v.w, t + 3));
   }
 };
+
+// Heads whose keys do not fit in LDS re-read the scores on every sweep: GU
+// 16-byte loads per thread are issued before any is used, so a sweep waits
+// for memory about once per GU * 4 * NT tokens instead of once per NT.
+constexpr int GU = 8;
+
+// Apply f(score, t) to the scores of tokens [0, n) read from global memory.
+template <class F>
+__device__ __forceinline__ void for_scores(const float* g, int n, const F& f) {
+  const int tid = threadIdx.x;
+  const int n4 = (reinterpret_cast<uintptr_t>(g) & 15) == 0 ? n >> 2 : 0;
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  for (int i0 = 0; i0 < n4; i0 += GU * NT) {
+    float4 v[GU];
+#pragma unroll
+    for (int u = 0; u < GU; ++u) {
+      const int i = i0 + tid + u * NT;
+      v[u] = i < n4 ? g4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < GU; ++u) {
+      const int i = i0 + tid + u * NT;
+      if (i < n4) { f(v[u].x, 4 * i); f(v[u].y, 4 * i + 1); f(v[u].z, 4 * i + 2); f(v[u].w, 4 * i + 3); }
+    }
+  }
+  for (int t = 4 * n4 + tid; t < n; t += NT) f(g[t], t);
+}
 
 template <typename I>
 __device__ __forceinline__ I wave_sum_i(I v) {
@@ -118,7 +152,7 @@ __device__ __forceinline__ void for_keys(const Keys<IN_LDS>& key, int n, const F
     }
     for (int t = 4 * n4 + tid; t < n; t += NT) f(key.lds[t]);
   } else {
-    for (int t = tid; t < n; t += NT) f(key(t));
+    for_scores(key.g, n, [&](float x, int t) { f(key.of(x, t)); });
   }
 }
 
@@ -279,7 +313,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     for (int t = 4 * n4 + tid; t < n; t += NT) keys_lds[t] = visit(to_key(src[t]), is_prot(t));
   } else {
     __syncthreads();
-    for (int t = tid; t < n; t += NT) visit(to_key(src[t]), is_prot(t));
+    for_scores(src, n, [&](float x, int t) { visit(to_key(x), is_prot(t)); });
   }
   mn = last_lane(wave_scan_u32(mn, 0xffffffffu, OpMin()));
   mx = last_lane(wave_scan_u32(mx, 0u, OpMax()));
@@ -510,20 +544,38 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     for (uint32_t i = lane; i < nk; i += WAVE)
       if (slot + i < (uint32_t)n) dst[slot + i] = (int32_t)stage[i];
   } else {
-    auto four = [&](int t, uint32_t* kk) __attribute__((always_inline)) {
+    // GU steps of the segment are loaded (16 bytes per lane each) before the
+    // first is counted or written; s0 is a multiple of 256, so a lane's four
+    // tokens start on a 16-byte boundary whenever the head's scores do.
+    const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+    const float4* g4 = reinterpret_cast<const float4*>(src);
+    auto load = [&](int b0, uint32_t (*kk)[4]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) kk[u] = t + u < s1 ? key(t + u) : 0u;
+      for (int u = 0; u < GU; ++u) {
+        const int t = b0 + u * 4 * WAVE + 4 * lane;
+        if (vec && t + 3 < s1) {
+          const uint4 k = key.four(g4[t >> 2], t);
+          kk[u][0] = k.x; kk[u][1] = k.y; kk[u][2] = k.z; kk[u][3] = k.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kk[u][e] = t + e < s1 ? key(t + e) : 0u;
+        }
+      }
     };
-    for (int base = s0; base < s1; base += 4 * WAVE) {
-      uint32_t kk[4];
-      four(base + 4 * lane, kk);
-      count4(base + 4 * lane, kk);
+    for (int b0 = s0; b0 < s1; b0 += GU * 4 * WAVE) {
+      uint32_t kk[GU][4];
+      load(b0, kk);
+#pragma unroll
+      for (int u = 0; u < GU; ++u)
+        if (b0 + u * 4 * WAVE < s1) count4(b0 + u * 4 * WAVE + 4 * lane, kk[u]);
     }
     prefix_of_waves();
-    for (int base = s0; base < s1; base += 4 * WAVE) {
-      uint32_t kk[4];
-      four(base + 4 * lane, kk);
-      write4(base + 4 * lane, kk);
+    for (int b0 = s0; b0 < s1; b0 += GU * 4 * WAVE) {
+      uint32_t kk[GU][4];
+      load(b0, kk);
+#pragma unroll
+      for (int u = 0; u < GU; ++u)
+        if (b0 + u * 4 * WAVE < s1) write4(b0 + u * 4 * WAVE + 4 * lane, kk[u]);
     }
   }
 }

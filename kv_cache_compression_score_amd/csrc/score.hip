@@ -11,12 +11,12 @@
 // Both sweeps over K tile the logit matrix into 32x32 MFMA blocks with the
 // K tile staged once per workgroup in LDS and each wave holding the Q
 // fragments of two 32-row blocks in registers.  K tiles of 64 tokens go from
-// HBM to LDS directly (no registers), three tiles ahead of the MFMAs, into
-// four buffers with XOR-swizzled 16-byte columns:
+// HBM to LDS directly (no registers), NB - 1 tiles ahead of the MFMAs, into NB
+// buffers (four for 16 KB tiles, else two) with XOR-swizzled 16-byte columns:
 //   pass 1: C[token,row] = K * Q^T, so one lane owns one row and 16 tokens
-//           per block and keeps a running (max, sum of exp2) per row in
-//           registers; the two half-waves are merged by a lane swizzle and
-//           the chunk partials published.
+//           per block and keeps a running (m, sum of 2^(x - m)) per row in
+//           registers, m at or below the row maximum; the two half-waves are
+//           merged by a lane swizzle and the chunk partials published.
 //   fold:   16 lanes per row merge the row's chunk partials (lanes over
 //           chunks, then a fixed butterfly) into a base-2 log-sum-exp.
 //   pass 2: C[row,token] = Q * K^T, so one lane owns one token and 16 rows
@@ -24,8 +24,9 @@
 //           half-waves and waves through LDS in a fixed order.
 // All logits are kept in base-2 units: c = scale*log2(e) is applied to the
 // fp32 dot product after the MFMA (bf16 inputs are never rescaled).  The
-// per-logit epilogue is kept to one FMA, one exp2 and one add (plus a max in
-// pass 1); masks only exist in tail tiles.
+// per-logit epilogue is kept to one FMA, one exp2 and one add (plus, in pass
+// 1, a maximum over three of each lane's sixteen logits per block); masks only
+// exist in tail tiles.
 #include <math.h>
 #include <stdint.h>
 

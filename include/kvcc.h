@@ -169,8 +169,11 @@ int kv_score_from_lse(const void* q_win, const void* k, const int32_t* ctx_len,
  *            of each head are its kept token indices in ascending order; the
  *            rest are not written
  * kept_count [B*Hkv] int32 out
- * workspace  kv_select_workspace_size() bytes (may be 0 bytes / NULL when
- *            that size is 0)
+ * workspace  kv_select_workspace_size() bytes: 0 (NULL allowed) for
+ *            N_max <= 32768.  Above, heads under a count budget (k, ratio,
+ *            threshold) are split over several workgroups that exchange radix
+ *            histograms through it; given less, every head takes one
+ *            workgroup (same result, slower).
  * ---------------------------------------------------------------------- */
 size_t kv_select_workspace_size(int B, int Hkv, int N_max);
 int kv_select(const float* scores, const int32_t* ctx_len,

@@ -156,6 +156,60 @@ __device__ __forceinline__ void for_keys(const Keys<IN_LDS>& key, int n, const F
   }
 }
 
+// One digit of a radix descent: sm.hist (and, with MASS, sm.hmass) hold the
+// digit's nb bins (nb even, at most 2 * NT).  Finds the bin at which the
+// top-down total (counts, or masses with MASS) reaches rem (1 <= rem <= the
+// total) and leaves it in sm.bin, with the count and mass of the bins above
+// it (sm.cnt_above, sm.mass_above) and its own count (sm.bin_cnt).  Clears
+// the bins.  Thread t owns descending positions 2t and 2t+1 (bins nb-1-2t,
+// nb-2-2t): it reads and clears them; a DPP wave scan and the wave totals
+// locate the bin.  All threads must call it.
+template <bool MASS>
+__device__ void resolve_digit(Smem& sm, int nb, unsigned long long rem) {
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int p0 = 2 * tid;
+  uint32_t c0 = 0, c1 = 0;
+  unsigned long long m0 = 0, m1 = 0;
+  if (p0 < nb) {
+    const int b0 = nb - 1 - p0, b1 = b0 - 1;
+    c0 = sm.hist[b0]; c1 = sm.hist[b1];
+    sm.hist[b0] = 0; sm.hist[b1] = 0;
+    if (MASS) {
+      m0 = sm.hmass[b0]; m1 = sm.hmass[b1];
+      sm.hmass[b0] = 0; sm.hmass[b1] = 0;
+    }
+  }
+  if (!MASS) { m0 = c0; m1 = c1; }
+  const unsigned long long own = m0 + m1;
+  const uint32_t own_c = c0 + c1;
+  unsigned long long incl;
+  uint32_t incl_c;
+  if (MASS) {
+    incl = wave_scan_add_u64(own);
+    incl_c = wave_scan_u32(own_c, 0u, OpAdd());
+  } else {
+    incl_c = wave_scan_u32(own_c, 0u, OpAdd());
+    incl = incl_c;
+  }
+  if (lane == WAVE - 1) { sm.f_m[wave] = incl; sm.f_c[wave] = incl_c; }
+  __syncthreads();
+  unsigned long long wb = 0;
+  uint32_t wbc = 0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    if (w < wave) { wb += sm.f_m[w]; wbc += sm.f_c[w]; }
+  }
+  const unsigned long long before = wb + incl - own;
+  if (before < rem && rem <= before + own) {   // exactly one thread
+    const bool first = before + m0 >= rem;      // then m0 > 0
+    sm.bin = (uint32_t)(first ? nb - 1 - p0 : nb - 2 - p0);
+    sm.cnt_above = wbc + incl_c - own_c + (first ? 0u : c0);
+    sm.mass_above = first ? before : before + m0;
+    sm.bin_cnt = first ? c0 : c1;
+  }
+  __syncthreads();
+}
+
 // Radix descent.  Without MASS: the k-th key T (rem = k, 1 <= k <= n) and,
 // in *rem_out, the quota of keys equal to T that are kept.  With MASS: the
 // key T at which the top-down fixed-point mass reaches rem, the count of
@@ -168,7 +222,6 @@ __device__ uint32_t descend(const Keys<IN_LDS>& key, int n, int cp, uint32_t lo_
                             unsigned long long rem, Smem& sm, const FX& fx,
                             uint32_t* cnt_above_out, unsigned long long* rem_out,
                             bool top_ready = false, uint32_t* eq_out = nullptr) {
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   if (top_ready) cp = 0;   // sm.hist already holds the top DIGIT bits of every key
   uint32_t pmask = cp <= 0 ? 0u : (cp >= 32 ? ~0u : ~0u << (32 - cp));
   uint32_t prefix = lo_key & pmask, cnt_above = 0;
@@ -191,49 +244,7 @@ __device__ uint32_t descend(const Keys<IN_LDS>& key, int n, int cp, uint32_t lo_
     }
     ready = false;
     __syncthreads();
-    // Thread t owns descending positions 2t and 2t+1 (bins nb-1-2t, nb-2-2t):
-    // it reads them, clears them for the next digit, and scans.
-    const int p0 = 2 * tid;
-    uint32_t c0 = 0, c1 = 0;
-    unsigned long long m0 = 0, m1 = 0;
-    if (p0 < nb) {
-      const int b0 = nb - 1 - p0, b1 = b0 - 1;   // nb is even
-      c0 = sm.hist[b0]; c1 = sm.hist[b1];
-      sm.hist[b0] = 0; sm.hist[b1] = 0;
-      if (MASS) {
-        m0 = sm.hmass[b0]; m1 = sm.hmass[b1];
-        sm.hmass[b0] = 0; sm.hmass[b1] = 0;
-      }
-    }
-    if (!MASS) { m0 = c0; m1 = c1; }
-    const unsigned long long own = m0 + m1;
-    const uint32_t own_c = c0 + c1;
-    unsigned long long incl;
-    uint32_t incl_c;
-    if (MASS) {
-      incl = wave_scan_add_u64(own);
-      incl_c = wave_scan_u32(own_c, 0u, OpAdd());
-    } else {
-      incl_c = wave_scan_u32(own_c, 0u, OpAdd());
-      incl = incl_c;
-    }
-    if (lane == WAVE - 1) { sm.f_m[wave] = incl; sm.f_c[wave] = incl_c; }
-    __syncthreads();
-    unsigned long long wb = 0;
-    uint32_t wbc = 0;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) {
-      if (w < wave) { wb += sm.f_m[w]; wbc += sm.f_c[w]; }
-    }
-    const unsigned long long before = wb + incl - own;
-    if (before < rem && rem <= before + own) {   // exactly one thread
-      const bool first = before + m0 >= rem;      // then m0 > 0
-      sm.bin = (uint32_t)(first ? nb - 1 - p0 : nb - 2 - p0);
-      sm.cnt_above = wbc + incl_c - own_c + (first ? 0u : c0);
-      sm.mass_above = first ? before : before + m0;
-      sm.bin_cnt = first ? c0 : c1;
-    }
-    __syncthreads();
+    resolve_digit<MASS>(sm, nb, rem);
     rem -= MASS ? sm.mass_above : (unsigned long long)sm.cnt_above;
     cnt_above += sm.cnt_above;
     pref_cnt = sm.bin_cnt;
@@ -245,6 +256,35 @@ __device__ uint32_t descend(const Keys<IN_LDS>& key, int n, int cp, uint32_t lo_
   *rem_out = rem;
   if (eq_out) *eq_out = cp >= 32 ? (uint32_t)n : pref_cnt;   // keys equal to the result
   return prefix;
+}
+
+// The clamp range [lo, hi] of the threshold and mass budgets for a head of
+// n >= 1 tokens.
+__device__ __forceinline__ void budget_clamps(const kv_budget& bu, int n, int* lo, int* hi) {
+  const double nd = (double)n;
+  int l = (int)floor((double)bu.min_ratio * nd + 0.5);
+  int h = (int)floor((double)bu.max_ratio * nd + 0.5);
+  l = max(l, 1);
+  h = min(max(h, 1), n);
+  *lo = min(l, h);
+  *hi = h;
+}
+
+// k of the count budgets (explicit k, kept fraction, threshold with cnt
+// scores at or above tau), before the protected tokens raise it.
+__device__ __forceinline__ int count_budget(const kv_budget& bu, int head, int n, uint32_t cnt,
+                                            int lo, int hi) {
+  if (bu.mode == KV_BUDGET_K) {
+    const int k = bu.k ? bu.k[head] : bu.k_scalar;
+    return min(max(k, 1), n);
+  }
+  if (bu.mode == KV_BUDGET_RATIO) {
+    const float r = bu.ratio ? bu.ratio[head] : bu.ratio_scalar;
+    const double nd = (double)n;
+    const double x = floor((double)r * nd + 0.5);
+    return x >= 1.0 ? (x >= nd ? n : (int)x) : 1;
+  }
+  return min(max((int)cnt, lo), hi);   // threshold
 }
 
 template <bool IN_LDS>
@@ -332,22 +372,11 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   Keys<IN_LDS> key{keys_lds, src, p_end, r_begin};
 
   // Budget -> k.
-  const double nd = (double)n;
-  int lo = (int)floor((double)bu.min_ratio * nd + 0.5);
-  int hi = (int)floor((double)bu.max_ratio * nd + 0.5);
-  lo = max(lo, 1);
-  hi = min(max(hi, 1), n);
-  lo = min(lo, hi);
+  int lo, hi;
+  budget_clamps(bu, n, &lo, &hi);
   int k = 1;
-  if (bu.mode == KV_BUDGET_K) {
-    k = bu.k ? bu.k[head] : bu.k_scalar;
-    k = min(max(k, 1), n);
-  } else if (bu.mode == KV_BUDGET_RATIO) {
-    const float r = bu.ratio ? bu.ratio[head] : bu.ratio_scalar;
-    const double x = floor((double)r * nd + 0.5);
-    k = x >= 1.0 ? (x >= nd ? n : (int)x) : 1;
-  } else if (bu.mode == KV_BUDGET_THRESHOLD) {
-    k = min(max((int)cnt, lo), hi);
+  if (bu.mode != KV_BUDGET_MASS) {
+    k = count_budget(bu, head, n, cnt, lo, hi);
   } else if (tot > 0.0) {
     // mass: fixed point with 2^(61 - floor(log2 total)) so every sum < 2^62
     const double scale = ldexp(1.0, 61 - ilogb(tot));
@@ -580,24 +609,298 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Heads longer than LDS_KEYS tokens under a count budget.  One workgroup per
+// head would leave most CUs idle and re-read the head on every sweep, so the
+// head is cut into parts of PT tokens, one workgroup each, and the descent
+// runs as five launches over the (part, head) grid with fixed digits of 11,
+// 11 and 10 key bits:
+//   0: each part histograms the top digit of its keys and counts keys >= tau;
+//   1, 2: every workgroup of a head sums the parts' histograms of the last
+//         digit, resolves it exactly as resolve_digit does for one workgroup
+//         (so all of them agree), and histograms the next digit of its part;
+//   3: the last digit gives T and the number of keys equal to T to keep;
+//         each part counts its keys above T and equal to T;
+//   4: each part writes its kept indices at the offset the earlier parts
+//      leave, ties going to the earliest tokens.
+// Part 0 of a head publishes the resolved state of each launch.
+constexpr int PT = 16384;             // tokens per part
+constexpr int PQ = PT / (4 * NT);     // float4 loads per thread (4)
+
+struct PartState {
+  int k;
+  uint32_t prefix;   // resolved key bits
+  uint32_t rem;      // keys still to take among those matching prefix
+  uint32_t pad;
+};
+
+struct PartArgs {
+  SelectArgs s;
+  int P;                 // parts per head
+  uint32_t* hist;        // [H][3][P][NBINS]
+  uint32_t* pstat;       // [H][P][4]: count >= tau, count > T, count == T
+  PartState* state;      // [H][4]: after launches 0..3
+};
+
+size_t part_workspace(int H, int P) {
+  const size_t hist = (size_t)H * 3 * P * NBINS * sizeof(uint32_t);
+  const size_t pstat = (size_t)H * P * 4 * sizeof(uint32_t);
+  const size_t state = (size_t)H * 4 * sizeof(PartState);
+  return hist + pstat + state;
+}
+
+// Sum over the block of one value per thread (every thread gets it).
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, Smem& sm) {
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  v = last_lane(wave_scan_u32(v, 0u, OpAdd()));
+  if (lane == 0) sm.f_c[wave] = v;
+  __syncthreads();
+  uint32_t t = 0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) t += sm.f_c[w];
+  __syncthreads();
+  return t;
+}
+
+template <int PHASE>
+__global__ __launch_bounds__(NT) void select_part_kernel(PartArgs pa) {
+  __shared__ Smem sm;
+  const SelectArgs& a = pa.s;
+  const int part = blockIdx.x, head = blockIdx.y, b = head / a.Hkv;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int n = a.ctx ? min(max(a.ctx[b], 0), a.N_max) : a.N_max;
+  if (n == 0) {
+    if (PHASE == 4 && part == 0 && tid == 0) a.kept_count[head] = 0;
+    return;
+  }
+  const kv_budget& bu = a.bud;
+  const int p_end = min(max(bu.n_sink, 0), n);
+  const int r_begin = n - min(max(bu.n_recent, 0), n);
+  const int n_prot = min(n, p_end + (n - r_begin));
+  const int P = pa.P;
+  uint32_t* hist_h = pa.hist + (size_t)head * 3 * P * NBINS;
+  uint32_t* pstat_h = pa.pstat + (size_t)head * P * 4;
+  PartState* st_h = pa.state + (size_t)head * 4;
+
+  // This thread's keys: tokens t0 + 4 (tid + u NT) + e, valid below t1.
+  const int t0 = part * PT, t1 = min(t0 + PT, n);
+  const float* src = a.scores + (size_t)head * a.N_max;
+  const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+  Keys<false> key{nullptr, src, p_end, r_begin};
+  uint32_t kk[PQ][4];
+#pragma unroll
+  for (int u = 0; u < PQ; ++u) {
+    const int t = t0 + 4 * (tid + u * NT);
+    if (vec && t + 3 < t1) {
+      const uint4 k4 = key.four(reinterpret_cast<const float4*>(src)[t >> 2], t);
+      kk[u][0] = k4.x; kk[u][1] = k4.y; kk[u][2] = k4.z; kk[u][3] = k4.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kk[u][e] = t + e < t1 ? key(t + e) : 0u;
+    }
+  }
+  auto valid = [&](int u, int e) { return t0 + 4 * (tid + u * NT) + e < t1; };
+  auto sum_parts = [&](int d, int nb) {   // sm.hist = sum over parts of digit d
+    for (int i = tid; i < nb; i += NT) {
+      uint32_t c = 0;
+      for (int q = 0; q < P; ++q) c += hist_h[((size_t)d * P + q) * NBINS + i];
+      sm.hist[i] = c;
+    }
+    __syncthreads();
+  };
+  auto publish = [&](int d, int nb) {     // this part's histogram of digit d
+    __syncthreads();
+    for (int i = tid; i < nb; i += NT) {
+      hist_h[((size_t)d * P + part) * NBINS + i] = sm.hist[i];
+    }
+  };
+
+  if (PHASE == 0) {
+    for (int i = tid; i < NBINS; i += NT) sm.hist[i] = 0;
+    __syncthreads();
+    const uint32_t tk = to_key(bu.tau);
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int u = 0; u < PQ; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (valid(u, e)) {
+          cnt += kk[u][e] >= tk ? 1u : 0u;
+          atomicAdd(&sm.hist[kk[u][e] >> 21], 1u);
+        }
+    cnt = block_sum(cnt, sm);
+    if (tid == 0) pstat_h[part * 4 + 0] = cnt;
+    publish(0, NBINS);
+    return;
+  }
+
+  if (PHASE == 1) {
+    uint32_t cnt = 0;
+    for (int q = 0; q < P; ++q) cnt += pstat_h[q * 4 + 0];
+    int lo, hi;
+    budget_clamps(bu, n, &lo, &hi);
+    int k = count_budget(bu, head, n, cnt, lo, hi);
+    k = min(max(k, n_prot), n);
+    sum_parts(0, NBINS);
+    resolve_digit<false>(sm, NBINS, (unsigned long long)k);
+    const uint32_t bin = sm.bin;
+    const uint32_t rem = (uint32_t)k - sm.cnt_above;
+    if (part == 0 && tid == 0) st_h[1] = PartState{k, bin << 21, rem, 0u};
+#pragma unroll
+    for (int u = 0; u < PQ; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (valid(u, e) && (kk[u][e] >> 21) == bin) atomicAdd(&sm.hist[(kk[u][e] >> 10) & 2047], 1u);
+    publish(1, NBINS);
+    return;
+  }
+
+  if (PHASE == 2) {
+    const PartState ps = st_h[1];
+    sum_parts(1, NBINS);
+    resolve_digit<false>(sm, NBINS, (unsigned long long)ps.rem);
+    const uint32_t prefix = ps.prefix | (sm.bin << 10);
+    const uint32_t rem = ps.rem - sm.cnt_above;
+    if (part == 0 && tid == 0) st_h[2] = PartState{ps.k, prefix, rem, 0u};
+#pragma unroll
+    for (int u = 0; u < PQ; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (valid(u, e) && (kk[u][e] >> 10) == (prefix >> 10)) atomicAdd(&sm.hist[kk[u][e] & 1023], 1u);
+    publish(2, 1024);
+    return;
+  }
+
+  if (PHASE == 3) {
+    const PartState ps = st_h[2];
+    sum_parts(2, 1024);
+    resolve_digit<false>(sm, 1024, (unsigned long long)ps.rem);
+    const uint32_t T = ps.prefix | sm.bin;
+    const uint32_t quota = ps.rem - sm.cnt_above;
+    if (part == 0 && tid == 0) st_h[3] = PartState{ps.k, T, quota, 0u};
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int u = 0; u < PQ; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (valid(u, e)) { gt += kk[u][e] > T ? 1u : 0u; eq += kk[u][e] == T ? 1u : 0u; }
+    gt = block_sum(gt, sm);
+    eq = block_sum(eq, sm);
+    if (tid == 0) { pstat_h[part * 4 + 1] = gt; pstat_h[part * 4 + 2] = eq; }
+    return;
+  }
+
+  // PHASE 4: emit.  The part's tokens form PQ * NWV chunks of 4 * WAVE
+  // consecutive tokens, chunk (u, w) = lanes of wave w at load u, in token
+  // order u-major; each chunk's kept tokens go out in lane order.
+  const PartState ps = st_h[3];
+  const uint32_t T = ps.prefix, quota = ps.rem;
+  uint32_t off = 0, eqb = 0;   // kept by, and ties in, the earlier parts
+  for (int q = 0; q < part; ++q) {
+    const uint32_t g = pstat_h[q * 4 + 1], e = pstat_h[q * 4 + 2];
+    const uint32_t left = quota > eqb ? quota - eqb : 0u;
+    off += g + min(left, e);
+    eqb += e;
+  }
+  if (part == 0 && tid == 0) a.kept_count[head] = ps.k;
+  __shared__ uint32_t cg[PQ][NWV], ce[PQ][NWV];
+#pragma unroll
+  for (int u = 0; u < PQ; ++u) {
+    uint32_t g = 0, e = 0;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      g += (uint32_t)__popcll(__ballot(valid(u, x) && kk[u][x] > T));
+      e += (uint32_t)__popcll(__ballot(valid(u, x) && kk[u][x] == T));
+    }
+    if (lane == 0) { cg[u][wave] = g; ce[u][wave] = e; }
+  }
+  __syncthreads();
+  int32_t* dst = a.kept_idx + (size_t)head * a.N_max;
+#pragma unroll
+  for (int u = 0; u < PQ; ++u) {
+    // slot and tie rank at the start of chunk (u, wave)
+    uint32_t slot = off, r = eqb;
+    for (int c = 0; c < u * NWV + wave; ++c) {
+      const uint32_t g = cg[c / NWV][c % NWV], e = ce[c / NWV][c % NWV];
+      const uint32_t left = quota > r ? quota - r : 0u;
+      slot += g + min(left, e);
+      r += e;
+    }
+    bool is_gt[4], is_eq[4], keep[4];
+    uint64_t be[4], bk[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      is_gt[x] = valid(u, x) && kk[u][x] > T;
+      is_eq[x] = valid(u, x) && kk[u][x] == T;
+      be[x] = __ballot(is_eq[x]);
+      r += mbcnt(be[x]);
+    }
+    uint32_t at = slot;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      keep[x] = is_gt[x] || (is_eq[x] && r < quota);
+      r += is_eq[x] ? 1u : 0u;
+      bk[x] = __ballot(keep[x]);
+      at += mbcnt(bk[x]);
+    }
+    const int t = t0 + 4 * (tid + u * NT);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      if (keep[x]) {
+        if (at < (uint32_t)n) dst[at] = t + x;
+        ++at;
+      }
+    }
+  }
+}
+
+// The five launches of the part path; per-kernel timing sees them as one
+// "select" (start stamped by the first dispatch, stop by the last).
+void select_parts(const SelectArgs& s, int P, void* ws, hipStream_t st) {
+  PartArgs pa;
+  pa.s = s;
+  pa.P = P;
+  const int H = s.B * s.Hkv;
+  pa.hist = static_cast<uint32_t*>(ws);
+  pa.pstat = pa.hist + (size_t)H * 3 * P * NBINS;
+  pa.state = reinterpret_cast<PartState*>(pa.pstat + (size_t)H * P * 4);
+  const dim3 grid(P, H), block(NT);
+  hipEvent_t e0, e1;
+  const bool timed = timing_events("select", &e0, &e1);
+  if (timed)
+    hipExtLaunchKernelGGL(select_part_kernel<0>, grid, block, 0, st, e0, nullptr, 0, pa);
+  else
+    hipLaunchKernelGGL(select_part_kernel<0>, grid, block, 0, st, pa);
+  hipLaunchKernelGGL(select_part_kernel<1>, grid, block, 0, st, pa);
+  hipLaunchKernelGGL(select_part_kernel<2>, grid, block, 0, st, pa);
+  hipLaunchKernelGGL(select_part_kernel<3>, grid, block, 0, st, pa);
+  if (timed) {
+    hipExtLaunchKernelGGL(select_part_kernel<4>, grid, block, 0, st, nullptr, e1, 0, pa);
+    timing_done("select", e0, e1);
+  } else {
+    hipLaunchKernelGGL(select_part_kernel<4>, grid, block, 0, st, pa);
+  }
+}
+
 }  // namespace
 }  // namespace kvcc
 
 using namespace kvcc;
 
 extern "C" size_t kv_select_workspace_size(int B, int Hkv, int N_max) {
-  (void)B; (void)Hkv; (void)N_max;
-  return 0;
+  if (B < 1 || Hkv < 1 || N_max <= LDS_KEYS) return 0;
+  return part_workspace(B * Hkv, ceil_div(N_max, PT));
 }
 
 extern "C" int kv_select(const float* scores, const int32_t* ctx_len,
                          int B, int Hkv, int N_max, const kv_budget* budget,
                          int32_t* kept_idx, int32_t* kept_count,
                          void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace; (void)workspace_bytes;
   if (!scores || !budget || !kept_idx || !kept_count) return KV_ERR_NULL;
   if (!aligned16(scores) || !aligned16(ctx_len) || !aligned16(kept_idx) ||
-      !aligned16(kept_count) || !aligned16(budget->k) || !aligned16(budget->ratio))
+      !aligned16(kept_count) || !aligned16(budget->k) || !aligned16(budget->ratio) ||
+      !aligned16(workspace))
     return KV_ERR_ALIGN;
   if (B < 1 || Hkv < 1 || N_max < 1 || (int64_t)B * Hkv * N_max >= (int64_t(1) << 31))
     return KV_ERR_SHAPE;
@@ -611,6 +914,18 @@ extern "C" int kv_select(const float* scores, const int32_t* ctx_len,
   if (bu.mode == KV_BUDGET_THRESHOLD && isnan(bu.tau)) return KV_ERR_MODE;
   if (bu.n_sink < 0 || bu.n_recent < 0) return KV_ERR_MODE;
 
+  // Long heads under a count budget take the part path when the workspace
+  // is there (its size covers it whenever N_max > LDS_KEYS).
+  const int P = ceil_div(N_max, PT);
+  if (N_max > LDS_KEYS && bu.mode != KV_BUDGET_MASS && workspace &&
+      workspace_bytes >= part_workspace(B * Hkv, P)) {
+    SelectArgs a;
+    a.scores = scores; a.ctx = ctx_len; a.n_head = nullptr; a.B = B; a.Hkv = Hkv; a.N_max = N_max;
+    a.k_zero_ok = 0;
+    a.bud = bu; a.kept_idx = kept_idx; a.kept_count = kept_count;
+    select_parts(a, P, workspace, static_cast<hipStream_t>(stream));
+    return launch_status();
+  }
   select_launch(scores, ctx_len, nullptr, B, Hkv, N_max, bu, false, kept_idx, kept_count,
                 static_cast<hipStream_t>(stream), "select");
   return launch_status();

@@ -20,7 +20,8 @@
 // the first q such tokens; the emit walks wave-contiguous token segments with
 // ballot/mbcnt prefixes, so indices come out ascending.  Heads of up to 32768
 // tokens keep their keys in LDS (and a wave's segment in registers for the
-// emit); longer heads re-read the scores.
+// emit); longer heads re-read the scores, or, under a count budget with the
+// workspace given, are split over several workgroups (the part path below).
 //
 // Protected tokens (the first n_sink and last n_recent of a head) get the
 // largest key, 0xffffffff, above every finite score: they lead the order,

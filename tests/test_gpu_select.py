@@ -206,3 +206,48 @@ def test_select_protected(kind, shape):
                     assert np.array_equal(idx_g[bb, h, :kg], ref), (bb, h)
                     assert set(np.flatnonzero(prot)) <= set(idx_g[bb, h, :kg].tolist())
 
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_select_long_heads_parts_equal_one_workgroup(kind):
+    # Heads above 32768 tokens under a count budget are split over several
+    # workgroups when the workspace is given; without it one workgroup per
+    # head selects.  Both must give the same kept indices, bit for bit, and
+    # match the oracle.
+    from kv_cache_compression_score_amd import _lib
+    import ctypes
+    B, Hkv, N, ctx = 2, 2, 70001, [70001, 40000]
+    s_np = synth_scores(KINDS.index(kind) * 7919 + 5, B, Hkv, N, ctx, kind)
+    s = torch.from_numpy(s_np).cuda()
+    c = torch.tensor(ctx, dtype=torch.int32).cuda()
+    L = _lib.lib()
+    need = int(L.kv_select_workspace_size(B, Hkv, N))
+    assert need > 0
+    ws = torch.empty(need, device="cuda", dtype=torch.uint8)
+    buds = [(api.Budget(api.BUDGET_RATIO, ratio_scalar=0.1), dict(mode=orc.BUDGET_RATIO, ratio=0.1)),
+            (api.Budget(api.BUDGET_K, k_scalar=5000), dict(mode=orc.BUDGET_K, k=5000)),
+            (api.Budget(api.BUDGET_THRESHOLD, tau=float(np.median(s_np[0, 0, :40000])),
+                        min_ratio=0.02, max_ratio=0.5),
+             dict(mode=orc.BUDGET_THRESHOLD, tau=float(np.median(s_np[0, 0, :40000])),
+                  min_ratio=0.02, max_ratio=0.5)),
+            (api.Budget(api.BUDGET_RATIO, ratio_scalar=0.05, n_sink=4, n_recent=300),
+             dict(mode=orc.BUDGET_RATIO, ratio=0.05, n_sink=4, n_recent=300))]
+    for bud, ref in buds:
+        out = []
+        for w, nb in ((ws, need), (None, 0)):
+            idx = torch.full((B, Hkv, N), -1, device="cuda", dtype=torch.int32)
+            cnt = torch.zeros(B * Hkv, device="cuda", dtype=torch.int32)
+            cb = bud.to_c()
+            st = L.kv_select(api._ptr(s), api._ptr(c), B, Hkv, N, ctypes.byref(cb), api._ptr(idx),
+                             api._ptr(cnt), api._ptr(w), nb, api._stream())
+            assert st == 0, st
+            torch.cuda.synchronize()
+            out.append((idx.cpu().numpy(), cnt.cpu().numpy()))
+        (i_p, c_p), (i_1, c_1) = out
+        assert np.array_equal(c_p, c_1)
+        for h in range(B * Hkv):
+            k = int(c_p[h])
+            assert np.array_equal(i_p.reshape(B * Hkv, N)[h, :k], i_1.reshape(B * Hkv, N)[h, :k]), h
+        mode = ref.pop("mode")
+        idx_r, cnt_r = orc.select(s_np, ctx, mode, **ref)
+        compare_sets(i_p, c_p, idx_r, cnt_r)

@@ -40,6 +40,8 @@ namespace {
 constexpr int TOK = 64;          // tokens per LDS tile
 constexpr int RBW = 2;           // 32-row blocks per wave
 constexpr int SLOTS_1 = 256 * 2; // pass-1 chunking target: resident workgroups on 256 CUs
+constexpr int RANGE_HEADS = 256;  // most heads (B * Hkv) the balanced pass-2 ranges take
+constexpr int TAB_MAX = 2048;     // most pass-2 workgroups in that mode
 
 template <typename T> struct FragT;
 template <> struct FragT<__bf16> { using vec = bf16x8; };   // 8 elements = 16 B
@@ -144,8 +146,62 @@ struct ScoreArgs {
   int B, Hq, Hkv, N_max, W, G, R, R_pad, causal;
   int TC, n_chunks;    // pass-1 token chunks (fixed by the sizes: sets the merge order)
   int TC2, n_chunks2;  // pass-2 token chunks (free: no cross-chunk arithmetic)
+  int ranges;          // pass 2: balanced tile ranges over G2 workgroups (see score_pass)
+  int G2;              // pass-2 workgroups in that mode
+  int4* tab;           // [TAB_MAX] the ranges, written by pass 1: {head, t0, t1, n}
   float c;             // scale * log2(e)
 };
+
+// Pass-2 work ranges, built by one workgroup of pass 1 so that pass 2 reads
+// its range with one load.  Each head's 64-token tiles are cut into ranges
+// of L tiles, L = ceil(T / G) if that leaves at most G ranges, else
+// ceil(T / (G - H)) (T tiles in all, G = a.G2 workgroups, H heads), and range
+// i goes to workgroup i in (sequence, head, range) order: with ragged lengths
+// no workgroup gets more than about T / (G - H) tiles, where chunks sized for
+// N_max leave some CUs whole heads and others nothing; with equal lengths the
+// ranges are those chunks.  Unused entries get head -1.  `scr` is LDS for
+// 2 B + 3 ints (B <= RANGE_HEADS).
+__device__ void build_ranges(const ScoreArgs& a, int* scr) {
+  const int tid = threadIdx.x, nt_thr = blockDim.x;
+  const int B = a.B, Hkv = a.Hkv, H = B * Hkv, G = a.G2;
+  int* seqr = scr;              // ranges per head of sequence b
+  int* seqpre = scr + B;        // ranges before sequence b (B + 1 entries)
+  int* tot = scr + 2 * B + 1;   // tiles, ranges
+  auto len = [&](int bb) { return a.ctx ? min(max(a.ctx[bb], 0), a.N_max) : a.N_max; };
+  if (tid == 0) { tot[0] = 0; tot[1] = 0; }
+  __syncthreads();
+  for (int bb = tid; bb < B; bb += nt_thr) atomicAdd(&tot[0], Hkv * ((len(bb) + TOK - 1) / TOK));
+  __syncthreads();
+  const int total = tot[0];
+  int L = max(1, (total + G - 1) / G);
+  for (int bb = tid; bb < B; bb += nt_thr)
+    atomicAdd(&tot[1], Hkv * (((len(bb) + TOK - 1) / TOK + L - 1) / L));
+  __syncthreads();
+  if (tot[1] > G) L = max(1, (total + (G - H) - 1) / (G - H));
+  for (int bb = tid; bb < B; bb += nt_thr) seqr[bb] = ((len(bb) + TOK - 1) / TOK + L - 1) / L;
+  __syncthreads();
+  if (tid == 0) {
+    seqpre[0] = 0;
+    for (int bb = 0; bb < B; ++bb) seqpre[bb + 1] = seqpre[bb] + Hkv * seqr[bb];
+  }
+  __syncthreads();
+  const int R = seqpre[B];
+  for (int i = tid; i < G; i += nt_thr) {
+    int4 e = make_int4(-1, 0, 0, 0);
+    if (i < R) {
+      int lo = 0, hi = B - 1;   // largest b with seqpre[b] <= i (empty sequences are passed over)
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (seqpre[mid] <= i) lo = mid; else hi = mid - 1;
+      }
+      const int q = i - seqpre[lo], rb = seqr[lo];
+      const int nb = len(lo);
+      const int t0 = (q % rb) * L * TOK;
+      e = make_int4(lo * Hkv + q / rb, t0, min(t0 + L * TOK, nb), nb);
+    }
+    a.tab[i] = e;
+  }
+}
 
 template <typename T, int D, int NW, int PASS>
 __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
@@ -164,21 +220,41 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
   __shared__ float red[3][PASS == 2 ? NW : 1][TOK];
   __shared__ __attribute__((aligned(8))) int rowpos[PASS == 2 ? NW * RBW * 32 : 2];
 
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int hf = lane >> 5, l32 = lane & 31;
-  const int n = a.ctx ? min(max(a.ctx[b], 0), a.N_max) : a.N_max;
-  const int head = b * a.Hkv + h;
-  const int TC = PASS == 1 ? a.TC : a.TC2;
-  const int t0 = c * TC;
 
-  if (t0 >= n) {
-    if (PASS == 1)
-      for (int r = tid; r < a.R_pad; r += NT)
-        a.part[((size_t)head * a.R_pad + r) * a.n_chunks + c] = make_float2(-INFINITY, 0.f);
-    return;
+  // The workgroup's tokens [t0, t1) of head (b, h).  Chunk mode: chunk
+  // blockIdx.x of head (blockIdx.z, blockIdx.y).  Balanced mode (pass 2,
+  // a.ranges): range blockIdx.x of the table that one workgroup of pass 1
+  // built (build_ranges), read with one scalar load.
+  int b, h, c, t0, t1, n;
+  if (PASS == 1 && a.ranges && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) {
+    build_ranges(a, reinterpret_cast<int*>(&ktile[0][0]));   // LDS not in use yet
+    __syncthreads();
   }
-  const int t1 = min(t0 + TC, n);
+  if (PASS == 2 && a.ranges) {
+    const int4 e = a.tab[blockIdx.x];
+    const int hd = __builtin_amdgcn_readfirstlane(e.x);
+    if (hd < 0) return;   // fewer ranges than workgroups
+    // the division runs on the VALU: bring the quotient back to SGPRs
+    b = __builtin_amdgcn_readfirstlane(hd / a.Hkv); h = hd - b * a.Hkv; c = 0;
+    t0 = __builtin_amdgcn_readfirstlane(e.y);
+    t1 = __builtin_amdgcn_readfirstlane(e.z);
+    n = __builtin_amdgcn_readfirstlane(e.w);
+  } else {
+    c = blockIdx.x; h = blockIdx.y; b = blockIdx.z;
+    n = a.ctx ? min(max(a.ctx[b], 0), a.N_max) : a.N_max;
+    const int TC = PASS == 1 ? a.TC : a.TC2;
+    t0 = c * TC;
+    if (t0 >= n) {
+      if (PASS == 1)
+        for (int r = tid; r < a.R_pad; r += NT)
+          a.part[((size_t)(b * a.Hkv + h) * a.R_pad + r) * a.n_chunks + c] = make_float2(-INFINITY, 0.f);
+      return;
+    }
+    t1 = min(t0 + TC, n);
+  }
+  const int head = b * a.Hkv + h;
   const int ntiles = (t1 - t0 + TOK - 1) / TOK;
   const char* kh = static_cast<const char*>(a.k) + (size_t)head * a.N_max * ROWB;
   const int last_w0 = n - a.W;   // position of window row 0; row w sits at last_w0 + w
@@ -558,7 +634,7 @@ __global__ __launch_bounds__(256) void score_fold(ScoreArgs a) {
 
 struct ScorePlan {
   int G, R, R_pad, NW, TC, n_chunks;
-  size_t off_lse, bytes;
+  size_t off_lse, off_tab, bytes;
 };
 
 // Tokens per workgroup: the tile count per chunk (at least `min_tiles`) that
@@ -593,7 +669,9 @@ bool plan_score(int B, int Hq, int Hkv, int N_max, int W, int d, ScorePlan* p) {
   p->n_chunks = ceil_div(N_max, p->TC);
   const size_t part = (size_t)B * Hkv * p->n_chunks * p->R_pad * sizeof(float2);
   p->off_lse = (part + 255) & ~size_t(255);
-  p->bytes = p->off_lse + (size_t)B * Hkv * p->R_pad * sizeof(float);
+  const size_t lse_end = p->off_lse + (size_t)B * Hkv * p->R_pad * sizeof(float);
+  p->off_tab = (lse_end + 255) & ~size_t(255);
+  p->bytes = p->off_tab + (size_t)TAB_MAX * sizeof(int4);
   return true;
 }
 
@@ -617,7 +695,14 @@ void launch_score(ScoreArgs a, hipStream_t st) {
   a.TC2 = chunk_tokens((int64_t)a.B * a.Hkv, a.N_max,
                        resident_slots(score_pass<T, D, NW, 2>, NW * WAVE, &slots2), 4);
   a.n_chunks2 = ceil_div(a.N_max, a.TC2);
-  const dim3 grid1(a.n_chunks, a.Hkv, a.B), grid2(a.n_chunks2, a.Hkv, a.B);
+  const dim3 grid1(a.n_chunks, a.Hkv, a.B);
+  dim3 grid2(a.n_chunks2, a.Hkv, a.B);
+  // Balanced pass-2 ranges (two-pass path): one workgroup per resident slot,
+  // at least two per head; pass 1 writes the table
+  const int H = a.B * a.Hkv;
+  a.G2 = std::min(slots2 > 0 ? slots2 : SLOTS_1, TAB_MAX);
+  a.ranges = a.tab && !a.lse_in && H <= RANGE_HEADS && 2 * H <= a.G2 ? 1 : 0;
+  if (a.ranges) grid2 = dim3((unsigned)a.G2, 1, 1);
   if (a.lse_in) {   // row LSEs given: the column-sum pass alone
     launch("score_colsum", score_pass<T, D, NW, 2>, grid2, dim3(NW * WAVE), 0, st, a);
     return;
@@ -668,6 +753,7 @@ extern "C" int kv_score(const void* q_win, const void* k, const int32_t* ctx_len
   a.lse_in = nullptr;
   a.part = static_cast<float2*>(workspace);
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_lse);
+  a.tab = reinterpret_cast<int4*>(static_cast<char*>(workspace) + p.off_tab);
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N_max = N_max; a.W = W; a.G = p.G;
   a.R = p.R; a.R_pad = p.R_pad; a.TC = p.TC; a.n_chunks = p.n_chunks;
   a.TC2 = p.TC; a.n_chunks2 = p.n_chunks;
@@ -699,7 +785,7 @@ extern "C" int kv_score_from_lse(const void* q_win, const void* k, const int32_t
 
   ScoreArgs a;
   a.q = q_win; a.k = k; a.ctx = ctx_len; a.scores = scores; a.row_lse = nullptr;
-  a.lse_in = row_lse_in; a.part = nullptr; a.lse2 = nullptr;
+  a.lse_in = row_lse_in; a.part = nullptr; a.lse2 = nullptr; a.tab = nullptr;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N_max = N_max; a.W = W; a.G = p.G;
   a.R = p.R; a.R_pad = p.R_pad; a.TC = p.TC; a.n_chunks = p.n_chunks;
   a.TC2 = p.TC; a.n_chunks2 = p.n_chunks;

@@ -400,7 +400,7 @@ def main():
     cold_w = step_distribution(pipe, args.steps, lambda: buf.fill_(1.0))
     del buf
     t = {k: v[0] * 1e-3 for k, v in kt.items()}
-    t_score = t["score_rowstats"] + t["score_fold"] + t["score_colsum"]
+    t_score = t["score_rowstats"] + t.get("score_fold", 0.0) + t["score_colsum"]   # fold: row LSEs asked for
     t_dec = t["decode_split"] + t["decode_merge"]
     t_scd = t["select"] + t["compact"] + t_dec
     res = {

@@ -42,6 +42,7 @@ constexpr int RBW = 2;           // 32-row blocks per wave
 constexpr int SLOTS_1 = 256 * 2; // pass-1 chunking target: resident workgroups on 256 CUs
 constexpr int RANGE_HEADS = 256;  // most heads (B * Hkv) the balanced pass-2 ranges take
 constexpr int TAB_MAX = 2048;     // most pass-2 workgroups in that mode
+constexpr int SELF_MERGE = 16;    // pass 2 merges pass 1's partials itself up to this many chunks
 
 template <typename T> struct FragT;
 template <> struct FragT<__bf16> { using vec = bf16x8; };   // 8 elements = 16 B
@@ -139,7 +140,7 @@ struct ScoreArgs {
   const void* k;
   const int32_t* ctx;
   float* scores;
-  float2* part;     // [B*Hkv][R_pad][n_chunks] per-chunk (max, sum of exp2) per row
+  float2* part;     // [B*Hkv][n_chunks][R_pad] per-chunk (max, sum of exp2) per row
   float* lse2;      // [B*Hkv][R_pad] base-2 row log-sum-exp (+inf: row adds nothing)
   float* row_lse;   // [B][Hq][W] natural log, optional
   const float* lse_in;  // [B][Hq][W] natural-log row LSE given by the caller (one-pass), or null
@@ -149,6 +150,7 @@ struct ScoreArgs {
   int ranges;          // pass 2: balanced tile ranges over G2 workgroups (see score_pass)
   int G2;              // pass-2 workgroups in that mode
   int4* tab;           // [TAB_MAX] the ranges, written by pass 1: {head, t0, t1, n}
+  int self_merge;      // pass 2 merges the pass-1 partials (n_chunks <= SELF_MERGE); else the fold's lse2
   float c;             // scale * log2(e)
 };
 
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
     if (t0 >= n) {
       if (PASS == 1)
         for (int r = tid; r < a.R_pad; r += NT)
-          a.part[((size_t)(b * a.Hkv + h) * a.R_pad + r) * a.n_chunks + c] = make_float2(-INFINITY, 0.f);
+          a.part[((size_t)(b * a.Hkv + h) * a.n_chunks + c) * a.R_pad + r] = make_float2(-INFINITY, 0.f);
       return;
     }
     t1 = min(t0 + TC, n);
@@ -298,23 +300,63 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
   if (PASS == 1) {
 #pragma unroll
     for (int i = 0; i < RBW; ++i) { m_run[i] = -INFINITY; s_run[i] = 0.f; }
-  } else {
+  } else if (a.lse_in) {
 #pragma unroll
     for (int i = 0; i < RBW; ++i) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = (wave * RBW + i) * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
-        float v;
-        if (a.lse_in) {   // caller's natural-log LSE of row (j, w), to base 2
-          // rc / W by a float reciprocal: exact for rc < 1024 (error < 0.5/W)
-          const int rc = min(r, a.R - 1);
-          const int jw = (int)(((float)rc + 0.5f) * inv_w);
-          const int j = h * a.G + jw, w = rc - jw * a.W;
-          v = a.lse_in[((size_t)b * a.Hq + j) * a.W + w] * (float)LOG2E_D;
-        } else {
-          v = a.lse2[(size_t)head * a.R_pad + min(r, a.R_pad - 1)];
-        }
+        // caller's natural-log LSE of row (j, w), to base 2;
+        // rc / W by a float reciprocal: exact for rc < 1024 (error < 0.5/W)
+        const int rc = min(r, a.R - 1);
+        const int jw = (int)(((float)rc + 0.5f) * inv_w);
+        const int j = h * a.G + jw, w = rc - jw * a.W;
+        const float v = a.lse_in[((size_t)b * a.Hq + j) * a.W + w] * (float)LOG2E_D;
         nl2[i][e] = r < a.R ? -v : -INFINITY;
+      }
+    }
+  } else if (!a.self_merge) {   // the fold's row LSEs
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = (wave * RBW + i) * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+        nl2[i][e] = r < a.R ? -a.lse2[(size_t)head * a.R_pad + min(r, a.R_pad - 1)] : -INFINITY;
+      }
+    }
+  } else {
+    // Base-2 LSE of each row from pass 1's per-chunk (m, sum) partials of
+    // this head (at most 16, loads all issued at once): M = max of the m's,
+    // then the sum of sum * 2^(m - M).  Staged in `red` (not in use before
+    // tile 0).
+    float* lse_s = &red[0][0][0];
+    for (int r = tid; r < NW * RBW * 32; r += NT) {
+      float v = INFINITY;
+      if (r < a.R) {
+        const float2* src = a.part + (size_t)head * a.n_chunks * a.R_pad + r;
+        float2 pk[SELF_MERGE];
+#pragma unroll
+        for (int u = 0; u < SELF_MERGE; ++u)   // chunk u of the row: lanes read consecutive rows
+          pk[u] = u < a.n_chunks ? src[(size_t)u * a.R_pad] : make_float2(-INFINITY, 0.f);
+        float M = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < SELF_MERGE; ++u) M = fmaxf(M, pk[u].x);
+        if (M != -INFINITY) {
+          float S = 0.f;
+#pragma unroll
+          for (int u = 0; u < SELF_MERGE; ++u) S = fmaf(pk[u].y, fast_exp2(pk[u].x - M), S);
+          if (S > 0.f) v = M + log2f(S);
+        }
+      }
+      lse_s[r] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = (wave * RBW + i) * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+        nl2[i][e] = r < a.R ? -lse_s[r] : -INFINITY;
       }
     }
   }
@@ -578,7 +620,7 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
       if (mn != -INFINITY) s = s_run[i] * fast_exp2(m_run[i] - mn) + so * fast_exp2(mo - mn);
       const int r = (wave * RBW + i) * 32 + l32;
       if (hf == 0 && r < a.R_pad)
-        a.part[((size_t)head * a.R_pad + r) * a.n_chunks + c] = make_float2(mn, s);
+        a.part[((size_t)head * a.n_chunks + c) * a.R_pad + r] = make_float2(mn, s);
     }
   }
 }
@@ -602,9 +644,9 @@ __global__ __launch_bounds__(256) void score_fold(ScoreArgs a) {
   const int head = row_id / a.R_pad, r = row_id % a.R_pad;
   float m = -INFINITY, s = 0.f;
   if (live && r < a.R) {
-    const float2* src = a.part + (size_t)row_id * a.n_chunks;
+    const float2* src = a.part + (size_t)head * a.n_chunks * a.R_pad + r;
     for (int c = l; c < a.n_chunks; c += FOLD_LANES) {
-      const float2 p = src[c];
+      const float2 p = src[(size_t)c * a.R_pad];
       merge(m, s, p.x, p.y);
     }
   }
@@ -703,13 +745,18 @@ void launch_score(ScoreArgs a, hipStream_t st) {
   a.G2 = std::min(slots2 > 0 ? slots2 : SLOTS_1, TAB_MAX);
   a.ranges = a.tab && !a.lse_in && H <= RANGE_HEADS && 2 * H <= a.G2 ? 1 : 0;
   if (a.ranges) grid2 = dim3((unsigned)a.G2, 1, 1);
+  a.self_merge = a.n_chunks <= SELF_MERGE ? 1 : 0;
   if (a.lse_in) {   // row LSEs given: the column-sum pass alone
     launch("score_colsum", score_pass<T, D, NW, 2>, grid2, dim3(NW * WAVE), 0, st, a);
     return;
   }
   launch("score_rowstats", score_pass<T, D, NW, 1>, grid1, dim3(NW * WAVE), 0, st, a);
-  const int rows = a.B * a.Hkv * a.R_pad;
-  launch("score_fold", score_fold, dim3(ceil_div(rows, 256 / FOLD_LANES)), dim3(256), 0, st, a);
+  // with few chunks pass 2 merges the partials of its own head, and the fold
+  // runs only to hand the caller the row LSEs
+  if (a.row_lse || !a.self_merge) {
+    const int rows = a.B * a.Hkv * a.R_pad;
+    launch("score_fold", score_fold, dim3(ceil_div(rows, 256 / FOLD_LANES)), dim3(256), 0, st, a);
+  }
   launch("score_colsum", score_pass<T, D, NW, 2>, grid2, dim3(NW * WAVE), 0, st, a);
 }
 

@@ -93,6 +93,24 @@ def test_score_far_outlier_logit(spread):
     np.testing.assert_allclose(lse_gpu.cpu().numpy(), lse_ref, atol=1e-3, rtol=0)
 
 
+@pytest.mark.parametrize("N", [4000, 5000])
+def test_score_pass1_chunk_merge_paths(N):
+    # One KV head: pass 1 cuts 4000 tokens into 16 chunks (pass 2 merges the
+    # partials itself) and 5000 into 20 (pass 2 reads the fold's row LSEs).
+    # Either way the scores match the oracle, and asking for the row LSEs
+    # (which adds the fold launch) leaves the scores bit for bit unchanged.
+    lay = wl.random_case(31, B=1, Hq=4, Hkv=1, d=128, N_max=N, W=48, dtype=torch.bfloat16)
+    log(f"score chunk merge N={N}")
+    q, k = dev(lay.q_win), dev(lay.k)
+    s1, _ = api.kv_score(q, k, None, causal=True)
+    s2, lse = api.kv_score(q, k, None, causal=True, with_row_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    s_ref, lse_ref = orc.window_scores(lay.q_win, lay.k, None, causal=True)
+    check_scores(s1.cpu().numpy(), s_ref, np.array([N]), 48, 4)
+    np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, atol=1e-3, rtol=0)
+
+
 def test_score_llama8b_layer_full():
     cfg = wl.CONFIGS["llama8b_layer"]
     lay = wl.make_layer(cfg, with_v=False)

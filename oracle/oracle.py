@@ -312,7 +312,9 @@ def decode(q, k_c, v_c, offsets, Hkv: int, scale=None):
     q [B][Hq][d]; k_c, v_c [total][d] (float arrays or bf16 tensors);
     offsets [B*Hkv+1].  For query head j of KV head h = j // G with rows
     o..o+k-1:  u_i = scale*<q, K_c[o+i]>,  out = sum_i softmax(u)_i V_c[o+i],
-    lse = m + log(sum_i exp(u_i - m)).  Returns (out [B][Hq][d], lse [B][Hq]).
+    lse = m + log(sum_i exp(u_i - m)).  A head with no rows has an empty sum:
+    lse = log 0 = -inf, and its output is taken as 0.
+    Returns (out [B][Hq][d], lse [B][Hq]).
     """
     qq = _f64(q)
     kc = _f64(k_c)
@@ -327,6 +329,9 @@ def decode(q, k_c, v_c, offsets, Hkv: int, scale=None):
         for j in range(Hq):
             h = j // G
             lo, hi = int(off[b * Hkv + h]), int(off[b * Hkv + h + 1])
+            if hi <= lo:
+                lse[b, j] = -math.inf
+                continue
             u = sc * (kc[lo:hi] @ qq[b, j])
             m = u.max()
             e = np.exp(u - m)

@@ -293,3 +293,17 @@ def test_fidelity_matches_brute_force():
             assert math.isclose(f["lse_diff"][0, j], lh - l, abs_tol=1e-12)
             assert math.isclose(f["out_err2"][0, j], math.fsum((a - b) ** 2 for a, b in zip(yh, y)),
                                 rel_tol=1e-10, abs_tol=1e-24)
+
+
+def test_decode_empty_head():
+    # A head with no kept rows: the empty sum gives lse = log 0 = -inf and a
+    # zero output; the other heads are the same as without it.
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 4, 8))
+    k_c = rng.standard_normal((6, 8))
+    v_c = rng.standard_normal((6, 8))
+    out, lse = orc.decode(q, k_c, v_c, np.array([0, 0, 6]), 2)   # head 0 empty, G = 2
+    assert np.all(out[0, :2] == 0.0) and np.all(np.isneginf(lse[0, :2]))
+    out1, lse1 = orc.decode(q[:, 2:], k_c, v_c, np.array([0, 6]), 1)
+    np.testing.assert_allclose(out[0, 2:], out1[0], rtol=1e-15, atol=0)
+    np.testing.assert_allclose(lse[0, 2:], lse1[0], rtol=1e-15, atol=0)

@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Throughput of the score -> select -> compact -> decode path on one GPU.
 
-One step = kv_score + kv_select + kv_compact + kv_decode_attn over one batch
+One step = kv_score + kv_select + kv_compact_decode (kv_compact and
+kv_decode_attn in one pass over the kept rows) over one batch
 of the chosen synthetic workload (default: batch 4 at 32K context, 32 query
 / 8 KV heads, d = 128, W = 64, keep 10%, one decode step), inputs resident
 in HBM before timing starts.  Prints one JSON line:
@@ -17,6 +18,8 @@ in HBM before timing starts.  Prints one JSON line:
               summary under profiles/ and reported only while the kernel's
               sources still hash to the recorded value
   copy_gbps   a 1 GiB device-to-device copy (read + write bytes / time)
+  unfused     the same step with kv_compact and kv_decode_attn as two calls;
+              decode_hbm_gbps is that decode's rate
   fidelity    output / log-sum-exp loss terms of the compacted cache
               against the full cache for the step's decode queries (and,
               fidelity_window_query, for the last window row of each head)
@@ -69,9 +72,10 @@ def parse():
 
 
 class Pipeline:
-    def __init__(self, lay: wl.Layer):
+    def __init__(self, lay: wl.Layer, fused: bool = True):
         cfg = lay.cfg
         self.cfg = cfg
+        self.fused = fused
         d = torch.device("cuda:0")
         self.q = lay.q_win.to(d)
         self.k = lay.k.to(d)
@@ -104,6 +108,11 @@ class Pipeline:
     def step(self):
         api.kv_score(self.q, self.k, self.c, scores=self.scores, workspace=self.ws_s)
         api.kv_select(self.scores, self.c, self.budget, kept_idx=self.idx, kept_count=self.cnt)
+        if self.fused:
+            api.kv_compact_decode(self.k, self.v, self.idx, self.cnt, self.cap, self.qd,
+                                  out=self.comp, attn_out=self.out, lse=self.lse,
+                                  workspace=self.ws_d)
+            return
         k_c, v_c, _, off = api.kv_compact(self.k, self.v, self.idx, self.cnt, self.cap,
                                           out=self.comp)
         api.kv_decode_attn(self.qd, k_c, v_c, off, self.cfg.Hkv, out=self.out, lse=self.lse,
@@ -243,6 +252,7 @@ KERNEL_SOURCES = {
     "score_rowstats": ("score.hip", "common.hpp"), "score_colsum": ("score.hip", "common.hpp"),
     "score_fold": ("score.hip", "common.hpp"), "select": ("select.hip", "common.hpp"),
     "compact": ("compact.hip", "common.hpp"), "decode_split": ("decode.hip", "common.hpp"),
+    "compact_decode": ("decode.hip", "common.hpp"),
     "decode_merge": ("decode.hip", "common.hpp"),
 }
 CSRC = os.path.join(ROOT, "kv_cache_compression_score_amd", "csrc")
@@ -366,10 +376,11 @@ def main():
     bytes_sel = 4.0 * th + 4.0 * kept + 4.0 * B * Hkv
     bytes_comp = kept * (4.0 * D * esz + 8.0) + 8.0 * (B * Hkv + 1)
     bytes_dec = 2.0 * kept * D * esz + B * cfg.Hq * D * (esz + 4.0) + 4.0 * B * cfg.Hq
+    # fused: the kept rows are read and written once, plus the queries and outputs
+    bytes_cd = bytes_comp + B * cfg.Hq * D * (esz + 4.0) + 4.0 * B * cfg.Hq
     peak_f = PEAK_TFLOPS[lay.k.dtype]
     work = {"score_rowstats": ("mfma", flop_pass), "score_colsum": ("mfma", flop_pass),
-            "select": ("hbm", bytes_sel), "compact": ("hbm", bytes_comp),
-            "decode_split": ("hbm", bytes_dec)}
+            "select": ("hbm", bytes_sel), "compact_decode": ("hbm", bytes_cd)}
     dom = max(work, key=lambda k: kt.get(k, (0.0,))[0])
     # the host work since the last step leaves the GPU idle long enough for
     # its clocks to drop: settle them again, right before the warmup steps
@@ -386,6 +397,11 @@ def main():
     else:
         achieved, peak, unit = amount / t_dom / 1e9, PEAK_HBM_GBPS, "GB/s"
     t_one = one_pass_score_ms(pipe, args.steps) * 1e-3
+    pipe.fused = False
+    ms_unf, kt_unf = timed_steps(pipe, args.steps)
+    pipe.fused = True
+    t_unf = {k: v[0] * 1e-3 for k, v in kt_unf.items()}
+    t_dec = t_unf["decode_split"] + t_unf["decode_merge"]
     vec = vector_measure(pipe, args.steps)
     # per-step spread, back to back and from cold caches (a 1 GiB buffer
     # overwritten before every step, outside the timed interval)
@@ -401,8 +417,8 @@ def main():
     del buf
     t = {k: v[0] * 1e-3 for k, v in kt.items()}
     t_score = t["score_rowstats"] + t.get("score_fold", 0.0) + t["score_colsum"]   # fold: row LSEs asked for
-    t_dec = t["decode_split"] + t["decode_merge"]
-    t_scd = t["select"] + t["compact"] + t_dec
+    t_cd = t["compact_decode"] + t["decode_merge"]
+    t_scd = t["select"] + t_cd
     res = {
         "metric": METRIC,
         "value": tokens / (ms * 1e-3),
@@ -424,6 +440,11 @@ def main():
                      "traffic": measured_traffic(dom, cfg.name)},
         "copy_gbps": copy_bw,
         "decode_hbm_gbps": bytes_dec / t_dec / 1e9,
+        "unfused": {"ms_per_step_every_launch_timed": ms_unf,
+                    "fused_ms_per_step_every_launch_timed": ms_all,
+                    "compact_ms": t_unf["compact"] * 1e3,
+                    "decode_ms": t_dec * 1e3,
+                    "compact_gbps": bytes_comp / t_unf["compact"] / 1e9},
         "score_stage": {"ms": t_score * 1e3,
                         "algorithmic_tflops": flop_pass / t_score / 1e12,
                         "algorithmic_frac": flop_pass / t_score / 1e12 / peak_f,
@@ -433,9 +454,8 @@ def main():
                            "algorithmic_frac": flop_pass / t_one / 1e12 / peak_f},
         "vector_routing": vec,
         "select_compact_decode": {"ms": t_scd * 1e3,
-                                  "gbps": (bytes_sel + bytes_comp + bytes_dec) / t_scd / 1e9,
-                                  "frac": (bytes_sel + bytes_comp + bytes_dec) / t_scd / 1e9
-                                  / PEAK_HBM_GBPS},
+                                  "gbps": (bytes_sel + bytes_cd) / t_scd / 1e9,
+                                  "frac": (bytes_sel + bytes_cd) / t_scd / 1e9 / PEAK_HBM_GBPS},
         "kernels_ms": {k: v[0] for k, v in kt.items()},
         "step_ms_warm": warm,
         "step_ms_cold": cold,
@@ -458,9 +478,9 @@ def main():
     if not args.no_cpu_baseline:
         log("bench: oracle baseline on the host")
         cb = cpu_baseline(lay, min(args.cpu_seqs, B))
-        gpu_s = {"score": t_score, "select": t["select"], "compact": t["compact"], "decode": t_dec}
-        cb["stage_speedup"] = {k: cb["stage_s"][k] / cb["fraction_of_batch"] / gpu_s[k]
-                               for k in gpu_s}
+        gpu_s = {"score": t_score, "select": t["select"], "compact_decode": t_cd}
+        cpu_s = dict(cb["stage_s"], compact_decode=cb["stage_s"]["compact"] + cb["stage_s"]["decode"])
+        cb["stage_speedup"] = {k: cpu_s[k] / cb["fraction_of_batch"] / gpu_s[k] for k in gpu_s}
         res["cpu_baseline"] = cb
     print(json.dumps(res), flush=True)
 

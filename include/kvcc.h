@@ -232,6 +232,32 @@ int kv_decode_attn(const void* q, const void* k_c, const void* v_c, const int64_
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------
+ * kv_compact_decode - kv_compact and kv_decode_attn in one pass over the
+ * kept rows.
+ *
+ * Decode over the packed cache is bandwidth-bound ("KVzap: Fast, Adaptive,
+ * and Faithful KV Cache Pruning", section 4), and the compaction has just
+ * moved the same rows, so the split kernel gathers each kept row from k / v
+ * through kept_idx, writes it to k_c / v_c (and its token to pos) and feeds
+ * it to the attention in the same visit.  Outputs equal kv_compact followed
+ * by kv_decode_attn over k_c / v_c with capacity_rows (bit for bit): the same
+ * packed cache, offsets, pos, out and lse.  A kept index outside [0, N_max)
+ * leaves its packed row unwritten (as kv_compact) and drops the row from the
+ * attention.
+ *
+ * Arguments as in kv_compact (k, v, kept_idx, kept_count, k_c, v_c, pos,
+ * offsets, capacity_rows) and kv_decode_attn (q [B][Hq][d] dtype, scale,
+ * out, lse); workspace: kv_decode_workspace_size(B, Hq, Hkv, d,
+ * capacity_rows) bytes.  Limits: B*Hkv <= 4096.
+ * ---------------------------------------------------------------------- */
+int kv_compact_decode(const void* k, const void* v, const int32_t* kept_idx,
+                      const int32_t* kept_count, int B, int Hq, int Hkv, int N_max,
+                      int d, int dtype, int64_t capacity_rows, const void* q,
+                      float scale, void* k_c, void* v_c, int32_t* pos,
+                      int64_t* offsets, float* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------------
  * VECTOR three-way routing: retain, approximate or evict.
  *
  * "A Simple Plug-in for Improving Eviction-Based KV Cache Compression"
@@ -306,7 +332,8 @@ int kv_vector_decode(const void* q, const void* k_c, const void* v_c, const int3
  * kernels (or a negative kv_status).  kv_timing_only(name) restricts the
  * recording to launches of that kernel name (one of "score_rowstats",
  * "score_fold" (launched only when row LSEs are requested or pass 1 has
- * more than 16 chunks per head), "score_colsum", "select", "compact", "decode_split",
+ * more than 16 chunks per head), "score_colsum", "select", "compact",
+ * "compact_decode", "decode_split",
  * "decode_merge", "vector_counts", "vector_pool", "vector_residual",
  * "vector_apx", "vector_vmap", "vector_copy", "vector_decode_split",
  * "vector_decode_merge"); NULL or "" records every launch.  The name is copied.

@@ -42,6 +42,10 @@ PROTOTYPES = {
     "kv_decode_attn": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p,
                                c_int, c_int, c_int, c_int, c_int, c_float, c_int64,
                                c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "kv_compact_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_int, c_int, c_int, c_int, c_int, c_int, c_int64,
+                                  c_void_p, c_float, c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "kv_status_string": (ctypes.c_char_p, [c_int]),
     "kv_vector_route_workspace_size": (c_size_t, [c_int, c_int]),
     "kv_vector_route": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,

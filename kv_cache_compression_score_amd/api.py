@@ -184,6 +184,39 @@ def kv_decode_attn(q: torch.Tensor, k_c: torch.Tensor, v_c: torch.Tensor,
     return out, lse
 
 
+def kv_compact_decode(k: torch.Tensor, v: torch.Tensor, kept_idx: torch.Tensor,
+                      kept_count: torch.Tensor, capacity_rows: int, q: torch.Tensor, *,
+                      scale: float = 0.0, out=None, attn_out: Optional[torch.Tensor] = None,
+                      lse: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None):
+    """kv_compact and kv_decode_attn in one pass: (k_c, v_c, pos, offsets, out, lse)."""
+    _check(k, "k"); _check(v, "v"); _check(q, "q")
+    if q.dtype != k.dtype or v.dtype != k.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    B, Hkv, N_max, d = k.shape
+    Hq = q.shape[1]
+    if out is None:
+        k_c = torch.empty(capacity_rows, d, device=k.device, dtype=k.dtype)
+        v_c = torch.empty(capacity_rows, d, device=k.device, dtype=k.dtype)
+        pos = torch.empty(capacity_rows, device=k.device, dtype=torch.int32)
+        offsets = torch.empty(B * Hkv + 1, device=k.device, dtype=torch.int64)
+    else:
+        k_c, v_c, pos, offsets = out
+    if attn_out is None:
+        attn_out = torch.empty(B, Hq, d, device=q.device, dtype=torch.float32)
+    if lse is None:
+        lse = torch.empty(B, Hq, device=q.device, dtype=torch.float32)
+    need = kv_decode_workspace_size(B, Hq, Hkv, d, capacity_rows)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 1), device=q.device, dtype=torch.uint8)
+    _call("kv_compact_decode", lib().kv_compact_decode(
+        _ptr(k), _ptr(v), _ptr(kept_idx), _ptr(kept_count), B, Hq, Hkv, N_max, d,
+        _dtype_code(k), int(capacity_rows), _ptr(q), float(scale), _ptr(k_c), _ptr(v_c),
+        _ptr(pos), _ptr(offsets), _ptr(attn_out), _ptr(lse), _ptr(workspace), workspace.numel(),
+        _stream()))
+    return k_c, v_c, pos, offsets, attn_out, lse
+
+
 # ---- VECTOR three-way routing ------------------------------------------------
 
 def kv_vector_route(scores: torch.Tensor, ctx_len: Optional[torch.Tensor], k: torch.Tensor,

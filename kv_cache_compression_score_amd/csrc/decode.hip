@@ -50,6 +50,18 @@ struct DecodeArgs {
   float rope_base;
   int64_t vcap;
   float* part_u;           // [n_sub][items_max][GT][D]: sum of p * RoPE^-1(k) of rebuilt rows
+  // fused compaction (kv_compact_decode): the offsets are the exclusive scan
+  // of cnt, and row r of head h is token idx[h][r - off[h]] of ksrc / vsrc,
+  // copied to kc_w / vc_w (position to pos_w) as the split kernel reads it
+  const int32_t* cnt;      // [B*Hkv] kept counts (NULL: plain decode over kc / vc)
+  const int32_t* idx;      // [B*Hkv][N_max]
+  const char* ksrc;
+  const char* vsrc;
+  int N_max;
+  char* kc_w;
+  char* vc_w;
+  int32_t* pos_w;
+  int64_t* off_w;          // [B*Hkv+1] the unclipped offsets, written by workgroup 0
 };
 
 // Row offsets clipped to the capacity, and the first item of every head.
@@ -57,9 +69,35 @@ __device__ void build_items(const DecodeArgs& a, long long* off, int* ist, int* 
   const int H = a.B * a.Hkv;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   constexpr int NWV = DT / WAVE;
-  for (int i = tid; i <= H; i += DT) {
-    const long long o = a.offsets[i];
-    off[i] = o < 0 ? 0 : (o > a.cap ? a.cap : o);
+  if (a.cnt) {   // fused compaction: exclusive scan of the kept counts
+    __shared__ long long wl[DT / WAVE];
+    long long carry = 0;
+    for (int base = 0; base < H; base += DT) {
+      const int i = base + tid;
+      const long long c = i < H ? (long long)max(a.cnt[i], 0) : 0ll;
+      const long long inc = wave_incl_scan<long long>(c);
+      if (lane == WAVE - 1) wl[wave] = inc;
+      __syncthreads();
+      long long before = 0, chunk = 0;
+      for (int w = 0; w < NWV; ++w) {
+        if (w < wave) before += wl[w];
+        chunk += wl[w];
+      }
+      if (i < H) off[i] = carry + before + inc - c;
+      carry += chunk;
+      __syncthreads();
+    }
+    if (tid == 0) off[H] = carry;
+    __syncthreads();
+    if (blockIdx.x == 0 && blockIdx.y == 0)
+      for (int i = tid; i <= H; i += DT) a.off_w[i] = off[i];
+    __syncthreads();
+    for (int i = tid; i <= H; i += DT) off[i] = min(off[i], (long long)a.cap);
+  } else {
+    for (int i = tid; i <= H; i += DT) {
+      const long long o = a.offsets[i];
+      off[i] = o < 0 ? 0 : (o > a.cap ? a.cap : o);
+    }
   }
   __syncthreads();
   int carry = 0;
@@ -239,7 +277,10 @@ struct GroupMerge {
   }
 };
 
-template <typename T, int D, int GT>
+// FUSED: the rows come from the full cache through the kept indices and are
+// written to the packed cache on the way (kv_compact_decode); the arithmetic
+// is the same, so the result equals kv_compact followed by kv_decode_attn.
+template <typename T, int D, int GT, bool FUSED>
 __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
   constexpr int EPL = 16 / (int)sizeof(T);     // elements per lane
   constexpr int LPR = D / EPL;                 // lanes per row (power of two, <= 32)
@@ -276,15 +317,49 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
     for (long long base = r0; base < r1; base += PASS) {
       uint4 kr[RPG], vr[RPG];
       bool ok[RPG];
+      if constexpr (FUSED) {
+        int t[RPG];
 #pragma unroll
-      for (int u = 0; u < RPG; ++u) {
-        const long long row = base + grp + (long long)u * NG;
-        ok[u] = row < r1;
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
-        if (ok[u]) {
-          kr[u] = ld16(a.kc + (size_t)row * ROWB + sub * 16);
-          vr[u] = ld16(a.vc + (size_t)row * ROWB + sub * 16);
+        for (int u = 0; u < RPG; ++u) {
+          const long long row = base + grp + (long long)u * NG;
+          const long long r = row - off[head];
+          t[u] = row < r1 && r < a.N_max ? a.idx[(size_t)head * a.N_max + r] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < RPG; ++u) {
+          // an out-of-range index leaves its packed row unwritten (as
+          // kv_compact does) and the row out of the attention
+          ok[u] = (unsigned)t[u] < (unsigned)a.N_max;
+          kr[u] = make_uint4(0, 0, 0, 0);
+          vr[u] = make_uint4(0, 0, 0, 0);
+          if (ok[u]) {
+            const size_t src = ((size_t)head * a.N_max + t[u]) * ROWB + sub * 16;
+            kr[u] = ld16(a.ksrc + src);
+            vr[u] = ld16(a.vsrc + src);
+          }
+        }
+        if (qsub == 0) {
+#pragma unroll
+          for (int u = 0; u < RPG; ++u) {
+            const long long row = base + grp + (long long)u * NG;
+            if (ok[u]) {
+              st16(a.kc_w + (size_t)row * ROWB + sub * 16, kr[u]);
+              st16(a.vc_w + (size_t)row * ROWB + sub * 16, vr[u]);
+            }
+            if (row < r1 && sub == 0) a.pos_w[row] = t[u];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < RPG; ++u) {
+          const long long row = base + grp + (long long)u * NG;
+          ok[u] = row < r1;
+          kr[u] = make_uint4(0, 0, 0, 0);
+          vr[u] = make_uint4(0, 0, 0, 0);
+          if (ok[u]) {
+            kr[u] = ld16(a.kc + (size_t)row * ROWB + sub * 16);
+            vr[u] = ld16(a.vc + (size_t)row * ROWB + sub * 16);
+          }
         }
       }
       float sc[RPG][GT];
@@ -638,7 +713,10 @@ void launch_decode(const DecodeArgs& a, hipStream_t st) {
   if constexpr (VEC) {
     launch("vector_decode_split", vector_decode_split<T, D, GT>, grid, dim3(DT), (uint32_t)dyn, st, a);
   } else {
-    launch("decode_split", decode_split<T, D, GT>, grid, dim3(DT), (uint32_t)dyn, st, a);
+    if (a.cnt)
+      launch("compact_decode", decode_split<T, D, GT, true>, grid, dim3(DT), (uint32_t)dyn, st, a);
+    else
+      launch("decode_split", decode_split<T, D, GT, false>, grid, dim3(DT), (uint32_t)dyn, st, a);
   }
   launch(VEC ? "vector_decode_merge" : "decode_merge", decode_merge<D, GT, VEC>,
          dim3(a.B * a.Hkv, a.n_sub), dim3(GT * D), 0, st, a);
@@ -700,6 +778,8 @@ extern "C" int kv_decode_attn(const void* q, const void* k_c, const void* v_c,
   a.out = out; a.lse = lse;
   a.vmap = nullptr; a.pos = nullptr; a.w = nullptr; a.rope_base = 0.f; a.vcap = 0;
   a.part_u = nullptr;
+  a.cnt = nullptr; a.idx = nullptr; a.ksrc = nullptr; a.vsrc = nullptr; a.N_max = 0;
+  a.kc_w = nullptr; a.vc_w = nullptr; a.pos_w = nullptr; a.off_w = nullptr;
 
   launch_decode_any<false>(a, dtype, d, p.GT, static_cast<hipStream_t>(stream));
   return launch_status();
@@ -742,7 +822,47 @@ extern "C" int kv_vector_decode(const void* q, const void* k_c, const void* v_c,
   a.part_u = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_u);
   a.out = out; a.lse = lse;
   a.vmap = vmap; a.pos = pos; a.w = w; a.rope_base = rope_base; a.vcap = v_capacity_rows;
+  a.cnt = nullptr; a.idx = nullptr; a.ksrc = nullptr; a.vsrc = nullptr; a.N_max = 0;
+  a.kc_w = nullptr; a.vc_w = nullptr; a.pos_w = nullptr; a.off_w = nullptr;
 
   launch_decode_any<true>(a, dtype, d, p.GT, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+extern "C" int kv_compact_decode(const void* k, const void* v, const int32_t* kept_idx,
+                                 const int32_t* kept_count, int B, int Hq, int Hkv, int N_max,
+                                 int d, int dtype, int64_t capacity_rows, const void* q,
+                                 float scale, void* k_c, void* v_c, int32_t* pos,
+                                 int64_t* offsets, float* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!k || !v || !kept_idx || !kept_count || !q || !offsets || !out) return KV_ERR_NULL;
+  if (capacity_rows > 0 && (!k_c || !v_c || !pos)) return KV_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(kept_idx) || !aligned16(kept_count) ||
+      !aligned16(q) || !aligned16(k_c) || !aligned16(v_c) || !aligned16(pos) ||
+      !aligned16(offsets) || !aligned16(out) || !aligned16(lse) || !aligned16(workspace))
+    return KV_ERR_ALIGN;
+  if (dtype != KV_F32 && dtype != KV_BF16) return KV_ERR_DTYPE;
+  if (N_max < 1 || (int64_t)B * Hkv * N_max >= (int64_t(1) << 31)) return KV_ERR_SHAPE;
+  DecodePlan p;
+  if (!plan_decode(B, Hq, Hkv, d, capacity_rows, &p)) return KV_ERR_SHAPE;
+  if (!workspace || workspace_bytes < p.bytes) return KV_ERR_WORKSPACE;
+
+  DecodeArgs a;
+  a.q = q; a.kc = static_cast<const char*>(k_c); a.vc = static_cast<const char*>(v_c);
+  a.offsets = offsets; a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+  a.n_sub = p.n_sub; a.items_max = p.items_max; a.cap = capacity_rows;
+  a.c = (float)((scale > 0.f ? (double)scale : 1.0 / sqrt((double)d)) * LOG2E_D);
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + p.off_ml);
+  a.item_start = reinterpret_cast<int*>(static_cast<char*>(workspace) + p.off_ist);
+  a.out = out; a.lse = lse;
+  a.vmap = nullptr; a.pos = nullptr; a.w = nullptr; a.rope_base = 0.f; a.vcap = 0;
+  a.part_u = nullptr;
+  a.cnt = kept_count; a.idx = kept_idx;
+  a.ksrc = static_cast<const char*>(k); a.vsrc = static_cast<const char*>(v); a.N_max = N_max;
+  a.kc_w = static_cast<char*>(k_c); a.vc_w = static_cast<char*>(v_c);
+  a.pos_w = pos; a.off_w = offsets;
+
+  launch_decode_any<false>(a, dtype, d, p.GT, static_cast<hipStream_t>(stream));
   return launch_status();
 }

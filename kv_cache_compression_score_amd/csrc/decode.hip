@@ -314,17 +314,25 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
     qs.template load<D>(a, b, h, qsub, sub);
     RowState<GT, EPL> st;
     st.reset();
+    // fused: the kept indices of a pass are loaded while the previous pass's
+    // rows are in flight
+    int tn[RPG];
+    auto load_idx = [&](long long base) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < RPG; ++u) {
+        const long long row = base + grp + (long long)u * NG;
+        const long long r = row - off[head];
+        tn[u] = row < r1 && r < a.N_max ? a.idx[(size_t)head * a.N_max + r] : -1;
+      }
+    };
+    if constexpr (FUSED) load_idx(r0);
     for (long long base = r0; base < r1; base += PASS) {
       uint4 kr[RPG], vr[RPG];
       bool ok[RPG];
       if constexpr (FUSED) {
         int t[RPG];
 #pragma unroll
-        for (int u = 0; u < RPG; ++u) {
-          const long long row = base + grp + (long long)u * NG;
-          const long long r = row - off[head];
-          t[u] = row < r1 && r < a.N_max ? a.idx[(size_t)head * a.N_max + r] : -1;
-        }
+        for (int u = 0; u < RPG; ++u) t[u] = tn[u];
 #pragma unroll
         for (int u = 0; u < RPG; ++u) {
           // an out-of-range index leaves its packed row unwritten (as
@@ -338,6 +346,7 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
             vr[u] = ld16(a.vsrc + src);
           }
         }
+        if (base + PASS < r1) load_idx(base + PASS);
         if (qsub == 0) {
 #pragma unroll
           for (int u = 0; u < RPG; ++u) {

@@ -86,3 +86,32 @@ def test_compact_decode_no_rows():
     assert torch.equal(off.cpu(), torch.zeros(B * Hkv + 1, dtype=torch.int64))
     assert torch.count_nonzero(out).item() == 0
     assert torch.all(torch.isneginf(lse)).item()
+
+
+def test_compact_decode_out_of_range_index_is_dropped():
+    # A kept index outside [0, N_max) keeps its slot (pos records it), its
+    # packed row is not written, and the attention leaves the row out.
+    B, Hq, Hkv, N, d = 1, 4, 2, 300, 128
+    g = torch.Generator().manual_seed(43)
+    k = torch.randn(B, Hkv, N, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, N, d, generator=g).to(torch.bfloat16)
+    q = torch.randn(B, Hq, d, generator=g).to(torch.bfloat16)
+    idx = torch.zeros(B, Hkv, N, dtype=torch.int32)
+    rows = [np.array([3, 50, 70, 299]), np.array([0, 10, 20, 30, 40])]
+    for h, r in enumerate(rows):
+        idx[0, h, :len(r)] = torch.from_numpy(r.astype(np.int32))
+    idx[0, 1, 2] = N   # out of range: the third kept row of head 1
+    cnt = torch.tensor([[len(rows[0]), len(rows[1])]], dtype=torch.int32)
+    fk, fv, fpos, foff, fout, flse = api.kv_compact_decode(dev(k), dev(v), dev(idx), dev(cnt), 9,
+                                                            dev(q))
+    torch.cuda.synchronize()
+    assert foff.cpu().tolist() == [0, 4, 9]
+    assert fpos.cpu().tolist()[4:9] == [0, 10, N, 30, 40]
+    assert torch.equal(fk[:4].cpu(), k[0, 0, rows[0]])
+    # the oracle over the valid rows only
+    keep1 = np.array([0, 10, 30, 40])
+    k_ref = torch.cat([k[0, 0, rows[0]], k[0, 1, keep1]])
+    v_ref = torch.cat([v[0, 0, rows[0]], v[0, 1, keep1]])
+    o_ref, l_ref = orc.decode(q, k_ref, v_ref, np.array([0, 4, 8]), Hkv)
+    np.testing.assert_allclose(fout.cpu().numpy(), o_ref, atol=1e-2, rtol=0)
+    np.testing.assert_allclose(flse.cpu().numpy(), l_ref, atol=1e-2, rtol=0)

@@ -193,7 +193,10 @@ int kv_select(const float* scores, const int32_t* ctx_len,
  *   pos[offsets[i] + r] = kept_idx[b,h,r]          (original token index)
  *
  * k, v          [B][Hkv][N_max][d] dtype
- * kept_idx, kept_count as produced by kv_select (indices must be < N_max)
+ * kept_idx, kept_count as produced by kv_select.  A kept index outside
+ *               [0, N_max) (or a count above N_max) packs a zero K row and
+ *               a zero V row; its pos entry holds the index as given (-1
+ *               past N_max entries).
  * k_c, v_c      [capacity_rows][d] dtype out
  * pos           [capacity_rows] int32 out
  * offsets       [B*Hkv + 1] int64 out; always the true prefix sums
@@ -241,9 +244,9 @@ int kv_decode_attn(const void* q, const void* k_c, const void* v_c, const int64_
  * through kept_idx, writes it to k_c / v_c (and its token to pos) and feeds
  * it to the attention in the same visit.  Outputs equal kv_compact followed
  * by kv_decode_attn over k_c / v_c with capacity_rows (bit for bit): the same
- * packed cache, offsets, pos, out and lse.  A kept index outside [0, N_max)
- * leaves its packed row unwritten (as kv_compact) and drops the row from the
- * attention.
+ * packed cache, offsets, pos, out and lse, also for a kept index outside
+ * [0, N_max), which packs a zero K/V row (as kv_compact) that the attention
+ * reads like any other row.
  *
  * Arguments as in kv_compact (k, v, kept_idx, kept_count, k_c, v_c, pos,
  * offsets, capacity_rows) and kv_decode_attn (q [B][Hq][d] dtype, scale,

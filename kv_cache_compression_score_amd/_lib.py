@@ -6,7 +6,10 @@ import os
 
 from ctypes import c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvcc.so")
+# KVCC_LIBRARY names another build of the same ABI (e.g. the host-side
+# sanitizer build that the validation tests run against).
+LIB_PATH = os.environ.get("KVCC_LIBRARY") or \
+    os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvcc.so")
 
 KV_F32 = 0
 KV_BF16 = 1

@@ -82,13 +82,42 @@ def kv_score_workspace_size(B, Hq, Hkv, N_max, W, d) -> int:
     return int(lib().kv_score_workspace_size(B, Hq, Hkv, N_max, W, d))
 
 
+def _check_lengths(ctx_len, ctx_len_host, B: int, N_max: int, W: int, causal: bool):
+    """Per-sequence preconditions the library cannot check on the host:
+    0 <= n_b <= N_max, and W <= n_b when the window is causal (its rows sit
+    at the last W positions).  Uses ctx_len_host when given; otherwise a
+    causal call reads the device lengths back (one synchronisation)."""
+    if ctx_len is None:
+        if causal and W > N_max:
+            raise ValueError(f"causal scoring needs W <= n_b (W={W}, N_max={N_max})")
+        return
+    if ctx_len_host is None:
+        if not causal:
+            return
+        ctx_len_host = ctx_len.cpu()
+    n = [int(x) for x in (ctx_len_host.tolist() if hasattr(ctx_len_host, "tolist")
+                          else ctx_len_host)]
+    if len(n) != B:
+        raise ValueError(f"ctx_len has {len(n)} entries, expected {B}")
+    for b, nb in enumerate(n):
+        if not 0 <= nb <= N_max:
+            raise ValueError(f"ctx_len[{b}] = {nb} outside [0, {N_max}]")
+        if causal and nb < W:
+            raise ValueError(f"causal scoring needs W <= n_b: ctx_len[{b}] = {nb} < W = {W}")
+
+
 def kv_score(q_win: torch.Tensor, k: torch.Tensor, ctx_len: Optional[torch.Tensor] = None, *,
              scale: float = 0.0, causal: bool = False, with_row_lse: bool = False,
-             scores: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
-    """Window scores [B][Hkv][N_max] fp32 (and row LSE [B][Hq][W] if asked)."""
+             scores: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+             ctx_len_host=None):
+    """Window scores [B][Hkv][N_max] fp32 (and row LSE [B][Hq][W] if asked).
+
+    ctx_len_host (host sequence of the B lengths) lets the binding check the
+    per-sequence limits without reading ctx_len back."""
     _check(q_win, "q_win"); _check(k, "k")
     B, Hq, W, d = q_win.shape
     _, Hkv, N_max, _ = k.shape
+    _check_lengths(ctx_len, ctx_len_host, B, N_max, W, causal)
     if scores is None:
         scores = torch.empty(B, Hkv, N_max, device=k.device, dtype=torch.float32)
     row_lse = torch.empty(B, Hq, W, device=k.device, dtype=torch.float32) if with_row_lse else None
@@ -106,11 +135,12 @@ def kv_score(q_win: torch.Tensor, k: torch.Tensor, ctx_len: Optional[torch.Tenso
 
 def kv_score_from_lse(q_win: torch.Tensor, k: torch.Tensor, ctx_len: Optional[torch.Tensor],
                       row_lse_in: torch.Tensor, *, scale: float = 0.0, causal: bool = False,
-                      scores: Optional[torch.Tensor] = None):
+                      scores: Optional[torch.Tensor] = None, ctx_len_host=None):
     """Window scores [B][Hkv][N_max] fp32 in one sweep, given the row LSE [B][Hq][W]."""
     _check(q_win, "q_win"); _check(k, "k"); _check(row_lse_in, "row_lse_in")
     B, Hq, W, d = q_win.shape
     _, Hkv, N_max, _ = k.shape
+    _check_lengths(ctx_len, ctx_len_host, B, N_max, W, causal)
     if row_lse_in.dtype != torch.float32 or tuple(row_lse_in.shape) != (B, Hq, W):
         raise ValueError("row_lse_in must be fp32 [B][Hq][W]")
     if scores is None:

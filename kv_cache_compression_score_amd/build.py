@@ -63,5 +63,49 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-checking build: the same library with AddressSanitizer and
+# UndefinedBehaviorSanitizer on its host code only (argument validation,
+# workspace planning, launch set-up); the device code is built as usual.
+SAN_DIR = os.path.join(BUILD, "sanitized")
+SAN_LIB = os.path.join(SAN_DIR, "libkvcc_sanitized.so")
+SAN_FLAGS = FLAGS + ["-g", "-Xarch_host", "-fsanitize=address,undefined",
+                     "-Xarch_host", "-fno-sanitize-recover=undefined",
+                     "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def sanitizer_runtime() -> str:
+    """Path of the clang ASan runtime (it also carries the UBSan handlers),
+    to be preloaded into a process that loads the sanitized library."""
+    pat = os.path.join(os.path.dirname(os.path.dirname(_hipcc())), "llvm", "lib", "clang", "*",
+                       "lib", "linux", "libclang_rt.asan-x86_64.so")
+    found = sorted(glob.glob(pat))
+    if not found:
+        raise RuntimeError(f"no ASan runtime at {pat}")
+    return found[-1]
+
+
+def build_sanitized(force: bool = False) -> str:
+    """Build the host-checking library (reused while it is newer than every
+    source, header and this script, unless force)."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    deps = srcs + glob.glob(os.path.join(CSRC, "*.hpp")) + \
+        glob.glob(os.path.join(INCLUDE, "*.h")) + [os.path.abspath(__file__)]
+    if not force and os.path.exists(SAN_LIB) and \
+            os.path.getmtime(SAN_LIB) > max(os.path.getmtime(p) for p in deps):
+        return SAN_LIB
+    objs = [os.path.join(SAN_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    with cf.ThreadPoolExecutor(min(len(srcs), 8)) as ex:
+        for f in [ex.submit(_run, [_hipcc(), *SAN_FLAGS, *EXTRA.get(os.path.basename(s), []),
+                                   "-c", s, "-o", o]) for s, o in zip(srcs, objs)]:
+            f.result()
+    _run([_hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Xarch_host",
+          "-fsanitize=address,undefined", "-o", SAN_LIB, *objs])
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitized" in sys.argv:
+        print(build_sanitized())
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -10,7 +10,8 @@
 // walks the flat space of output rows grid-stride; a row finds its head by
 // binary search over the offsets.  A group of d*sizeof(T)/16 lanes copies
 // one row with 16-byte loads and stores, so a wave moves whole rows and the
-// copy is bit-exact.  Output rows at or past the capacity are skipped.
+// copy is bit-exact.  Output rows at or past the capacity are skipped; a
+// kept index outside [0, N_max) packs a zero K/V row (its pos holds the index).
 #include "common.hpp"
 
 namespace kvcc {
@@ -90,6 +91,8 @@ __global__ __launch_bounds__(CT) void compact_kernel(CompactArgs a) {
         const int head = find_head(off, H, row);
         const long long r = row - off[head];
         const int t = r < a.N_max ? a.idx[(size_t)head * a.N_max + r] : -1;
+        kb[u] = make_uint4(0, 0, 0, 0);   // an index outside [0, N_max): zero row
+        vb[u] = make_uint4(0, 0, 0, 0);
         if ((unsigned)t < (unsigned)a.N_max) {
           const size_t src = ((size_t)head * a.N_max + t) * a.rowb + sub * 16;
           kb[u] = ld16(a.k + src);
@@ -102,11 +105,9 @@ __global__ __launch_bounds__(CT) void compact_kernel(CompactArgs a) {
     for (int u = 0; u < RU; ++u) {
       const long long row = r0 + (long long)u * rpi;
       if (row < total) {
-        if ((unsigned)tt[u] < (unsigned)a.N_max) {
-          const size_t dst = (size_t)row * a.rowb + sub * 16;
-          st16(a.kc + dst, kb[u]);
-          st16(a.vc + dst, vb[u]);
-        }
+        const size_t dst = (size_t)row * a.rowb + sub * 16;
+        st16(a.kc + dst, kb[u]);
+        st16(a.vc + dst, vb[u]);
         if (sub == 0) a.pos[row] = tt[u];
       }
     }

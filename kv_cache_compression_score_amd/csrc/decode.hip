@@ -335,12 +335,12 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
         for (int u = 0; u < RPG; ++u) t[u] = tn[u];
 #pragma unroll
         for (int u = 0; u < RPG; ++u) {
-          // an out-of-range index leaves its packed row unwritten (as
-          // kv_compact does) and the row out of the attention
-          ok[u] = (unsigned)t[u] < (unsigned)a.N_max;
+          // an index outside [0, N_max) packs a zero K/V row (as kv_compact
+          // does), which the attention then reads like any other row
+          ok[u] = base + grp + (long long)u * NG < r1;
           kr[u] = make_uint4(0, 0, 0, 0);
           vr[u] = make_uint4(0, 0, 0, 0);
-          if (ok[u]) {
+          if ((unsigned)t[u] < (unsigned)a.N_max) {
             const size_t src = ((size_t)head * a.N_max + t[u]) * ROWB + sub * 16;
             kr[u] = ld16(a.ksrc + src);
             vr[u] = ld16(a.vsrc + src);
@@ -354,8 +354,8 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
             if (ok[u]) {
               st16(a.kc_w + (size_t)row * ROWB + sub * 16, kr[u]);
               st16(a.vc_w + (size_t)row * ROWB + sub * 16, vr[u]);
+              if (sub == 0) a.pos_w[row] = t[u];
             }
-            if (row < r1 && sub == 0) a.pos_w[row] = t[u];
           }
         }
       } else {

@@ -30,6 +30,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -717,32 +718,36 @@ bool plan_score(int B, int Hq, int Hkv, int N_max, int W, int d, ScorePlan* p) {
   return true;
 }
 
-// Resident workgroups of a kernel on the current device (cached per kernel).
+// Resident workgroups of a kernel on the current device, cached per kernel
+// and device.  Threads that race on a first call compute the same value and
+// store it atomically, so the cache needs no lock.
+constexpr int MAX_DEVICES = 64;
 template <typename K>
-int64_t resident_slots(K kernel, int threads, int* cache) {
-  if (*cache > 0) return *cache;
+int resident_slots(K kernel, int threads, std::atomic<int>* cache) {
   int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return SLOTS_1;
+  const int c = cache[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
       cus < 1 || per_cu < 1)
     return SLOTS_1;
-  *cache = cus * per_cu;
-  return *cache;
+  cache[dev].store(cus * per_cu, std::memory_order_relaxed);
+  return cus * per_cu;
 }
 
 template <typename T, int D, int NW>
 void launch_score(ScoreArgs a, hipStream_t st) {
-  static int slots2 = 0;
-  a.TC2 = chunk_tokens((int64_t)a.B * a.Hkv, a.N_max,
-                       resident_slots(score_pass<T, D, NW, 2>, NW * WAVE, &slots2), 4);
+  static std::atomic<int> slots_cache[MAX_DEVICES];   // zero: not yet known
+  const int slots2 = resident_slots(score_pass<T, D, NW, 2>, NW * WAVE, slots_cache);
+  a.TC2 = chunk_tokens((int64_t)a.B * a.Hkv, a.N_max, slots2, 4);
   a.n_chunks2 = ceil_div(a.N_max, a.TC2);
   const dim3 grid1(a.n_chunks, a.Hkv, a.B);
   dim3 grid2(a.n_chunks2, a.Hkv, a.B);
   // Balanced pass-2 ranges (two-pass path): one workgroup per resident slot,
   // at least two per head; pass 1 writes the table
   const int H = a.B * a.Hkv;
-  a.G2 = std::min(slots2 > 0 ? slots2 : SLOTS_1, TAB_MAX);
+  a.G2 = std::min(slots2, TAB_MAX);
   a.ranges = a.tab && !a.lse_in && H <= RANGE_HEADS && 2 * H <= a.G2 ? 1 : 0;
   if (a.ranges) grid2 = dim3((unsigned)a.G2, 1, 1);
   a.self_merge = a.n_chunks <= SELF_MERGE ? 1 : 0;

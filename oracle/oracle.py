@@ -184,6 +184,33 @@ def total_order(s: np.ndarray, protected=None) -> np.ndarray:
     return np.lexsort((idx, np.where(p, 0.0, -s), (~p).astype(np.int8)))
 
 
+def exact_prefix_sums(values):
+    """Exact prefix sums of float values, as Python integers in units of
+    2^-1074 (every finite double is an integer multiple of it), so the
+    mass budget's C(k) is the true sum of the first k scores with no
+    rounding at all."""
+    out = []
+    acc = 0
+    for x in np.asarray(values, dtype=np.float64).tolist():
+        num, den = x.as_integer_ratio()            # den = 2^m, m <= 1074
+        acc += num << (1074 - den.bit_length() + 1)
+        out.append(acc)
+    return out
+
+
+def mass_count(s_ordered, f: float) -> int:
+    """Fewest k >= 1 with C(k) >= f * C(n), C(k) the exact sum of the first k
+    entries of s_ordered and f the fp32 fraction (an exact dyadic rational);
+    n when no shorter prefix reaches it."""
+    c = exact_prefix_sums(s_ordered)
+    num, den = float(np.float32(f)).as_integer_ratio()
+    target = num * c[-1]                           # compare C(k) * den >= num * C(n)
+    for k, ck in enumerate(c, start=1):
+        if ck * den >= target:
+            return k
+    return len(c)
+
+
 def _round_half_up(x: float) -> int:
     return int(math.floor(x + 0.5))
 
@@ -204,8 +231,9 @@ def budget_count(s, mode: int, *, k=None, ratio=None, tau=None, mass=None,
                       to [max(1, round(min_ratio*n)), round(max_ratio*n)]
     BUDGET_MASS:      fewest k >= 1 whose first-k score sum C(k) in the
                       total order (protected tokens first, with their real
-                      scores) reaches f*C(n) (f fp32; float64 sums), then the
-                      same clamp as the threshold mode
+                      scores) reaches f*C(n) (f fp32; sums and the comparison
+                      exact, see ``mass_count``), then the same clamp as the
+                      threshold mode
     Protected tokens count toward k and are always kept: the result is at
     least their number.
     """
@@ -227,11 +255,7 @@ def budget_count(s, mode: int, *, k=None, ratio=None, tau=None, mass=None,
         kk = min(max(cnt, lo), hi)
     elif mode == BUDGET_MASS:
         lo, hi = _clamp_bounds(n, min_ratio, max_ratio)
-        f = float(np.float32(mass))
-        c = np.cumsum(s[total_order(s, p)])
-        target = f * c[-1]
-        kk = int(np.searchsorted(c, target, side="left")) + 1
-        kk = min(kk, n)
+        kk = mass_count(s[total_order(s, p)], mass)
         kk = min(max(kk, lo), hi)
     else:
         raise ValueError(f"unknown budget mode {mode}")

@@ -8,7 +8,9 @@ Tolerances:
   fp32 scores); end to end: they may differ only on tokens whose oracle score
   lies within 1e-5 relative of the k-th oracle score (plus the same floor);
 * gathered K/V, positions, counts and offsets: bit-exact;
-* decode: out within 1e-2 absolute, lse within 1e-3 absolute.
+* decode: out within 1e-2 absolute, lse within 1e-3 absolute;
+* mass-budget counts: a GPU count may differ from the oracle's only if it
+  brackets f * C(n) to within a band on exact sums (``mass_count_ok``).
 """
 from __future__ import annotations
 
@@ -17,6 +19,8 @@ import sys
 
 import numpy as np
 import torch
+
+from fractions import Fraction
 
 from oracle import oracle as orc
 
@@ -110,3 +114,51 @@ def bits(t: torch.Tensor) -> np.ndarray:
 
 def ratio_k(n: int, r: float) -> int:
     return min(max(int(math.floor(float(np.float32(r)) * n + 0.5)), 1), n)
+
+
+# The mass budget's count band, relative to the head's total C(n).  The GPU
+# sums scores in 64-bit fixed point at 2^(61 - floor(log2 C(n))): each score
+# is truncated by less than 2^-61 C(n), so its C(k) falls short of the exact
+# sum by less than k 2^-61 C(n), and its target ceil(f * total) (double
+# products) is off by less than 2^-51 C(n).  Its count therefore brackets
+# f * C(n) on exact sums to within (2 n 2^-61 + 2^-50) C(n) < 1.2e-13 C(n)
+# for n <= 2^17; 1e-12 covers that.
+MASS_BAND = 1e-12
+
+
+def mass_count_range(s_head, f, lo, hi, band, prot=None):
+    """The counts a mass budget may return for one head when C(k) is known to
+    within band * C(n): every clamp of a k with C(k) >= f C(n) - band C(n) and
+    C(k - 1) < f C(n) + band C(n), C the exact prefix sums of the scores in
+    the total order (protected tokens first).  Returns (k_min, k_max); the
+    clamp of a monotone interval is the interval of the clamped ends."""
+    s_head = np.asarray(s_head, dtype=np.float64)
+    n = len(s_head)
+    c = orc.exact_prefix_sums(s_head[orc.total_order(s_head, prot)])
+    total = Fraction(c[-1])
+    target = Fraction(float(np.float32(f))) * total
+    slack = Fraction(band) * total
+    k_a = next(k for k in range(1, n + 1) if c[k - 1] >= target - slack)
+    k_b = max(k for k in range(1, n + 1) if k == 1 or c[k - 2] < target + slack)
+    n_prot = 0 if prot is None else int(np.count_nonzero(prot))
+    k_lo = max(1, int(np.floor(np.float32(lo) * n + 0.5)))
+    k_hi = min(n, max(1, int(np.floor(np.float32(hi) * n + 0.5))))
+    k_lo = min(k_lo, k_hi)
+    clamp = lambda k: min(max(min(max(k, k_lo), k_hi), n_prot), n)
+    return clamp(k_a), clamp(k_b)
+
+
+def mass_count_ok(s_head, k_g, f, lo, hi, band=MASS_BAND, prot=None):
+    k_min, k_max = mass_count_range(s_head, f, lo, hi, band, prot)
+    return k_min <= k_g <= k_max
+
+
+def mass_between(s_head, k1, k2, prot=None):
+    """Exact score mass of the tokens ranked between two counts, relative to
+    the head's total."""
+    s_head = np.asarray(s_head, dtype=np.float64)
+    c = orc.exact_prefix_sums(s_head[orc.total_order(s_head, prot)])
+    a, b = sorted((k1, k2))
+    if a == b or c[-1] == 0:
+        return 0.0
+    return float(Fraction(c[b - 1] - (c[a - 1] if a > 0 else 0), c[-1]))

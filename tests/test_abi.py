@@ -157,3 +157,20 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         _lib.lib()
+
+
+def test_binding_checks_sequence_lengths():
+    # The per-sequence limits the library cannot see on the host: the binding
+    # checks 0 <= n_b <= N_max, and W <= n_b for a causal window.
+    import torch
+    from kv_cache_compression_score_amd.api import _check_lengths
+    _check_lengths(None, None, 2, 64, 8, True)
+    _check_lengths(torch.tensor([64, 8], dtype=torch.int32), None, 2, 64, 8, True)
+    _check_lengths(torch.tensor([64, 3], dtype=torch.int32), None, 2, 64, 8, False)
+    for bad, causal in (([64, 7], True), ([65, 8], False), ([-1, 8], False), ([8], False)):
+        with pytest.raises(ValueError):
+            _check_lengths(torch.tensor([9, 9], dtype=torch.int32), bad, 2, 64, 8, causal)
+    with pytest.raises(ValueError):
+        _check_lengths(torch.tensor([64, 7], dtype=torch.int32), None, 2, 64, 8, True)
+    with pytest.raises(ValueError):
+        _check_lengths(None, None, 1, 16, 32, True)

@@ -9,7 +9,7 @@ from kv_cache_compression_score_amd import api
 from kv_cache_compression_score_amd import workloads as wl
 from oracle import oracle as orc
 
-from gpu_helpers import dev, log
+from gpu_helpers import MASS_BAND, dev, log, mass_between, mass_count_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -100,31 +100,6 @@ def test_select_threshold(kind, shape):
         compare_sets(idx_g, cnt_g, idx_r, cnt_r)
 
 
-def mass_count_ok(s_head, k_g, f, lo, hi, prot=None):
-    """A GPU count that differs from the oracle's is accepted only if it is the
-    clamp of a count that brackets f * C(n) to within 1e-12 * C(n) on the
-    oracle's float64 sums, C(k) the sum of the first k scores in the total
-    order (protected tokens first).  Raising k to the protected count makes
-    the clamp [max(lo, |P|), max(hi, |P|)]."""
-    c = np.cumsum(s_head[orc.total_order(s_head, prot)])
-    target = float(np.float32(f)) * c[-1]
-    band = 1e-12 * c[-1]
-    n = len(s_head)
-    n_prot = 0 if prot is None else int(np.count_nonzero(prot))
-    k_lo = max(1, int(np.floor(np.float32(lo) * n + 0.5)))
-    k_hi = min(n, max(1, int(np.floor(np.float32(hi) * n + 0.5))))
-    k_lo, k_hi = max(min(k_lo, k_hi), n_prot), max(k_hi, n_prot)
-    reaches = lambda k: c[k - 1] >= target - band          # C(k) reaches the target
-    short = lambda k: k == 1 or c[k - 2] < target + band   # C(k-1) does not (within band)
-    if k_lo < k_g < k_hi:
-        return reaches(k_g) and short(k_g)
-    if k_g == k_hi:
-        return short(k_g)          # the crossing lies at or beyond the upper clamp
-    if k_g == k_lo:
-        return reaches(k_g)        # the crossing lies at or below the lower clamp
-    return False
-
-
 @pytest.mark.parametrize("kind", ["ties", "heavy", "uniform"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"B{s[0]}H{s[1]}N{s[2]}")
 def test_select_mass(kind, shape):
@@ -134,16 +109,23 @@ def test_select_mass(kind, shape):
         b = api.Budget(api.BUDGET_MASS, mass=f, min_ratio=lo, max_ratio=hi)
         idx_g, cnt_g = run_select(s, ctx, b)
         idx_r, cnt_r = orc.select(s, ctx, orc.BUDGET_MASS, mass=f, min_ratio=lo, max_ratio=hi)
+        worst_dk, worst_mass = 0, 0.0
         for bb in range(B):
             for h in range(Hkv):
                 i = bb * Hkv + h
                 kg, kr = int(cnt_g[i]), int(cnt_r[i])
+                sh = s[bb, h, :ctx[bb]].astype(np.float64)
                 if kg != kr:
-                    n = ctx[bb]
-                    assert mass_count_ok(s[bb, h, :n].astype(np.float64), kg, f, lo, hi), \
-                        (bb, h, kg, kr)
-                ref = np.sort(orc.total_order(s[bb, h, :ctx[bb]].astype(np.float64))[:kg])
+                    # the counts may differ only where the exact prefix sums
+                    # stay within the fixed-point band of f * C(n)
+                    assert mass_count_ok(sh, kg, f, lo, hi), (bb, h, kg, kr)
+                    worst_dk = max(worst_dk, abs(kg - kr))
+                    worst_mass = max(worst_mass, mass_between(sh, kg, kr))
+                    assert worst_mass <= 2 * MASS_BAND, (bb, h, kg, kr, worst_mass)
+                ref = np.sort(orc.total_order(sh)[:kg])
                 assert np.array_equal(idx_g[bb, h, :kg], ref), (bb, h)
+        log(f"mass {kind} {shape[:3]} f={f}: max |k_gpu - k_oracle| {worst_dk}, "
+            f"mass between them {worst_mass:.1e} of the total")
 
 
 def test_select_on_real_scores_and_determinism():
@@ -201,7 +183,8 @@ def test_select_protected(kind, shape):
                     kg, kr = int(cnt_g[i]), int(cnt_r[i])
                     sh = s[bb, h, :n].astype(np.float64)
                     if kg != kr:
-                        assert mass_count_ok(sh, kg, f, lo, hi, prot), (bb, h, kg, kr)
+                        assert mass_count_ok(sh, kg, f, lo, hi, prot=prot), (bb, h, kg, kr)
+                        assert mass_between(sh, kg, kr, prot) <= 2 * MASS_BAND, (bb, h)
                     ref = np.sort(orc.total_order(sh, prot)[:kg])
                     assert np.array_equal(idx_g[bb, h, :kg], ref), (bb, h)
                     assert set(np.flatnonzero(prot)) <= set(idx_g[bb, h, :kg].tolist())

@@ -89,6 +89,28 @@ def test_mass_budget_bracket_and_brute_force(seed):
         assert math.fsum(top[:k - 1]) < ff * total + 1e-12
 
 
+def test_exact_prefix_sums_match_correctly_rounded_sums():
+    # each exact prefix, rounded once, is the correctly rounded sum (fsum)
+    from fractions import Fraction
+    rng = np.random.default_rng(3)
+    s = np.exp(rng.standard_normal(200) * 20)           # magnitudes over ~17 decades
+    c = orc.exact_prefix_sums(s)
+    for k in (1, 2, 17, 100, 200):
+        assert float(Fraction(c[k - 1], 2 ** 1074)) == math.fsum(s[:k])
+    assert orc.exact_prefix_sums([5e-324, 5e-324]) == [1, 2]   # the smallest subnormal is one unit
+
+
+def test_mass_budget_counts_a_flat_tail_exactly():
+    # f = 1 needs every positive score: closed form k = #positive.  The tail
+    # scores sit far below one ulp of the running sum, where a float64
+    # cumulative sum stops growing (it would return k = 1).
+    s = np.concatenate([[1.0], np.full(50, 1e-20), np.zeros(10)])
+    assert orc.budget_count(s, orc.BUDGET_MASS, mass=1.0) == 51
+    assert np.cumsum(s)[0] == np.cumsum(s)[-1]           # the float64 cumsum is saturated
+    # any fraction below 1 is reached by the head token alone
+    assert orc.budget_count(s, orc.BUDGET_MASS, mass=float(np.float32(1.0 - 1e-7))) == 1
+
+
 def test_per_head_ctx_and_arrays():
     s = np.random.default_rng(0).random((2, 2, 12))
     kept, cnt = orc.select(s, [12, 5], orc.BUDGET_RATIO, ratio=[0.5, 0.25, 1.0, 0.5])

@@ -235,6 +235,27 @@ int kv_decode_attn(const void* q, const void* k_c, const void* v_c, const int64_
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------
+ * kv_decode_attn_noalloc - kv_decode_attn for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument and no
+ * allocation of any kind; the split partials go to a scratch array the
+ * library holds per GPU (16 MiB, kept until the process ends).
+ *
+ * Arguments, results and errors as kv_decode_attn.  KV_ERR_WORKSPACE: the
+ * call needs more than the scratch holds, i.e.
+ * kv_decode_workspace_size(B, Hq, Hkv, d, capacity_rows) > 16 MiB (about
+ * 2 million capacity rows at B*Hkv = 128, G = 4, d = 128).  KV_ERR_LAUNCH:
+ * the scratch address could not be looked up on the current device.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents (nothing in it needs clearing): calls that overlap in
+ * time on one GPU (e.g. on two streams) race and give wrong results.
+ * ---------------------------------------------------------------------- */
+int kv_decode_attn_noalloc(const void* q, const void* k_c, const void* v_c,
+                           const int64_t* offsets, int B, int Hq, int Hkv, int d, int dtype,
+                           float scale, int64_t capacity_rows, float* out, float* lse,
+                           void* stream);
+
+/* ----------------------------------------------------------------------
  * kv_compact_decode - kv_compact and kv_decode_attn in one pass over the
  * kept rows.
  *

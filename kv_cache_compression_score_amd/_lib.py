@@ -45,6 +45,9 @@ PROTOTYPES = {
     "kv_decode_attn": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p,
                                c_int, c_int, c_int, c_int, c_int, c_float, c_int64,
                                c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "kv_decode_attn_noalloc": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_int, c_int, c_int, c_int, c_int, c_float, c_int64,
+                                       c_void_p, c_void_p, c_void_p]),
     "kv_compact_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_int, c_int, c_int, c_int, c_int, c_int, c_int64,
                                   c_void_p, c_float, c_void_p, c_void_p, c_void_p, c_void_p,

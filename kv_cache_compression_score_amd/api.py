@@ -214,6 +214,25 @@ def kv_decode_attn(q: torch.Tensor, k_c: torch.Tensor, v_c: torch.Tensor,
     return out, lse
 
 
+def kv_decode_attn_noalloc(q: torch.Tensor, k_c: torch.Tensor, v_c: torch.Tensor,
+                           offsets: torch.Tensor, Hkv: int, out: torch.Tensor,
+                           lse: torch.Tensor, *, scale: float = 0.0):
+    """kv_decode_attn with no workspace and no allocation: the caller passes
+    out [B][Hq][d] fp32 and lse [B][Hq] fp32; the library's per-GPU scratch
+    holds the partials (calls overlapping on one GPU race)."""
+    for t, name in ((q, "q"), (k_c, "k_c"), (v_c, "v_c"), (offsets, "offsets"), (out, "out"),
+                    (lse, "lse")):
+        _check(t, name)
+    B, Hq, d = q.shape
+    if tuple(out.shape) != (B, Hq, d) or tuple(lse.shape) != (B, Hq) or \
+            out.dtype != torch.float32 or lse.dtype != torch.float32:
+        raise ValueError("out must be fp32 [B][Hq][d] and lse fp32 [B][Hq]")
+    _call("kv_decode_attn_noalloc", lib().kv_decode_attn_noalloc(
+        _ptr(q), _ptr(k_c), _ptr(v_c), _ptr(offsets), B, Hq, Hkv, d, _dtype_code(q),
+        float(scale), k_c.shape[0], _ptr(out), _ptr(lse), _stream()))
+    return out, lse
+
+
 def kv_compact_decode(k: torch.Tensor, v: torch.Tensor, kept_idx: torch.Tensor,
                       kept_count: torch.Tensor, capacity_rows: int, q: torch.Tensor, *,
                       scale: float = 0.0, out=None, attn_out: Optional[torch.Tensor] = None,

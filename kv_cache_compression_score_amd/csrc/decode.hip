@@ -19,6 +19,8 @@
 // rebuilt list, and the merge adds W_h times the rebuilt rows' sum.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.hpp"
 
 namespace kvcc {
@@ -792,6 +794,53 @@ extern "C" int kv_decode_attn(const void* q, const void* k_c, const void* v_c,
 
   launch_decode_any<false>(a, dtype, d, p.GT, static_cast<hipStream_t>(stream));
   return launch_status();
+}
+
+// Scratch of kv_decode_attn_noalloc: the split partials live in this
+// file-scope device array instead of a caller workspace.  Each GPU holds its
+// own copy at its own address; host code never passes the array's name to a
+// kernel (on the host it is only a stand-in), but the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current and kept per device.
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+namespace kvcc {
+namespace {
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::once_flag scratch_once[NOALLOC_MAX_DEVICES];
+void* scratch_ptr[NOALLOC_MAX_DEVICES];   // written once per device under its once_flag
+
+// The scratch array's device address on the current device, or null.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) return nullptr;
+  std::call_once(scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess) scratch_ptr[dev] = ptr;
+  });
+  return scratch_ptr[dev];
+}
+}  // namespace
+}  // namespace kvcc
+
+extern "C" int kv_decode_attn_noalloc(const void* q, const void* k_c, const void* v_c,
+                                      const int64_t* offsets, int B, int Hq, int Hkv, int d,
+                                      int dtype, float scale, int64_t capacity_rows, float* out,
+                                      float* lse, void* stream) {
+  if (!q || !offsets || !out) return KV_ERR_NULL;
+  if (capacity_rows > 0 && (!k_c || !v_c)) return KV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_c) || !aligned16(v_c) || !aligned16(offsets) ||
+      !aligned16(out) || !aligned16(lse))
+    return KV_ERR_ALIGN;
+  if (dtype != KV_F32 && dtype != KV_BF16) return KV_ERR_DTYPE;
+  DecodePlan p;
+  if (!plan_decode(B, Hq, Hkv, d, capacity_rows, &p)) return KV_ERR_SHAPE;
+  if (p.bytes > NOALLOC_SCRATCH_BYTES) return KV_ERR_WORKSPACE;
+  void* ws = device_scratch();
+  if (!ws) return KV_ERR_LAUNCH;
+  return kv_decode_attn(q, k_c, v_c, offsets, B, Hq, Hkv, d, dtype, scale, capacity_rows, out,
+                        lse, ws, NOALLOC_SCRATCH_BYTES, stream);
 }
 
 extern "C" size_t kv_vector_decode_workspace_size(int B, int Hq, int Hkv, int d,

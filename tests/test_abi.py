@@ -174,3 +174,19 @@ def test_binding_checks_sequence_lengths():
         _check_lengths(torch.tensor([64, 7], dtype=torch.int32), None, 2, 64, 8, True)
     with pytest.raises(ValueError):
         _check_lengths(None, None, 1, 16, 32, True)
+
+
+def test_decode_noalloc_validation():
+    # host checks only: nothing is launched
+    L = _lib.lib()
+    assert L.kv_decode_attn_noalloc(None, P, P, P, 1, 4, 2, 64, 1, 0.0, 8, P, None,
+                                    None) == KV_ERR_NULL
+    assert L.kv_decode_attn_noalloc(P, P, P, P + 8, 1, 4, 2, 64, 1, 0.0, 8, P, None,
+                                    None) == KV_ERR_ALIGN
+    assert L.kv_decode_attn_noalloc(P, P, P, P, 1, 4, 3, 64, 1, 0.0, 8, P, None,
+                                    None) == KV_ERR_SHAPE
+    # beyond the 16 MiB scratch
+    big = 1 << 30
+    assert L.kv_decode_workspace_size(64, 32, 8, 128, big) > 16 << 20
+    assert L.kv_decode_attn_noalloc(P, P, P, P, 64, 32, 8, 128, 1, 0.0, big, P, None,
+                                    None) == KV_ERR_WORKSPACE

@@ -210,3 +210,66 @@ def random_case(seed: int, *, B: int, Hq: int, Hkv: int, d: int, N_max: int, W: 
     return Layer(cfg=cfg, layer=0, ctx_len=torch.from_numpy(ctx_arr.astype(np.int32)),
                  q_win=_round(q, dtype), k=_round(k, dtype), v=_round(v, dtype),
                  q_dec=_round(q_dec, dtype))
+
+
+def make_layer_device(cfg: Config, layer: int = 0, device="cuda") -> Layer:
+    """``make_layer``'s recipe drawn on the device, for sizes where drawing on
+    the host takes minutes (the 32 layers of long128k, the ragged batch).
+
+    The same distributions, scales, padding, Zipf profile, needles and draw
+    order as ``make_layer``; the context lengths are the first draws of the
+    same PCG64 stream (so a ragged batch has the same lengths), everything
+    else comes from torch's device generator seeded from (seed, layer), so
+    the values differ from the host-drawn layer.  Returns device tensors."""
+    B, N_max = cfg.B, cfg.N_max
+    Hq, Hkv, d, W = cfg.Hq, cfg.Hkv, cfg.d, cfg.W
+    rng = layer_rng(cfg, layer)
+    if cfg.ctx_range is not None:
+        lo, hi = cfg.ctx_range
+        hi = min(hi, N_max)
+        lo = min(lo, hi)
+        ctx = rng.integers(lo, hi + 1, size=B, dtype=np.int64)
+    else:
+        ctx = np.full(B, N_max, dtype=np.int64)
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence([cfg.seed, layer, 1]).generate_state(1)[0]))
+    f32 = dict(device=device, dtype=torch.float32, generator=g)
+    ch_scale = torch.exp(torch.randn(Hkv, d, **f32)) if cfg.channel_lognormal else None
+    k = torch.randn(B, Hkv, N_max, d, **f32)
+    if ch_scale is not None:
+        k *= ch_scale[None, :, None, :]
+    v = torch.randn(B, Hkv, N_max, d, **f32)
+    q_win = torch.randn(B, Hq, W, d, **f32)
+    for b in range(B):
+        k[b, :, ctx[b]:, :] = 0.0
+        v[b, :, ctx[b]:, :] = 0.0
+    if cfg.zipf > 0.0:
+        for b in range(B):
+            n = int(ctx[b])
+            f = torch.arange(1, n + 1, device=device, dtype=torch.float64) ** (-cfg.zipf)
+            f = (f / torch.sqrt(torch.mean(f * f))).to(torch.float32)
+            for h in range(Hkv):
+                perm = torch.randperm(n, device=device, generator=g)
+                k[b, h, :n, :] *= f[perm][:, None]
+    k_t = k.to(cfg.dtype)
+    del k
+    q_t = q_win.to(cfg.dtype)
+    needle_pos = None
+    if cfg.needles > 0:
+        G = cfg.G
+        needle_pos = np.zeros((B, Hkv, cfg.needles), dtype=np.int64)
+        for b in range(B):
+            n = int(ctx[b])
+            for h in range(Hkv):
+                u = q_t[b, h * G:(h + 1) * G].reshape(G * W, d).double().mean(dim=0)
+                u = u / torch.linalg.vector_norm(u)
+                mean_norm = torch.linalg.vector_norm(k_t[b, h, :n].double(), dim=1).mean()
+                pos = torch.randperm(n, device=device, generator=g)[:cfg.needles]
+                pos = torch.sort(pos).values
+                needle_pos[b, h] = pos.cpu().numpy()
+                k_t[b, h, pos, :] = (3.0 * mean_norm * u).to(torch.float32).to(cfg.dtype)
+    steps = max(cfg.decode_steps, 1)
+    q_dec = torch.randn(steps, B, Hq, d, **f32).to(cfg.dtype)
+    return Layer(cfg=cfg, layer=layer,
+                 ctx_len=torch.from_numpy(ctx.astype(np.int32)).to(device),
+                 q_win=q_t, k=k_t, v=v.to(cfg.dtype), q_dec=q_dec, needle_pos=needle_pos)

@@ -47,3 +47,26 @@ def test_needles_are_retained_by_the_oracle():
         keep = set(kept[0, h, :cnt[h]].tolist())
         missing = [p for p in lay.needle_pos[0, h].tolist() if p not in keep]
         assert not missing, f"head {h} lost needles {missing}"
+
+
+def test_device_drawn_layer_follows_the_same_recipe():
+    # make_layer_device (run here on the CPU generator): reproducible, the same
+    # context lengths as the host-drawn layer, zero padding rows, needles at
+    # the recorded positions, independent layers.
+    import dataclasses
+    cfg = dataclasses.replace(wl.CONFIGS["ragged_adaptive"], B=3, N_max=4096)
+    a = wl.make_layer_device(cfg, 0, "cpu")
+    b = wl.make_layer_device(cfg, 0, "cpu")
+    assert torch.equal(a.k, b.k) and torch.equal(a.q_dec, b.q_dec)
+    assert torch.equal(a.ctx_len, wl.make_layer(cfg, B=3, N_max=4096, with_v=False).ctx_len)
+    for bb in range(3):
+        n = int(a.ctx_len[bb])
+        assert torch.count_nonzero(a.k[bb, :, n:]) == 0 and torch.count_nonzero(a.v[bb, :, n:]) == 0
+    ncfg = dataclasses.replace(wl.CONFIGS["needle32k"], B=1, N_max=2048)
+    lay = wl.make_layer_device(ncfg, 0, "cpu")
+    for h in range(ncfg.Hkv):
+        rows = lay.k[0, h, torch.from_numpy(lay.needle_pos[0, h])]
+        assert torch.equal(rows, rows[:1].expand_as(rows))      # one planted key per head
+    lcfg = dataclasses.replace(wl.CONFIGS["long128k"], N_max=256)
+    assert not torch.equal(wl.make_layer_device(lcfg, 0, "cpu").k,
+                           wl.make_layer_device(lcfg, 1, "cpu").k)

@@ -586,8 +586,20 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
   step_m(T_{}, I0{}, T_{}, I1{}, t0, masked_tile(0));           // MMA(1, r0) | epi(0, r1)
   emit_col(0, 0);
   step_m(T_{}, I1{}, T_{}, I0{}, t0 + 32, masked_tile(0));      // MMA(1, r1) | epi(1, r0)
+  // Issue priority falls with progress (3 for the first quarter of the
+  // tiles, 0 for the last): of the two workgroups that share a CU, the one
+  // ahead yields issue slots to the one behind, so both finish together
+  // instead of the younger one running its last tiles alone.
+  __builtin_amdgcn_s_setprio(3);
+  int prio_next = 1;   // the next quarter boundary, as a quarter index
   for (int tile = 1; tile < ntiles; ++tile) {
     const int tt0 = t0 + tile * TOK, buf = tile % NB;
+    if (prio_next < 4 && 4 * tile >= prio_next * ntiles) {
+      if (prio_next == 1) __builtin_amdgcn_s_setprio(2);
+      else if (prio_next == 2) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+      ++prio_next;
+    }
     wait_tile(tile);
     __syncthreads();
     if (tile >= 2) reduce_tile(tile - 2);

@@ -692,6 +692,87 @@ __global__ __launch_bounds__(GT * D) void decode_merge(DecodeArgs a) {
   if (a.lse && e == 0) a.lse[bj] = any ? (M + log2f(L)) * LN2_F : -INFINITY;
 }
 
+// Merge of a plain (not routed) cache's partials: one wave per (head, query
+// head, 64-element slice of the output).  M is the largest item maximum; item
+// i weighs 2^(m_i - M).  A head of at most 64 items takes one round trip
+// (every load issued at once, the weights broadcast from LDS); longer heads
+// walk their items 64 at a time,
+// lane i turning item c + i's maximum into its weight (kept in LDS) while
+// every lane sums its output element over the 64 items.  The sums run in
+// item order (the normaliser's lane sums by a fixed butterfly), so the
+// result is deterministic.
+template <int D, int GT>
+__global__ __launch_bounds__(WAVE) void decode_merge_w(DecodeArgs a) {
+  constexpr int UB = 16;   // item loads in flight per lane (heads of more than 64 items)
+  __shared__ __attribute__((aligned(16))) float wts[WAVE];
+  const int head = blockIdx.x, jg = blockIdx.y, ds = blockIdx.z;
+  const int qsub = jg / GT, g = jg % GT;
+  const int lane = threadIdx.x;
+  const int i0 = a.item_start[head], i1 = a.item_start[head + 1];
+  const int n = i1 - i0;
+  const size_t base = (size_t)qsub * a.items_max;
+  const float2* ml = a.part_ml + base * GT + g;              // item it: ml[it * GT]
+  const int e = ds * WAVE + lane;
+  const float* po = a.part_o + (base * GT + g) * D + e;     // item it: po[it * GT * D]
+  float M = -INFINITY, O = 0.f, L = 0.f;
+  if (n <= 0) {
+    // a head with no rows: out = 0, lse = -inf
+  } else if (n <= WAVE) {
+    // One round trip: lane i loads item i's (m, l) while every lane loads its
+    // element of all n items (indices past the last item re-read it, so the
+    // loads need no branch); then the maximum, the weights and the sums, in
+    // item order.
+    float2 p = make_float2(-INFINITY, 0.f);
+    if (lane < n) p = ml[(size_t)(i0 + lane) * GT];
+    float ov[WAVE];
+#pragma unroll
+    for (int v = 0; v < WAVE; ++v) ov[v] = po[(size_t)(i0 + min(v, n - 1)) * GT * D];
+    M = wave_max(p.x);
+    if (M != -INFINITY) {
+      const float w = lane < n ? fast_exp2(p.x - M) : 0.f;   // 0 for an item with no rows
+      L = wave_sum(p.y * w);
+      wts[lane] = w;   // one wave: its LDS reads below follow this write
+#pragma unroll
+      for (int v = 0; v < WAVE; v += 4) {
+        const float4 w4 = *reinterpret_cast<const float4*>(&wts[v]);   // broadcast read
+        if (v < n) O = fmaf(ov[v], w4.x, O);
+        if (v + 1 < n) O = fmaf(ov[v + 1], w4.y, O);
+        if (v + 2 < n) O = fmaf(ov[v + 2], w4.z, O);
+        if (v + 3 < n) O = fmaf(ov[v + 3], w4.w, O);
+      }
+    }
+  } else {
+    for (int it = i0 + lane; it < i1; it += WAVE) M = fmaxf(M, ml[(size_t)it * GT].x);
+    M = wave_max(M);
+    if (M != -INFINITY) {
+      for (int c0 = i0; c0 < i1; c0 += WAVE) {
+        const int it = c0 + lane;
+        float w = 0.f;
+        if (it < i1) {
+          const float2 p = ml[(size_t)it * GT];
+          w = fast_exp2(p.x - M);
+          L = fmaf(p.y, w, L);
+        }
+        wts[lane] = w;   // one wave: its LDS reads below follow this write
+        const int nc = min(WAVE, i1 - c0);
+        for (int u = 0; u < nc; u += UB) {
+          float ov[UB];
+#pragma unroll
+          for (int v = 0; v < UB; ++v)
+            ov[v] = u + v < nc ? po[(size_t)(c0 + u + v) * GT * D] : 0.f;
+#pragma unroll
+          for (int v = 0; v < UB; ++v) O = fmaf(ov[v], wts[u + v], O);
+        }
+      }
+      L = wave_sum(L);
+    }
+  }
+  const size_t bj = (size_t)(head / a.Hkv) * a.Hq + (head % a.Hkv) * a.G + jg;
+  const bool any = L > 0.f;
+  a.out[bj * D + e] = any ? O / L : 0.f;
+  if (a.lse && ds == 0 && lane == 0) a.lse[bj] = any ? (M + log2f(L)) * LN2_F : -INFINITY;
+}
+
 struct DecodePlan {
   int GT, n_sub, items_max;
   size_t off_ml, off_ist, off_u, bytes;
@@ -729,8 +810,12 @@ void launch_decode(const DecodeArgs& a, hipStream_t st) {
     else
       launch("decode_split", decode_split<T, D, GT, false>, grid, dim3(DT), (uint32_t)dyn, st, a);
   }
-  launch(VEC ? "vector_decode_merge" : "decode_merge", decode_merge<D, GT, VEC>,
-         dim3(a.B * a.Hkv, a.n_sub), dim3(GT * D), 0, st, a);
+  if constexpr (VEC)
+    launch("vector_decode_merge", decode_merge<D, GT, true>, dim3(a.B * a.Hkv, a.n_sub),
+           dim3(GT * D), 0, st, a);
+  else
+    launch("decode_merge", decode_merge_w<D, GT>, dim3(a.B * a.Hkv, a.G, D / WAVE), dim3(WAVE),
+           0, st, a);
 }
 
 template <typename T, int D, bool VEC>

@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Throughput of the score -> select -> compact -> decode path on one GPU.
 
-One step = kv_score + kv_select + kv_compact_decode (kv_compact and
-kv_decode_attn in one pass over the kept rows) over one batch of the chosen
+One step = kv_score_select (kv_score and kv_select in one call) +
+kv_compact_decode (kv_compact and kv_decode_attn in one pass over the kept
+rows) over one batch of the chosen
 synthetic workload (default: batch 4 at 32K context, 32 query / 8 KV heads,
 d = 128, W = 64, keep 10%, one decode step), inputs resident in HBM before
 timing starts.  Prints one JSON line:
@@ -25,7 +26,8 @@ timing starts.  Prints one JSON line:
               bf16 MFMA peak, select + compact + decode against HBM
   copy_gbps   a 1 GiB device-to-device copy (read + write bytes / time)
   unfused     the same step with kv_compact and kv_decode_attn as two calls;
-              decode_hbm_gbps is that decode's rate
+              decode_hbm_gbps is that decode's rate; score_then_select:
+              kv_score and kv_select as two calls
   fidelity    output / log-sum-exp loss terms of the compacted cache
               against the full cache for the step's decode queries (and,
               fidelity_window_query, for the last window row of each head)
@@ -80,6 +82,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true",
                    help="only the headline workload (no other workloads, VECTOR, fidelity)")
+    p.add_argument("--score-then-select", action="store_true",
+                   help="time kv_score + kv_select as two calls instead of kv_score_select")
     p.add_argument("--cpu-seqs", type=int, default=4,
                    help="sequences of the batch the oracle baseline processes")
     return p.parse_args()
@@ -115,8 +119,9 @@ class Pipeline:
         self.cap = capacity_of(cfg, B, Hkv, N)
         f32 = torch.float32
         self.scores = torch.empty(B, Hkv, N, device=DEV, dtype=f32)
-        self.ws_s = torch.zeros(api.kv_score_workspace_size(B, cfg.Hq, Hkv, N, cfg.W, D),
+        self.ws_s = torch.zeros(api.kv_score_select_workspace_size(B, cfg.Hq, Hkv, N, cfg.W, D),
                                 device=DEV, dtype=torch.uint8)
+        self.two_calls = False   # kv_score + kv_select instead of kv_score_select
         self.idx = torch.empty(B, Hkv, N, device=DEV, dtype=torch.int32)
         self.cnt = torch.empty(B * Hkv, device=DEV, dtype=torch.int32)
         self.comp = (torch.empty(self.cap, D, device=DEV, dtype=lay.k.dtype),
@@ -129,8 +134,13 @@ class Pipeline:
                                 device=DEV, dtype=torch.uint8)
 
     def step(self):
-        api.kv_score(self.q, self.k, self.c, scores=self.scores, workspace=self.ws_s)
-        api.kv_select(self.scores, self.c, self.budget, kept_idx=self.idx, kept_count=self.cnt)
+        if self.two_calls:
+            api.kv_score(self.q, self.k, self.c, scores=self.scores, workspace=self.ws_s)
+            api.kv_select(self.scores, self.c, self.budget, kept_idx=self.idx,
+                          kept_count=self.cnt)
+        else:
+            api.kv_score_select(self.q, self.k, self.c, self.budget, scores=self.scores,
+                                kept_idx=self.idx, kept_count=self.cnt, workspace=self.ws_s)
         if self.fused:
             api.kv_compact_decode(self.k, self.v, self.idx, self.cnt, self.cap, self.qd,
                                   out=self.comp, attn_out=self.out, lse=self.lse,
@@ -446,6 +456,7 @@ def oracle_on_sequences(lay: wl.Layer, seqs, threads=None) -> dict:
 def measure_headline(lay: wl.Layer, args, extras: bool) -> dict:
     cfg = lay.cfg
     pipe = Pipeline(lay)
+    pipe.two_calls = bool(getattr(args, "score_then_select", False))
     log("bench: device copy bandwidth")
     copy_bw = copy_gbps()
     log(f"bench: {torch.cuda.get_device_name(0)}; copy {copy_bw:.0f} GB/s; warmup {args.warmup}")
@@ -521,6 +532,11 @@ def measure_headline(lay: wl.Layer, args, extras: bool) -> dict:
         res["score_one_pass"] = {"ms": t_one * 1e3,
                                  "algorithmic_tflops": acc["flop_pass"] / t_one / 1e12,
                                  "algorithmic_frac": acc["flop_pass"] / t_one / 1e12 / peak_f}
+        pipe.two_calls = True
+        ms_two, kt_two = timed_steps(pipe.step, args.steps)
+        pipe.two_calls = False
+        res["score_then_select"] = {"ms_per_step_every_launch_timed": ms_two,
+                                    "kernels_ms": {k: v[0] for k, v in kt_two.items()}}
         pipe.fused = False
         ms_unf, kt_unf = timed_steps(pipe.step, args.steps)
         pipe.fused = True

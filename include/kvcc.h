@@ -182,6 +182,32 @@ int kv_select(const float* scores, const int32_t* ctx_len,
               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------
+ * kv_score_select - kv_score followed by kv_select in one call.
+ *
+ * The same scores (and row LSEs) as kv_score and the same kept indices and
+ * counts as kv_select on them, bit for bit: the score of every cached token
+ * ("KVSculpt: KV Cache Compression as Distillation", section 2.B; the
+ * attention-based importance of "A Simple Plug-in for Improving
+ * Eviction-Based KV Cache Compression", section "Enonce du Probleme"), then
+ * the budgeted per-head selection that evicts the low scorers.  Under a k or
+ * kept-fraction budget with no protected tokens and N_max <= 32768 the
+ * second score sweep also counts each head's scores by their top 11 key
+ * bits, so the selection starts from that histogram and ranks only the
+ * scores that share the k-th score's top bits.
+ *
+ * Arguments as kv_score (q_win ... scale) and kv_select (budget, kept_idx,
+ * kept_count); workspace: kv_score_select_workspace_size() bytes (one
+ * buffer for both steps).
+ * ---------------------------------------------------------------------- */
+size_t kv_score_select_workspace_size(int B, int Hq, int Hkv, int N_max, int W, int d);
+int kv_score_select(const void* q_win, const void* k, const int32_t* ctx_len,
+                    const kv_budget* budget, float* scores, float* row_lse,
+                    int32_t* kept_idx, int32_t* kept_count,
+                    int B, int Hq, int Hkv, int N_max, int W, int d, int dtype,
+                    int causal, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------------
  * kv_compact - gather the kept rows into one packed, ordered cache.
  *
  * The result keeps the plain K/V row layout so an ordinary attention kernel

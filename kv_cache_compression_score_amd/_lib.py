@@ -35,6 +35,11 @@ PROTOTYPES = {
     "kv_score_from_lse": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_float,
                                   c_void_p]),
+    "kv_score_select_workspace_size": (c_size_t, [c_int] * 6),
+    "kv_score_select": (c_int, [c_void_p, c_void_p, c_void_p, ctypes.POINTER(KvBudget),
+                                c_void_p, c_void_p, c_void_p, c_void_p,
+                                c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_float,
+                                c_void_p, c_size_t, c_void_p]),
     "kv_select_workspace_size": (c_size_t, [c_int] * 3),
     "kv_select": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, ctypes.POINTER(KvBudget),
                           c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),

@@ -153,6 +153,42 @@ def kv_score_from_lse(q_win: torch.Tensor, k: torch.Tensor, ctx_len: Optional[to
     return scores
 
 
+def kv_score_select_workspace_size(B, Hq, Hkv, N_max, W, d) -> int:
+    return int(lib().kv_score_select_workspace_size(B, Hq, Hkv, N_max, W, d))
+
+
+def kv_score_select(q_win: torch.Tensor, k: torch.Tensor, ctx_len: Optional[torch.Tensor],
+                    budget: Budget, *, scale: float = 0.0, causal: bool = False,
+                    with_row_lse: bool = False, scores: Optional[torch.Tensor] = None,
+                    kept_idx: Optional[torch.Tensor] = None,
+                    kept_count: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, ctx_len_host=None):
+    """kv_score then kv_select in one call: (scores, row_lse or None, kept_idx, kept_count)."""
+    _check(q_win, "q_win"); _check(k, "k")
+    B, Hq, W, d = q_win.shape
+    _, Hkv, N_max, _ = k.shape
+    _check_lengths(ctx_len, ctx_len_host, B, N_max, W, causal)
+    dev = k.device
+    if scores is None:
+        scores = torch.empty(B, Hkv, N_max, device=dev, dtype=torch.float32)
+    row_lse = torch.empty(B, Hq, W, device=dev, dtype=torch.float32) if with_row_lse else None
+    if kept_idx is None:
+        kept_idx = torch.empty(B, Hkv, N_max, device=dev, dtype=torch.int32)
+    if kept_count is None:
+        kept_count = torch.empty(B * Hkv, device=dev, dtype=torch.int32)
+    need = kv_score_select_workspace_size(B, Hq, Hkv, N_max, W, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
+    if ctx_len is not None:
+        _check(ctx_len, "ctx_len")
+    cb = budget.to_c()
+    _call("kv_score_select", lib().kv_score_select(
+        _ptr(q_win), _ptr(k), _ptr(ctx_len), ctypes.byref(cb), _ptr(scores), _ptr(row_lse),
+        _ptr(kept_idx), _ptr(kept_count), B, Hq, Hkv, N_max, W, d, _dtype_code(k),
+        int(bool(causal)), float(scale), _ptr(workspace), workspace.numel(), _stream()))
+    return scores, row_lse, kept_idx, kept_count
+
+
 def kv_select(scores: torch.Tensor, ctx_len: Optional[torch.Tensor], budget: Budget, *,
               kept_idx: Optional[torch.Tensor] = None, kept_count: Optional[torch.Tensor] = None):
     """Kept indices [B][Hkv][N_max] int32 (first count valid, ascending) and counts [B*Hkv]."""

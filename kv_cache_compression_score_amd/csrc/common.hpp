@@ -65,6 +65,21 @@ __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Order-preserving uint32 key of an fp32 score (a larger score gives a
+// larger key; -0.0 maps onto +0.0), and its inverse.  Selection ranks these
+// keys; the score kernels histogram their top bits for it.
+__device__ __forceinline__ uint32_t to_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+// Bins of the top-digit key histogram (its top KEY_DIGIT bits).
+constexpr int KEY_DIGIT = 11;
+constexpr int KEY_BINS = 1 << KEY_DIGIT;
+
 // exp2 / log2 on the hardware transcendental unit (v_exp_f32 / v_log_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -14,4 +14,23 @@ void select_launch(const float* scores, const int32_t* ctx, const int32_t* n_hea
                    int32_t* kept_idx, int32_t* kept_count, hipStream_t st,
                    const char* timer_name);
 
+// Host validation of a budget (kv_select's rules): KV_OK or a kv_status.
+int check_budget(const kv_budget& bu);
+
+// Selection from the top-digit key histogram [B*Hkv][KEY_BINS] that the
+// score kernels build (kv_score_select); only for the budgets and sizes
+// select_hist_eligible accepts: explicit k or kept fraction, no protected
+// tokens, N_max <= 32768.  Same kept indices and counts as select_launch.
+bool select_hist_eligible(const kv_budget& bud, int N_max);
+void select_hist_launch(const float* scores, const int32_t* ctx, const uint32_t* hist, int B,
+                        int Hkv, int N_max, const kv_budget& bud, int32_t* kept_idx,
+                        int32_t* kept_count, hipStream_t st);
+
+// The part path of kv_select for heads above 32768 tokens under a count
+// budget: its workspace size, and the launch (false if it does not apply).
+size_t select_part_workspace(int B, int Hkv, int N_max);
+bool select_parts_launch(const float* scores, const int32_t* ctx, int B, int Hkv, int N_max,
+                         const kv_budget& bud, int32_t* kept_idx, int32_t* kept_count,
+                         void* workspace, size_t workspace_bytes, hipStream_t st);
+
 }  // namespace kvcc

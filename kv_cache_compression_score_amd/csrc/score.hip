@@ -34,6 +34,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "internal.hpp"
 
 namespace kvcc {
 namespace {
@@ -153,6 +154,10 @@ struct ScoreArgs {
   int4* tab;           // [TAB_MAX] the ranges, written by pass 1: {head, t0, t1, n}
   int self_merge;      // pass 2 merges the pass-1 partials (n_chunks <= SELF_MERGE); else the fold's lse2
   float c;             // scale * log2(e)
+  // Optional [B*Hkv][KEY_BINS] histogram of the top key bits of each head's
+  // scores (the first radix digit of the selection): pass 1 clears it, pass
+  // 2 counts every score it writes.  Null: not built.
+  uint32_t* hist;
 };
 
 // Pass-2 work ranges, built by one workgroup of pass 1 so that pass 2 reads
@@ -222,6 +227,7 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char ktile[NB][TOK * ROWB];
   __shared__ float red[3][PASS == 2 ? NW : 1][TOK];
   __shared__ __attribute__((aligned(8))) int rowpos[PASS == 2 ? NW * RBW * 32 : 2];
+  __shared__ uint32_t khist[PASS == 2 ? KEY_BINS : 1];   // pass 2 with a.hist
 
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int hf = lane >> 5, l32 = lane & 31;
@@ -246,6 +252,8 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
     n = __builtin_amdgcn_readfirstlane(e.w);
   } else {
     c = blockIdx.x; h = blockIdx.y; b = blockIdx.z;
+    if (PASS == 1 && a.hist && c == 0)   // the head's key histogram starts empty
+      for (int i = tid; i < KEY_BINS; i += NT) a.hist[(size_t)(b * a.Hkv + h) * KEY_BINS + i] = 0u;
     n = a.ctx ? min(max(a.ctx[b], 0), a.N_max) : a.N_max;
     const int TC = PASS == 1 ? a.TC : a.TC2;
     t0 = c * TC;
@@ -293,6 +301,8 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
   }
   if (PASS == 2 && a.causal)
     for (int r = tid; r < NW * RBW * 32; r += NT) rowpos[r] = r % a.W;
+  if (PASS == 2 && a.hist)   // cleared before tile 0's barrier, counted after it
+    for (int i = tid; i < KEY_BINS; i += NT) khist[i] = 0u;
 
   // Pass-1 running state (per row owned by the lane) / pass-2 negated row lse2.
   float m_run[RBW], s_run[RBW];
@@ -565,6 +575,7 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
 #pragma unroll
         for (int w2 = 0; w2 < NW; ++w2) s += red[tile % 3][w2][tid];
         a.scores[(size_t)head * a.N_max + t] = s;
+        if (a.hist) atomicAdd(&khist[to_key(s) >> (32 - KEY_DIGIT)], 1u);
       }
     }
   };
@@ -620,6 +631,13 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
     __syncthreads();
     if (ntiles >= 2) reduce_tile(ntiles - 2);
     reduce_tile(ntiles - 1);
+    if (a.hist) {   // the range's counts into the head's histogram
+      __syncthreads();
+      for (int i = tid; i < KEY_BINS; i += NT) {
+        const uint32_t v = khist[i];
+        if (v) atomicAdd(&a.hist[(size_t)head * KEY_BINS + i], v);
+      }
+    }
   }
 
   if (PASS == 1) {
@@ -788,10 +806,95 @@ void launch_score_nw(const ScoreArgs& a, int NW, hipStream_t st) {
   }
 }
 
+void launch_score_any(const ScoreArgs& a, int dtype, int d, int NW, hipStream_t st) {
+  if (dtype == KV_BF16) {
+    if (d == 128) launch_score_nw<__bf16, 128>(a, NW, st);
+    else launch_score_nw<__bf16, 64>(a, NW, st);
+  } else {
+    if (d == 128) launch_score_nw<float, 128>(a, NW, st);
+    else launch_score_nw<float, 64>(a, NW, st);
+  }
+}
+
+// Two-pass arguments for kv_score / kv_score_select (workspace at ws).
+ScoreArgs two_pass_args(const void* q_win, const void* k, const int32_t* ctx_len, float* scores,
+                        float* row_lse, int B, int Hq, int Hkv, int N_max, int W, int d,
+                        int causal, float scale, const ScorePlan& p, void* ws) {
+  ScoreArgs a;
+  a.q = q_win; a.k = k; a.ctx = ctx_len; a.scores = scores; a.row_lse = row_lse;
+  a.lse_in = nullptr;
+  a.part = static_cast<float2*>(ws);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_lse);
+  a.tab = reinterpret_cast<int4*>(static_cast<char*>(ws) + p.off_tab);
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N_max = N_max; a.W = W; a.G = p.G;
+  a.R = p.R; a.R_pad = p.R_pad; a.TC = p.TC; a.n_chunks = p.n_chunks;
+  a.TC2 = p.TC; a.n_chunks2 = p.n_chunks;
+  a.causal = causal ? 1 : 0;
+  a.c = (float)((scale > 0.f ? (double)scale : 1.0 / sqrt((double)d)) * LOG2E_D);
+  a.hist = nullptr;
+  return a;
+}
+
+// kv_score_select's workspace: the score workspace, then the key histogram,
+// then the part-path selection workspace (heads above 32768 tokens).
+struct ScoreSelectPlan {
+  size_t off_hist, off_sel, sel_bytes, bytes;
+};
+bool plan_score_select(int B, int Hq, int Hkv, int N_max, int W, int d, ScorePlan* p,
+                       ScoreSelectPlan* q) {
+  if (!plan_score(B, Hq, Hkv, N_max, W, d, p)) return false;
+  q->off_hist = (p->bytes + 255) & ~size_t(255);
+  q->off_sel = (q->off_hist + (size_t)B * Hkv * KEY_BINS * sizeof(uint32_t) + 255) & ~size_t(255);
+  q->sel_bytes = select_part_workspace(B, Hkv, N_max);
+  q->bytes = q->off_sel + q->sel_bytes;
+  return true;
+}
+
 }  // namespace
 }  // namespace kvcc
 
 using namespace kvcc;
+
+extern "C" size_t kv_score_select_workspace_size(int B, int Hq, int Hkv, int N_max, int W, int d) {
+  kvcc::ScorePlan p;
+  kvcc::ScoreSelectPlan q;
+  return kvcc::plan_score_select(B, Hq, Hkv, N_max, W, d, &p, &q) ? q.bytes : 0;
+}
+
+extern "C" int kv_score_select(const void* q_win, const void* k, const int32_t* ctx_len,
+                               const kv_budget* budget, float* scores, float* row_lse,
+                               int32_t* kept_idx, int32_t* kept_count, int B, int Hq, int Hkv,
+                               int N_max, int W, int d, int dtype, int causal, float scale,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace kvcc;
+  if (!q_win || !k || !scores || !budget || !kept_idx || !kept_count) return KV_ERR_NULL;
+  if (!aligned16(q_win) || !aligned16(k) || !aligned16(scores) || !aligned16(ctx_len) ||
+      !aligned16(row_lse) || !aligned16(kept_idx) || !aligned16(kept_count) ||
+      !aligned16(workspace))
+    return KV_ERR_ALIGN;
+  if (dtype != KV_F32 && dtype != KV_BF16) return KV_ERR_DTYPE;
+  ScorePlan p;
+  ScoreSelectPlan q;
+  if (!plan_score_select(B, Hq, Hkv, N_max, W, d, &p, &q)) return KV_ERR_SHAPE;
+  if (const int st = check_budget(*budget)) return st;
+  if (!workspace || workspace_bytes < q.bytes) return KV_ERR_WORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  ScoreArgs a = two_pass_args(q_win, k, ctx_len, scores, row_lse, B, Hq, Hkv, N_max, W, d, causal,
+                              scale, p, ws);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + q.off_hist);
+  const bool fast = select_hist_eligible(*budget, N_max);
+  if (fast) a.hist = hist;
+  launch_score_any(a, dtype, d, p.NW, st);
+  if (fast)
+    select_hist_launch(scores, ctx_len, hist, B, Hkv, N_max, *budget, kept_idx, kept_count, st);
+  else if (!select_parts_launch(scores, ctx_len, B, Hkv, N_max, *budget, kept_idx, kept_count,
+                                ws + q.off_sel, q.sel_bytes, st))
+    select_launch(scores, ctx_len, nullptr, B, Hkv, N_max, *budget, false, kept_idx, kept_count,
+                  st, "select");
+  return launch_status();
+}
 
 extern "C" size_t kv_score_workspace_size(int B, int Hq, int Hkv, int N_max, int W, int d) {
   ScorePlan p;
@@ -812,26 +915,9 @@ extern "C" int kv_score(const void* q_win, const void* k, const int32_t* ctx_len
   if (!plan_score(B, Hq, Hkv, N_max, W, d, &p)) return KV_ERR_SHAPE;
   if (!workspace || workspace_bytes < p.bytes) return KV_ERR_WORKSPACE;
 
-  ScoreArgs a;
-  a.q = q_win; a.k = k; a.ctx = ctx_len; a.scores = scores; a.row_lse = row_lse;
-  a.lse_in = nullptr;
-  a.part = static_cast<float2*>(workspace);
-  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_lse);
-  a.tab = reinterpret_cast<int4*>(static_cast<char*>(workspace) + p.off_tab);
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N_max = N_max; a.W = W; a.G = p.G;
-  a.R = p.R; a.R_pad = p.R_pad; a.TC = p.TC; a.n_chunks = p.n_chunks;
-  a.TC2 = p.TC; a.n_chunks2 = p.n_chunks;
-  a.causal = causal ? 1 : 0;
-  a.c = (float)((scale > 0.f ? (double)scale : 1.0 / sqrt((double)d)) * LOG2E_D);
-
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dtype == KV_BF16) {
-    if (d == 128) launch_score_nw<__bf16, 128>(a, p.NW, st);
-    else launch_score_nw<__bf16, 64>(a, p.NW, st);
-  } else {
-    if (d == 128) launch_score_nw<float, 128>(a, p.NW, st);
-    else launch_score_nw<float, 64>(a, p.NW, st);
-  }
+  const ScoreArgs a = two_pass_args(q_win, k, ctx_len, scores, row_lse, B, Hq, Hkv, N_max, W, d,
+                                    causal, scale, p, workspace);
+  launch_score_any(a, dtype, d, p.NW, static_cast<hipStream_t>(stream));
   return launch_status();
 }
 
@@ -855,14 +941,7 @@ extern "C" int kv_score_from_lse(const void* q_win, const void* k, const int32_t
   a.TC2 = p.TC; a.n_chunks2 = p.n_chunks;
   a.causal = causal ? 1 : 0;
   a.c = (float)((scale > 0.f ? (double)scale : 1.0 / sqrt((double)d)) * LOG2E_D);
-
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dtype == KV_BF16) {
-    if (d == 128) launch_score_nw<__bf16, 128>(a, p.NW, st);
-    else launch_score_nw<__bf16, 64>(a, p.NW, st);
-  } else {
-    if (d == 128) launch_score_nw<float, 128>(a, p.NW, st);
-    else launch_score_nw<float, 64>(a, p.NW, st);
-  }
+  a.hist = nullptr;
+  launch_score_any(a, dtype, d, p.NW, static_cast<hipStream_t>(stream));
   return launch_status();
 }

@@ -43,8 +43,8 @@ namespace {
 constexpr int NT = 1024;
 constexpr int NWV = NT / WAVE;
 constexpr int LDS_KEYS = 32768;
-constexpr int NBINS = 2048;
-constexpr int DIGIT = 11;
+constexpr int NBINS = KEY_BINS;
+constexpr int DIGIT = KEY_DIGIT;
 
 struct SelectArgs {
   const float* scores;
@@ -57,14 +57,6 @@ struct SelectArgs {
   int32_t* kept_count;
 };
 
-__device__ __forceinline__ uint32_t to_key(float s) {
-  uint32_t u = __float_as_uint(s);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float from_key(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
 
 struct Smem {
   uint32_t hist[NBINS];
@@ -288,6 +280,99 @@ __device__ __forceinline__ int count_budget(const kv_budget& bu, int head, int n
   return min(max((int)cnt, lo), hi);   // threshold
 }
 
+// Emit of the kept indices from keys held in registers: wave w holds the
+// keys of its segment [s0, s1) (seg a multiple of 256, four consecutive
+// tokens per lane per step) in ek.  keys_lds is free LDS of at least n words
+// (its old contents are no longer needed by any wave once each holds its
+// keys, which the first barrier below ensures).  Keeps key > T, and the first
+// `quota` keys equal to T (eq_total of them in the head), ascending.
+constexpr int EPI = LDS_KEYS / NWV / (4 * WAVE);   // register steps per lane (seg <= EPI * 256)
+__device__ void emit_regs(const uint4 (&ek)[EPI], int s0, int s1, int n, uint32_t T,
+                          uint32_t quota, uint32_t eq_total, uint32_t* keys_lds, Smem& sm,
+                          int32_t* dst) {
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  uint32_t slot = 0, eqr = 0;
+  // Every wave holds its segment's keys in registers, so after one barrier
+  // the key area of LDS is free: each wave compacts its kept indices into
+  // its own key range [s0, s1), then copies them out contiguously.
+  // When every key equal to T is kept (no tie to rank) the keep rule is
+  // key >= T; otherwise waves first count their equal keys for the ranks.
+  const bool all_ties = quota >= eq_total;
+  if (!all_ties) {
+    uint32_t eqw = 0;
+#pragma unroll
+    for (int j = 0; j < EPI; ++j) {
+      if (s0 + j * 4 * WAVE < s1) {
+        const int t = s0 + j * 4 * WAVE + 4 * lane;
+        const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          eqw += (uint32_t)__popcll(__ballot(t + u < s1 && kk[u] == T));
+      }
+    }
+    if (lane == 0) sm.w_eq[wave] = eqw;
+  }
+  __syncthreads();   // also: every wave holds its keys in registers now
+  if (!all_ties)
+    for (int w = 0; w < wave; ++w) eqr += sm.w_eq[w];   // ties before this wave
+  uint32_t* stage = keys_lds + s0;
+  uint32_t nk = 0;
+#pragma unroll
+  for (int j = 0; j < EPI; ++j) {
+    if (all_ties && s0 + j * 4 * WAVE < s1) {
+      const int t = s0 + j * 4 * WAVE + 4 * lane;
+      const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
+      uint32_t at = nk;
+      bool keep[4];
+      uint64_t bk[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        keep[u] = t + u < s1 && kk[u] >= T;
+        bk[u] = __ballot(keep[u]);
+        at += mbcnt(bk[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (keep[u]) stage[at++] = (uint32_t)(t + u);
+        nk += (uint32_t)__popcll(bk[u]);
+      }
+    } else if (s0 + j * 4 * WAVE < s1) {
+      const int t = s0 + j * 4 * WAVE + 4 * lane;
+      const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
+      bool is_gt[4], is_eq[4], keep[4];
+      uint64_t be[4], bk[4];
+      uint32_t r = eqr;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool valid = t + u < s1;
+        is_gt[u] = valid && kk[u] > T;
+        is_eq[u] = valid && kk[u] == T;
+        be[u] = __ballot(is_eq[u]);
+        r += mbcnt(be[u]);
+      }
+      uint32_t at = nk;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        keep[u] = is_gt[u] || (is_eq[u] && r < quota);
+        r += is_eq[u] ? 1u : 0u;
+        bk[u] = __ballot(keep[u]);
+        at += mbcnt(bk[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (keep[u]) stage[at++] = (uint32_t)(t + u);
+        nk += (uint32_t)__popcll(bk[u]);
+        eqr += (uint32_t)__popcll(be[u]);
+      }
+    }
+  }
+  if (lane == 0) sm.w_gt[wave] = nk;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) slot += sm.w_gt[w];
+  for (uint32_t i = lane; i < nk; i += WAVE)
+    if (slot + i < (uint32_t)n) dst[slot + i] = (int32_t)stage[i];
+}
+
 template <bool IN_LDS>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t keys_lds[IN_LDS ? LDS_KEYS : 4];
@@ -487,92 +572,13 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   };
   if (tid == 0) a.kept_count[head] = k;
   if (IN_LDS) {
-    constexpr int EPI = LDS_KEYS / NWV / (4 * WAVE);   // seg <= EPI * 256
     uint4 ek[EPI];
 #pragma unroll
     for (int j = 0; j < EPI; ++j) {
       const int t = s0 + j * 4 * WAVE + 4 * lane;
       ek[j] = t < s1 ? *reinterpret_cast<const uint4*>(&keys_lds[t]) : make_uint4(0u, 0u, 0u, 0u);
     }
-    // Every wave holds its segment's keys in registers, so after one barrier
-    // the key area of LDS is free: each wave compacts its kept indices into
-    // its own key range [s0, s1), then copies them out contiguously.
-    // When every key equal to T is kept (no tie to rank) the keep rule is
-    // key >= T; otherwise waves first count their equal keys for the ranks.
-    const bool all_ties = quota >= eq_total;
-    if (!all_ties) {
-      uint32_t eqw = 0;
-#pragma unroll
-      for (int j = 0; j < EPI; ++j) {
-        if (s0 + j * 4 * WAVE < s1) {
-          const int t = s0 + j * 4 * WAVE + 4 * lane;
-          const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            eqw += (uint32_t)__popcll(__ballot(t + u < s1 && kk[u] == T));
-        }
-      }
-      if (lane == 0) sm.w_eq[wave] = eqw;
-    }
-    __syncthreads();   // also: every wave holds its keys in registers now
-    if (!all_ties)
-      for (int w = 0; w < wave; ++w) eqr += sm.w_eq[w];   // ties before this wave
-    uint32_t* stage = keys_lds + s0;
-    uint32_t nk = 0;
-#pragma unroll
-    for (int j = 0; j < EPI; ++j) {
-      if (all_ties && s0 + j * 4 * WAVE < s1) {
-        const int t = s0 + j * 4 * WAVE + 4 * lane;
-        const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
-        uint32_t at = nk;
-        bool keep[4];
-        uint64_t bk[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          keep[u] = t + u < s1 && kk[u] >= T;
-          bk[u] = __ballot(keep[u]);
-          at += mbcnt(bk[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (keep[u]) stage[at++] = (uint32_t)(t + u);
-          nk += (uint32_t)__popcll(bk[u]);
-        }
-      } else if (s0 + j * 4 * WAVE < s1) {
-        const int t = s0 + j * 4 * WAVE + 4 * lane;
-        const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
-        bool is_gt[4], is_eq[4], keep[4];
-        uint64_t be[4], bk[4];
-        uint32_t r = eqr;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bool valid = t + u < s1;
-          is_gt[u] = valid && kk[u] > T;
-          is_eq[u] = valid && kk[u] == T;
-          be[u] = __ballot(is_eq[u]);
-          r += mbcnt(be[u]);
-        }
-        uint32_t at = nk;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          keep[u] = is_gt[u] || (is_eq[u] && r < quota);
-          r += is_eq[u] ? 1u : 0u;
-          bk[u] = __ballot(keep[u]);
-          at += mbcnt(bk[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (keep[u]) stage[at++] = (uint32_t)(t + u);
-          nk += (uint32_t)__popcll(bk[u]);
-          eqr += (uint32_t)__popcll(be[u]);
-        }
-      }
-    }
-    if (lane == 0) sm.w_gt[wave] = nk;
-    __syncthreads();
-    for (int w = 0; w < wave; ++w) slot += sm.w_gt[w];
-    for (uint32_t i = lane; i < nk; i += WAVE)
-      if (slot + i < (uint32_t)n) dst[slot + i] = (int32_t)stage[i];
+    emit_regs(ek, s0, s1, n, T, quota, eq_total, keys_lds, sm, dst);
   } else {
     // GU steps of the segment are loaded (16 bytes per lane each) before the
     // first is counted or written; s0 is a multiple of 256, so a lane's four
@@ -610,6 +616,115 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Selection from a precomputed top-digit histogram (kv_score_select): the
+// score kernel has counted the top DIGIT key bits of every score of the
+// head into hist[head][NBINS].  Count budgets (k, kept fraction) without
+// protected tokens, heads of at most LDS_KEYS tokens.  One workgroup per
+// head:
+//   1. the histogram gives the top digit b1 of the k-th key and the count of
+//      keys above it (the same scan as resolve_digit);
+//   2. each wave loads its segment's scores into registers as keys, and the
+//      keys whose top digit is b1 (the candidates, as many as the histogram
+//      counted in b1) are gathered into LDS;
+//   3. the descent resolves the remaining key bits over the candidates only;
+//   4. the emit runs from the registers, as select_kernel's does.
+// The k-th key T and the tie quota are those of select_kernel, so the kept
+// indices are the same.
+template <bool VEC>   // VEC: 16-byte aligned scores with N_max a multiple of 4
+__global__ __launch_bounds__(NT) void select_hist_kernel(SelectArgs a, const uint32_t* hist) {
+  __shared__ __attribute__((aligned(16))) uint32_t keys_lds[LDS_KEYS];
+  __shared__ Smem sm;
+  __shared__ uint32_t cand_n;
+  const int head = blockIdx.x, b = head / a.Hkv;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int n = a.ctx ? min(max(a.ctx[b], 0), a.N_max) : a.N_max;
+  if (n == 0) {
+    if (tid == 0) a.kept_count[head] = 0;
+    return;
+  }
+  const int k = count_budget(a.bud, head, n, 0u, 1, n);
+  const float* src = a.scores + (size_t)head * a.N_max;
+  const uint32_t* hh = hist + (size_t)head * NBINS;
+  // Every load below is issued before any is used (no branch between them:
+  // indices past the head are clamped onto it and the keys masked later).
+  static_assert(NBINS == 2 * NT, "two bins per thread");
+  const uint32_t h0 = hh[tid], h1 = hh[tid + NT];
+  // this wave's segment, loaded while the histogram is scanned
+  const int seg = ((n + NWV - 1) / NWV + 4 * WAVE - 1) / (4 * WAVE) * (4 * WAVE);
+  const int s0 = wave * seg, s1 = min(s0 + seg, n);
+  uint4 ek[EPI];
+  if constexpr (VEC) {
+    // whole 16-byte loads, clamped onto the head's row (N_max - 4 is aligned);
+    // tokens at or past n are masked by their index
+    uint4 v[EPI];
+#pragma unroll
+    for (int j = 0; j < EPI; ++j) v[j] = ld16(src + min(s0 + j * 4 * WAVE + 4 * lane, a.N_max - 4));
+#pragma unroll
+    for (int j = 0; j < EPI; ++j)
+      ek[j] = make_uint4(to_key(__uint_as_float(v[j].x)), to_key(__uint_as_float(v[j].y)),
+                         to_key(__uint_as_float(v[j].z)), to_key(__uint_as_float(v[j].w)));
+  } else {
+    float v[EPI][4];
+#pragma unroll
+    for (int j = 0; j < EPI; ++j)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[j][u] = src[min(s0 + j * 4 * WAVE + 4 * lane + u, n - 1)];
+#pragma unroll
+    for (int j = 0; j < EPI; ++j)
+      ek[j] = make_uint4(to_key(v[j][0]), to_key(v[j][1]), to_key(v[j][2]), to_key(v[j][3]));
+  }
+  sm.hist[tid] = h0;
+  sm.hist[tid + NT] = h1;
+  if (tid == 0) cand_n = 0u;
+  __syncthreads();
+  resolve_digit<false>(sm, NBINS, (unsigned long long)k);   // leaves sm.hist cleared
+  const uint32_t b1 = sm.bin, above1 = sm.cnt_above;
+
+  // candidates: this wave's count first, one LDS atomic per wave, then the writes
+  auto is_cand = [&](uint32_t kk, int t) { return t < s1 && (kk >> (32 - DIGIT)) == b1; };
+  uint32_t wc = 0;
+#pragma unroll
+  for (int j = 0; j < EPI; ++j) {
+    const int t = s0 + j * 4 * WAVE + 4 * lane;
+    wc += (uint32_t)__popcll(__ballot(is_cand(ek[j].x, t))) +
+          (uint32_t)__popcll(__ballot(is_cand(ek[j].y, t + 1))) +
+          (uint32_t)__popcll(__ballot(is_cand(ek[j].z, t + 2))) +
+          (uint32_t)__popcll(__ballot(is_cand(ek[j].w, t + 3)));
+  }
+  uint32_t at = 0;
+  if (lane == 0 && wc) at = atomicAdd(&cand_n, wc);
+  at = __builtin_amdgcn_readfirstlane(at);
+#pragma unroll
+  for (int j = 0; j < EPI; ++j) {
+    const int t = s0 + j * 4 * WAVE + 4 * lane;
+    const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool c = is_cand(kk[u], t + u);
+      const uint64_t bc = __ballot(c);
+      if (c) keys_lds[at + mbcnt(bc)] = kk[u];
+      at += (uint32_t)__popcll(bc);
+    }
+  }
+  __syncthreads();
+  const int nc = (int)cand_n;
+
+  // the remaining key bits over the candidates (all share the top digit b1)
+  uint32_t T, quota, eq_total = 0;
+  {
+    Keys<true> key{keys_lds, nullptr, 0, INT32_MAX};
+    uint32_t above;
+    unsigned long long rem;
+    auto nofx = [](uint32_t) { return 0ull; };
+    T = descend<false>(key, nc, DIGIT, b1 << (32 - DIGIT), (unsigned long long)(k - above1), sm,
+                       nofx, &above, &rem, false, &eq_total);
+    quota = (uint32_t)rem;
+  }
+  if (tid == 0) a.kept_count[head] = k;
+  emit_regs(ek, s0, s1, n, T, quota, eq_total, keys_lds, sm, a.kept_idx + (size_t)head * a.N_max);
+}
 
 // ---------------------------------------------------------------------------
 // Heads longer than LDS_KEYS tokens under a count budget.  One workgroup per
@@ -890,8 +1005,7 @@ void select_parts(const SelectArgs& s, int P, void* ws, hipStream_t st) {
 using namespace kvcc;
 
 extern "C" size_t kv_select_workspace_size(int B, int Hkv, int N_max) {
-  if (B < 1 || Hkv < 1 || N_max <= LDS_KEYS) return 0;
-  return part_workspace(B * Hkv, ceil_div(N_max, PT));
+  return select_part_workspace(B, Hkv, N_max);
 }
 
 extern "C" int kv_select(const float* scores, const int32_t* ctx_len,
@@ -906,6 +1020,19 @@ extern "C" int kv_select(const float* scores, const int32_t* ctx_len,
   if (B < 1 || Hkv < 1 || N_max < 1 || (int64_t)B * Hkv * N_max >= (int64_t(1) << 31))
     return KV_ERR_SHAPE;
   const kv_budget& bu = *budget;
+  if (const int st = check_budget(bu)) return st;
+
+  // Long heads under a count budget take the part path when the workspace
+  // is there (its size covers it whenever N_max > LDS_KEYS).
+  if (select_parts_launch(scores, ctx_len, B, Hkv, N_max, bu, kept_idx, kept_count, workspace,
+                          workspace_bytes, static_cast<hipStream_t>(stream)))
+    return launch_status();
+  select_launch(scores, ctx_len, nullptr, B, Hkv, N_max, bu, false, kept_idx, kept_count,
+                static_cast<hipStream_t>(stream), "select");
+  return launch_status();
+}
+
+int kvcc::check_budget(const kv_budget& bu) {
   if (bu.mode < KV_BUDGET_K || bu.mode > KV_BUDGET_MASS) return KV_ERR_MODE;
   if (!(bu.min_ratio >= 0.f && bu.min_ratio <= 1.f && bu.max_ratio >= 0.f && bu.max_ratio <= 1.f))
     return KV_ERR_MODE;
@@ -914,22 +1041,46 @@ extern "C" int kv_select(const float* scores, const int32_t* ctx_len,
   if (bu.mode == KV_BUDGET_MASS && !(bu.mass >= 0.f && bu.mass <= 1.f)) return KV_ERR_MODE;
   if (bu.mode == KV_BUDGET_THRESHOLD && isnan(bu.tau)) return KV_ERR_MODE;
   if (bu.n_sink < 0 || bu.n_recent < 0) return KV_ERR_MODE;
+  if (!aligned16(bu.k) || !aligned16(bu.ratio)) return KV_ERR_ALIGN;
+  return KV_OK;
+}
 
-  // Long heads under a count budget take the part path when the workspace
-  // is there (its size covers it whenever N_max > LDS_KEYS).
+size_t kvcc::select_part_workspace(int B, int Hkv, int N_max) {
+  if (B < 1 || Hkv < 1 || N_max <= LDS_KEYS) return 0;
+  return part_workspace(B * Hkv, ceil_div(N_max, PT));
+}
+
+bool kvcc::select_parts_launch(const float* scores, const int32_t* ctx, int B, int Hkv, int N_max,
+                               const kv_budget& bud, int32_t* kept_idx, int32_t* kept_count,
+                               void* workspace, size_t workspace_bytes, hipStream_t st) {
   const int P = ceil_div(N_max, PT);
-  if (N_max > LDS_KEYS && bu.mode != KV_BUDGET_MASS && workspace &&
-      workspace_bytes >= part_workspace(B * Hkv, P)) {
-    SelectArgs a;
-    a.scores = scores; a.ctx = ctx_len; a.n_head = nullptr; a.B = B; a.Hkv = Hkv; a.N_max = N_max;
-    a.k_zero_ok = 0;
-    a.bud = bu; a.kept_idx = kept_idx; a.kept_count = kept_count;
-    select_parts(a, P, workspace, static_cast<hipStream_t>(stream));
-    return launch_status();
-  }
-  select_launch(scores, ctx_len, nullptr, B, Hkv, N_max, bu, false, kept_idx, kept_count,
-                static_cast<hipStream_t>(stream), "select");
-  return launch_status();
+  if (N_max <= LDS_KEYS || bud.mode == KV_BUDGET_MASS || !workspace ||
+      workspace_bytes < part_workspace(B * Hkv, P))
+    return false;
+  SelectArgs a;
+  a.scores = scores; a.ctx = ctx; a.n_head = nullptr; a.B = B; a.Hkv = Hkv; a.N_max = N_max;
+  a.k_zero_ok = 0;
+  a.bud = bud; a.kept_idx = kept_idx; a.kept_count = kept_count;
+  select_parts(a, P, workspace, st);
+  return true;
+}
+
+bool kvcc::select_hist_eligible(const kv_budget& bud, int N_max) {
+  return N_max <= LDS_KEYS && (bud.mode == KV_BUDGET_K || bud.mode == KV_BUDGET_RATIO) &&
+         bud.n_sink == 0 && bud.n_recent == 0;
+}
+
+void kvcc::select_hist_launch(const float* scores, const int32_t* ctx, const uint32_t* hist, int B,
+                              int Hkv, int N_max, const kv_budget& bud, int32_t* kept_idx,
+                              int32_t* kept_count, hipStream_t st) {
+  SelectArgs a;
+  a.scores = scores; a.ctx = ctx; a.n_head = nullptr; a.B = B; a.Hkv = Hkv; a.N_max = N_max;
+  a.k_zero_ok = 0;
+  a.bud = bud; a.kept_idx = kept_idx; a.kept_count = kept_count;
+  if (aligned16(scores) && N_max % 4 == 0)
+    launch("select", select_hist_kernel<true>, dim3(B * Hkv), dim3(NT), 0, st, a, hist);
+  else
+    launch("select", select_hist_kernel<false>, dim3(B * Hkv), dim3(NT), 0, st, a, hist);
 }
 
 void kvcc::select_launch(const float* scores, const int32_t* ctx, const int32_t* n_head, int B,

@@ -190,3 +190,26 @@ def test_decode_noalloc_validation():
     assert L.kv_decode_workspace_size(64, 32, 8, 128, big) > 16 << 20
     assert L.kv_decode_attn_noalloc(P, P, P, P, 64, 32, 8, 128, 1, 0.0, big, P, None,
                                     None) == KV_ERR_WORKSPACE
+
+
+def test_score_select_validation():
+    L = _lib.lib()
+    assert L.kv_score_select_workspace_size(4, 32, 8, 32768, 64, 128) > \
+        L.kv_score_workspace_size(4, 32, 8, 32768, 64, 128)
+    assert L.kv_score_select_workspace_size(1, 32, 7, 100, 8, 128) == 0
+
+    def call(budget, **kw):
+        a = dict(q=P, k=P, s=P, idx=P, cnt=P, Hkv=4, d=64, dtype=1, ws=P, wsb=1 << 30)
+        a.update(kw)
+        return L.kv_score_select(a["q"], a["k"], None, ctypes.byref(budget), a["s"], None,
+                                 a["idx"], a["cnt"], 1, 4, a["Hkv"], 256, 8, a["d"], a["dtype"],
+                                 0, 0.0, a["ws"], a["wsb"], None)
+    B = _lib.KvBudget
+    ok = B(1, None, None, 0, 0.5, 0, 0, 0, 1)
+    assert call(ok, idx=None) == KV_ERR_NULL
+    assert call(ok, cnt=P + 4) == KV_ERR_ALIGN
+    assert call(ok, dtype=9) == KV_ERR_DTYPE
+    assert call(ok, d=48) == KV_ERR_SHAPE
+    assert call(B(7, None, None, 0, 0.5, 0, 0, 0, 1)) == KV_ERR_MODE
+    assert call(B(1, None, None, 0, 1.5, 0, 0, 0, 1)) == KV_ERR_MODE
+    assert call(ok, wsb=64) == KV_ERR_WORKSPACE

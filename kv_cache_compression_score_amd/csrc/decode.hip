@@ -30,6 +30,7 @@ constexpr int DT = 256;
 constexpr int CH = 256;          // rows per work item (two passes of NG*RPG rows)
 constexpr int RPG = 8;           // rows per lane group per pass over an item
 constexpr int MAX_HEADS = 4096;
+constexpr int GRID_MAX = 1024;   // most split workgroups per query-head group
 
 struct DecodeArgs {
   const void* q;
@@ -801,7 +802,10 @@ bool plan_decode(int B, int Hq, int Hkv, int d, int64_t cap, DecodePlan* p, bool
 template <typename T, int D, int GT, bool VEC>
 void launch_decode(const DecodeArgs& a, hipStream_t st) {
   const size_t dyn = (size_t)(a.B * a.Hkv + 1) * (sizeof(long long) + sizeof(int));
-  const dim3 grid((unsigned)std::min(a.items_max, 8192), a.n_sub);
+  // items_max bounds the items from the capacity; the real count (from the
+  // offsets, on the device) can be far smaller, so the grid stops at
+  // GRID_MAX workgroups (four per CU on 256 CUs) that stride over the items.
+  const dim3 grid((unsigned)std::min(a.items_max, GRID_MAX), a.n_sub);
   if constexpr (VEC) {
     launch("vector_decode_split", vector_decode_split<T, D, GT>, grid, dim3(DT), (uint32_t)dyn, st, a);
   } else {

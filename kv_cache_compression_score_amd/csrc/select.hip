@@ -149,6 +149,124 @@ __device__ __forceinline__ void for_keys(const Keys<IN_LDS>& key, int n, const F
   }
 }
 
+// Adds one key to the LDS histogram (its bin, and with MASS its fixed-point
+// mass) for every lane with `active`.  All lanes of the wave call it together.
+// Score keys can crowd into one bin (a Zipf key-norm profile puts 98% of a
+// head's keys in one top-digit bin), and LDS atomics that hit one address
+// serialise, so when at least AGG_MIN active lanes share the first active
+// lane's bin, one lane adds their count (and summed mass) for all of them.
+// The sums are integers, so the result does not depend on the grouping.
+constexpr int AGG_MIN = 8;
+template <bool MASS>
+__device__ __forceinline__ void hist_add(Smem& sm, bool active, int bin, unsigned long long m) {
+  const uint64_t act = __ballot(active);
+  if (act == 0) return;
+  const int lead = __builtin_ctzll(act);
+  const int b0 = __builtin_amdgcn_readlane(bin, lead);
+  const bool same = active && bin == b0;
+  const uint64_t ms = __ballot(same);
+  const uint32_t c = (uint32_t)__popcll(ms);
+  const int lane = threadIdx.x & (WAVE - 1);
+  if (c >= (uint32_t)AGG_MIN) {
+    if (MASS) {
+      const unsigned long long tot = last_lane(wave_scan_add_u64(same ? m : 0ull));
+      if (lane == lead) atomicAdd(&sm.hmass[b0], tot);
+    }
+    if (lane == lead) atomicAdd(&sm.hist[b0], c);
+    if (active && !same) {
+      atomicAdd(&sm.hist[bin], 1u);
+      if (MASS) atomicAdd(&sm.hmass[bin], m);
+    }
+  } else if (active) {
+    atomicAdd(&sm.hist[bin], 1u);
+    if (MASS) atomicAdd(&sm.hmass[bin], m);
+  }
+}
+
+// A wave's histogram adds over one pass: the bin of the wave's first key
+// (hb, wave-uniform) is counted in registers, lane by lane, and added once
+// at the end (flush); other bins go through hist_add.  With one bin holding
+// most keys this leaves that bin no LDS atomic and no wave reduction per
+// step.  Every lane calls add at every step and flush once.
+template <bool MASS>
+struct HistAcc {
+  int hb = -1;
+  uint32_t c = 0;
+  unsigned long long m = 0;
+  __device__ __forceinline__ void add(Smem& sm, bool active, int bin, unsigned long long mass) {
+    if (hb < 0) {
+      const uint64_t act = __ballot(active);
+      if (act == 0) return;
+      hb = __builtin_amdgcn_readlane(bin, __builtin_ctzll(act));
+    }
+    const bool hot = active && bin == hb;
+    if (hot) {
+      ++c;
+      if (MASS) m += mass;
+    }
+    hist_add<MASS>(sm, active && !hot, bin, mass);
+  }
+  __device__ __forceinline__ void flush(Smem& sm) {
+    if (hb < 0) return;
+    const uint32_t cs = last_lane(wave_scan_u32(c, 0u, OpAdd()));
+    const unsigned long long ms = MASS ? last_lane(wave_scan_add_u64(m)) : 0ull;
+    if ((threadIdx.x & (WAVE - 1)) == 0) {
+      if (cs) atomicAdd(&sm.hist[hb], cs);
+      if (MASS && ms) atomicAdd(&sm.hmass[hb], ms);
+    }
+  }
+};
+
+// As for_keys, but every lane calls f(key, valid) at every step (no branch
+// around the call), so f may use wave-wide operations such as hist_add.
+template <bool IN_LDS, class F>
+__device__ __forceinline__ void for_keys_all(const Keys<IN_LDS>& key, int n, const F& f) {
+  const int tid = threadIdx.x;
+  const int n4 = n >> 2;
+  if (IN_LDS) {
+    constexpr int PER = LDS_KEYS / 4 / NT;   // n <= LDS_KEYS
+    const uint4* k4 = reinterpret_cast<const uint4*>(key.lds);
+    uint4 v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + u * NT;
+      v[u] = i < n4 ? k4[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const int wbase = tid & ~(WAVE - 1);   // the wave's first thread
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      if (wbase + u * NT >= n4) break;   // no lane of this wave has a key left (uniform)
+      const bool ok = tid + u * NT < n4;
+      f(v[u].x, ok); f(v[u].y, ok); f(v[u].z, ok); f(v[u].w, ok);
+    }
+    const int t = 4 * n4 + tid;   // the last n % 4 keys (fewer than NT)
+    if (wbase + 4 * n4 < n) f(t < n ? key.lds[t] : 0u, t < n);
+  } else {
+    const float* g = key.g;
+    const int m4 = (reinterpret_cast<uintptr_t>(g) & 15) == 0 ? n4 : 0;
+    const float4* g4 = reinterpret_cast<const float4*>(g);
+    for (int i0 = 0; i0 < m4; i0 += GU * NT) {
+      float4 v[GU];
+#pragma unroll
+      for (int u = 0; u < GU; ++u) {
+        const int i = i0 + tid + u * NT;
+        v[u] = i < m4 ? g4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < GU; ++u) {
+        const int i = i0 + tid + u * NT;
+        const bool ok = i < m4;
+        const uint4 k = key.four(v[u], 4 * i);
+        f(k.x, ok); f(k.y, ok); f(k.z, ok); f(k.w, ok);
+      }
+    }
+    for (int t0 = 4 * m4; t0 < n; t0 += NT) {   // uniform trip count
+      const int t = t0 + tid;
+      f(t < n ? key(t) : 0u, t < n);
+    }
+  }
+}
+
 // One digit of a radix descent: sm.hist (and, with MASS, sm.hmass) hold the
 // digit's nb bins (nb even, at most 2 * NT).  Finds the bin at which the
 // top-down total (counts, or masses with MASS) reaches rem (1 <= rem <= the
@@ -210,7 +328,9 @@ __device__ void resolve_digit(Smem& sm, int nb, unsigned long long rem) {
 // On entry sm.hist (and, with MASS, sm.hmass) are zero; on exit too.  The
 // sm.bin/cnt_above/mass_above reads of one digit all precede the next
 // digit's first barrier, so one set of fields serves every digit.
-template <bool MASS, bool IN_LDS, class FX>
+// REG: count the wave's first-key bin in registers (HistAcc), for key sets
+// that may crowd into one bin; otherwise every key goes through hist_add.
+template <bool MASS, bool IN_LDS, class FX, bool REG = true>
 __device__ uint32_t descend(const Keys<IN_LDS>& key, int n, int cp, uint32_t lo_key,
                             unsigned long long rem, Smem& sm, const FX& fx,
                             uint32_t* cnt_above_out, unsigned long long* rem_out,
@@ -226,13 +346,18 @@ __device__ uint32_t descend(const Keys<IN_LDS>& key, int n, int cp, uint32_t lo_
     const int bits = min(DIGIT, left);
     const int shift = left - bits;
     const int nb = 1 << bits;
-    if (!ready) {
-      for_keys(key, n, [&](uint32_t kk) {
-        if ((kk & pmask) == prefix) {
-          const int bin = (kk >> shift) & (nb - 1);
-          atomicAdd(&sm.hist[bin], 1u);
-          if (MASS) atomicAdd(&sm.hmass[bin], fx(kk));
-        }
+    if (!ready && REG) {
+      HistAcc<MASS> acc;
+      for_keys_all(key, n, [&](uint32_t kk, bool valid) {
+        const bool in = valid && (kk & pmask) == prefix;
+        acc.add(sm, in, (int)((kk >> shift) & (uint32_t)(nb - 1)), MASS && in ? fx(kk) : 0ull);
+      });
+      acc.flush(sm);
+    } else if (!ready) {
+      for_keys_all(key, n, [&](uint32_t kk, bool valid) {
+        const bool in = valid && (kk & pmask) == prefix;
+        hist_add<MASS>(sm, in, (int)((kk >> shift) & (uint32_t)(nb - 1)),
+                       MASS && in ? fx(kk) : 0ull);
       });
     }
     ready = false;
@@ -403,13 +528,18 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   double tot = 0.0;
   // Count budgets also histogram the top DIGIT key bits here (the first digit
   // of the descent), which saves one sweep over the keys.
-  auto visit = [&](uint32_t kr, bool prot) -> uint32_t {
+  // (every lane of a wave calls visit at every step: the histogram add is
+  // wave-wide)
+  HistAcc<false> acc;
+  auto visit = [&](uint32_t kr, bool prot, bool valid) -> uint32_t {
     const uint32_t kk = prot ? PROTECTED_KEY : kr;
-    mn = min(mn, kk);
-    mx = max(mx, kk);
-    cnt += kk >= tk ? 1u : 0u;
-    if (mass) tot += (double)from_key(kr);
-    else atomicAdd(&sm.hist[kk >> (32 - DIGIT)], 1u);
+    if (valid) {
+      mn = min(mn, kk);
+      mx = max(mx, kk);
+      cnt += kk >= tk ? 1u : 0u;
+      if (mass) tot += (double)from_key(kr);
+    }
+    acc.add(sm, valid && !mass, (int)(kk >> (32 - DIGIT)), 0ull);
     return kk;
   };
   for (int i = tid; i < NBINS; i += NT) { sm.hist[i] = 0; sm.hmass[i] = 0; }
@@ -427,20 +557,48 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int i = tid + u * NT;
-      if (i < n4) {
-        const int t = 4 * i;
-        const uint32_t k0 = visit(to_key(v[u].x), is_prot(t));
-        const uint32_t k1 = visit(to_key(v[u].y), is_prot(t + 1));
-        const uint32_t k2 = visit(to_key(v[u].z), is_prot(t + 2));
-        const uint32_t k3 = visit(to_key(v[u].w), is_prot(t + 3));
-        *reinterpret_cast<uint4*>(&keys_lds[t]) = make_uint4(k0, k1, k2, k3);
-      }
+      const bool ok = i < n4;
+      const int t = 4 * i;
+      const uint32_t k0 = visit(to_key(v[u].x), is_prot(t), ok);
+      const uint32_t k1 = visit(to_key(v[u].y), is_prot(t + 1), ok);
+      const uint32_t k2 = visit(to_key(v[u].z), is_prot(t + 2), ok);
+      const uint32_t k3 = visit(to_key(v[u].w), is_prot(t + 3), ok);
+      if (ok) *reinterpret_cast<uint4*>(&keys_lds[t]) = make_uint4(k0, k1, k2, k3);
     }
-    for (int t = 4 * n4 + tid; t < n; t += NT) keys_lds[t] = visit(to_key(src[t]), is_prot(t));
+    for (int t0 = 4 * n4; t0 < n; t0 += NT) {   // uniform trip count
+      const int t = t0 + tid;
+      const bool ok = t < n;
+      const uint32_t kk = visit(to_key(ok ? src[t] : 0.f), is_prot(t), ok);
+      if (ok) keys_lds[t] = kk;
+    }
   } else {
     __syncthreads();
-    for_scores(src, n, [&](float x, int t) { visit(to_key(x), is_prot(t)); });
+    const int m4 = (reinterpret_cast<uintptr_t>(src) & 15) == 0 ? n >> 2 : 0;
+    const float4* g4 = reinterpret_cast<const float4*>(src);
+    for (int i0 = 0; i0 < m4; i0 += GU * NT) {
+      float4 v[GU];
+#pragma unroll
+      for (int u = 0; u < GU; ++u) {
+        const int i = i0 + tid + u * NT;
+        v[u] = i < m4 ? g4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < GU; ++u) {
+        const int i = i0 + tid + u * NT;
+        const bool ok = i < m4;
+        visit(to_key(v[u].x), is_prot(4 * i), ok);
+        visit(to_key(v[u].y), is_prot(4 * i + 1), ok);
+        visit(to_key(v[u].z), is_prot(4 * i + 2), ok);
+        visit(to_key(v[u].w), is_prot(4 * i + 3), ok);
+      }
+    }
+    for (int t0 = 4 * m4; t0 < n; t0 += NT) {   // uniform trip count
+      const int t = t0 + tid;
+      const bool ok = t < n;
+      visit(to_key(ok ? src[t] : 0.f), is_prot(t), ok);
+    }
   }
+  acc.flush(sm);   // before the barrier below
   mn = last_lane(wave_scan_u32(mn, 0xffffffffu, OpMin()));
   mx = last_lane(wave_scan_u32(mx, 0u, OpMax()));
   cnt = last_lane(wave_scan_u32(cnt, 0u, OpAdd()));
@@ -718,8 +876,11 @@ __global__ __launch_bounds__(NT) void select_hist_kernel(SelectArgs a, const uin
     uint32_t above;
     unsigned long long rem;
     auto nofx = [](uint32_t) { return 0ull; };
-    T = descend<false>(key, nc, DIGIT, b1 << (32 - DIGIT), (unsigned long long)(k - above1), sm,
-                       nofx, &above, &rem, false, &eq_total);
+    // the candidates already share their top digit: plain adds (hist_add
+    // still aggregates a crowded bin)
+    T = descend<false, true, decltype(nofx), false>(key, nc, DIGIT, b1 << (32 - DIGIT),
+                                                    (unsigned long long)(k - above1), sm, nofx,
+                                                    &above, &rem, false, &eq_total);
     quota = (uint32_t)rem;
   }
   if (tid == 0) a.kept_count[head] = k;

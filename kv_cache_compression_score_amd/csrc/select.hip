@@ -183,11 +183,12 @@ __device__ __forceinline__ void hist_add(Smem& sm, bool active, int bin, unsigne
   }
 }
 
-// A wave's histogram adds over one pass: the bin of the wave's first key
-// (hb, wave-uniform) is counted in registers, lane by lane, and added once
-// at the end (flush); other bins go through hist_add.  With one bin holding
-// most keys this leaves that bin no LDS atomic and no wave reduction per
-// step.  Every lane calls add at every step and flush once.
+// A wave's histogram adds over one pass when its keys crowd into one bin
+// (see crowded below): the bin of the wave's first key (hb, wave-uniform) is
+// counted in registers, lane by lane, and added once at the end (flush);
+// other bins go through hist_add.  With one bin holding most keys this
+// leaves that bin no LDS atomic and no wave reduction per step.  Every lane
+// calls add at every step and flush once.
 template <bool MASS>
 struct HistAcc {
   int hb = -1;
@@ -216,6 +217,19 @@ struct HistAcc {
     }
   }
 };
+
+// Whether a wave's keys crowd into one bin: at least AGG_MODE of the 64
+// sampled keys (one per lane, `in` marking those that take part) share the
+// first one's bin.  Wave-uniform; decides, per wave and pass, between one
+// LDS atomic per key (diverse bins: nothing else is as cheap) and the
+// aggregating adds above.
+constexpr int AGG_MODE = 24;
+__device__ __forceinline__ bool crowded(bool in, int bin) {
+  const uint64_t act = __ballot(in);
+  if (act == 0) return false;
+  const int b0 = __builtin_amdgcn_readlane(bin, __builtin_ctzll(act));
+  return __popcll(__ballot(in && bin == b0)) >= AGG_MODE;
+}
 
 // As for_keys, but every lane calls f(key, valid) at every step (no branch
 // around the call), so f may use wave-wide operations such as hist_add.
@@ -331,7 +345,7 @@ __device__ void resolve_digit(Smem& sm, int nb, unsigned long long rem) {
 // REG: count the wave's first-key bin in registers (HistAcc), for key sets
 // that may crowd into one bin; otherwise every key goes through hist_add.
 template <bool MASS, bool IN_LDS, class FX, bool REG = true>
-__device__ uint32_t descend(const Keys<IN_LDS>& key, int n, int cp, uint32_t lo_key,
+__device__ __forceinline__ uint32_t descend(const Keys<IN_LDS>& key, int n, int cp, uint32_t lo_key,
                             unsigned long long rem, Smem& sm, const FX& fx,
                             uint32_t* cnt_above_out, unsigned long long* rem_out,
                             bool top_ready = false, uint32_t* eq_out = nullptr) {
@@ -346,13 +360,28 @@ __device__ uint32_t descend(const Keys<IN_LDS>& key, int n, int cp, uint32_t lo_
     const int bits = min(DIGIT, left);
     const int shift = left - bits;
     const int nb = 1 << bits;
-    if (!ready && REG) {
+    bool crowd = false;
+    if (!ready && REG) {   // sample: each lane's first key of the pass
+      const int t = 4 * (int)threadIdx.x;
+      const uint32_t kk = t < n ? key(t) : 0u;
+      const bool in = t < n && (kk & pmask) == prefix;
+      crowd = crowded(in, (int)((kk >> shift) & (uint32_t)(nb - 1)));
+    }
+    if (!ready && crowd) {
       HistAcc<MASS> acc;
       for_keys_all(key, n, [&](uint32_t kk, bool valid) {
         const bool in = valid && (kk & pmask) == prefix;
         acc.add(sm, in, (int)((kk >> shift) & (uint32_t)(nb - 1)), MASS && in ? fx(kk) : 0ull);
       });
       acc.flush(sm);
+    } else if (!ready && REG) {
+      for_keys(key, n, [&](uint32_t kk) {
+        if ((kk & pmask) == prefix) {
+          const int bin = (kk >> shift) & (nb - 1);
+          atomicAdd(&sm.hist[bin], 1u);
+          if (MASS) atomicAdd(&sm.hmass[bin], fx(kk));
+        }
+      });
     } else if (!ready) {
       for_keys_all(key, n, [&](uint32_t kk, bool valid) {
         const bool in = valid && (kk & pmask) == prefix;
@@ -412,7 +441,7 @@ __device__ __forceinline__ int count_budget(const kv_budget& bu, int head, int n
 // keys, which the first barrier below ensures).  Keeps key > T, and the first
 // `quota` keys equal to T (eq_total of them in the head), ascending.
 constexpr int EPI = LDS_KEYS / NWV / (4 * WAVE);   // register steps per lane (seg <= EPI * 256)
-__device__ void emit_regs(const uint4 (&ek)[EPI], int s0, int s1, int n, uint32_t T,
+__device__ __forceinline__ void emit_regs(const uint4 (&ek)[EPI], int s0, int s1, int n, uint32_t T,
                           uint32_t quota, uint32_t eq_total, uint32_t* keys_lds, Smem& sm,
                           int32_t* dst) {
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
@@ -527,22 +556,31 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   uint32_t mn = 0xffffffffu, mx = 0u, cnt = 0u;
   double tot = 0.0;
   // Count budgets also histogram the top DIGIT key bits here (the first digit
-  // of the descent), which saves one sweep over the keys.
-  // (every lane of a wave calls visit at every step: the histogram add is
-  // wave-wide)
+  // of the descent), which saves one sweep over the keys.  A wave whose keys
+  // crowd into one bin (sampled from its first keys) aggregates its adds
+  // (HistAcc, every lane calling visit at every step); other waves take one
+  // LDS atomic per key.
+  for (int i = tid; i < NBINS; i += NT) { sm.hist[i] = 0; sm.hmass[i] = 0; }
   HistAcc<false> acc;
-  auto visit = [&](uint32_t kr, bool prot, bool valid) -> uint32_t {
+  auto stats = [&](uint32_t kr, bool prot) -> uint32_t {
     const uint32_t kk = prot ? PROTECTED_KEY : kr;
-    if (valid) {
-      mn = min(mn, kk);
-      mx = max(mx, kk);
-      cnt += kk >= tk ? 1u : 0u;
-      if (mass) tot += (double)from_key(kr);
-    }
+    mn = min(mn, kk);
+    mx = max(mx, kk);
+    cnt += kk >= tk ? 1u : 0u;
+    if (mass) tot += (double)from_key(kr);
+    return kk;
+  };
+  auto visit = [&](uint32_t kr, bool prot) -> uint32_t {   // one atomic per key
+    const uint32_t kk = stats(kr, prot);
+    if (!mass) atomicAdd(&sm.hist[kk >> (32 - DIGIT)], 1u);
+    return kk;
+  };
+  auto visit_all = [&](uint32_t kr, bool prot, bool valid) -> uint32_t {   // aggregating
+    const uint32_t kk = prot ? PROTECTED_KEY : kr;
+    if (valid) stats(kr, prot);
     acc.add(sm, valid && !mass, (int)(kk >> (32 - DIGIT)), 0ull);
     return kk;
   };
-  for (int i = tid; i < NBINS; i += NT) { sm.hist[i] = 0; sm.hmass[i] = 0; }
   if (IN_LDS) {
     constexpr int PER = LDS_KEYS / 4 / NT;
     const int n4 = ((a.N_max & 3) == 0) ? n >> 2 : 0;
@@ -553,52 +591,76 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       const int i = tid + u * NT;
       v[u] = i < n4 ? src4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    const bool crowd = !mass && crowded(tid < n4, (int)(to_key(v[0].x) >> (32 - DIGIT)));
     __syncthreads();   // histogram cleared before the first count (loads in flight)
+    if (crowd) {
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int i = tid + u * NT;
-      const bool ok = i < n4;
-      const int t = 4 * i;
-      const uint32_t k0 = visit(to_key(v[u].x), is_prot(t), ok);
-      const uint32_t k1 = visit(to_key(v[u].y), is_prot(t + 1), ok);
-      const uint32_t k2 = visit(to_key(v[u].z), is_prot(t + 2), ok);
-      const uint32_t k3 = visit(to_key(v[u].w), is_prot(t + 3), ok);
-      if (ok) *reinterpret_cast<uint4*>(&keys_lds[t]) = make_uint4(k0, k1, k2, k3);
-    }
-    for (int t0 = 4 * n4; t0 < n; t0 += NT) {   // uniform trip count
-      const int t = t0 + tid;
-      const bool ok = t < n;
-      const uint32_t kk = visit(to_key(ok ? src[t] : 0.f), is_prot(t), ok);
-      if (ok) keys_lds[t] = kk;
+      for (int u = 0; u < PER; ++u) {
+        const int i = tid + u * NT;
+        const bool ok = i < n4;
+        const int t = 4 * i;
+        const uint32_t k0 = visit_all(to_key(v[u].x), is_prot(t), ok);
+        const uint32_t k1 = visit_all(to_key(v[u].y), is_prot(t + 1), ok);
+        const uint32_t k2 = visit_all(to_key(v[u].z), is_prot(t + 2), ok);
+        const uint32_t k3 = visit_all(to_key(v[u].w), is_prot(t + 3), ok);
+        if (ok) *reinterpret_cast<uint4*>(&keys_lds[t]) = make_uint4(k0, k1, k2, k3);
+      }
+      for (int t0 = 4 * n4; t0 < n; t0 += NT) {   // uniform trip count
+        const int t = t0 + tid;
+        const bool ok = t < n;
+        const uint32_t kk = visit_all(to_key(ok ? src[t] : 0.f), is_prot(t), ok);
+        if (ok) keys_lds[t] = kk;
+      }
+      acc.flush(sm);
+    } else {
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int i = tid + u * NT;
+        if (i < n4) {
+          const int t = 4 * i;
+          const uint32_t k0 = visit(to_key(v[u].x), is_prot(t));
+          const uint32_t k1 = visit(to_key(v[u].y), is_prot(t + 1));
+          const uint32_t k2 = visit(to_key(v[u].z), is_prot(t + 2));
+          const uint32_t k3 = visit(to_key(v[u].w), is_prot(t + 3));
+          *reinterpret_cast<uint4*>(&keys_lds[t]) = make_uint4(k0, k1, k2, k3);
+        }
+      }
+      for (int t = 4 * n4 + tid; t < n; t += NT) keys_lds[t] = visit(to_key(src[t]), is_prot(t));
     }
   } else {
+    const bool crowd = !mass && crowded(4 * tid < n, (int)(to_key(4 * tid < n ? src[4 * tid] : 0.f) >>
+                                                        (32 - DIGIT)));
     __syncthreads();
-    const int m4 = (reinterpret_cast<uintptr_t>(src) & 15) == 0 ? n >> 2 : 0;
-    const float4* g4 = reinterpret_cast<const float4*>(src);
-    for (int i0 = 0; i0 < m4; i0 += GU * NT) {
-      float4 v[GU];
+    if (crowd) {
+      const int m4 = (reinterpret_cast<uintptr_t>(src) & 15) == 0 ? n >> 2 : 0;
+      const float4* g4 = reinterpret_cast<const float4*>(src);
+      for (int i0 = 0; i0 < m4; i0 += GU * NT) {
+        float4 v[GU];
 #pragma unroll
-      for (int u = 0; u < GU; ++u) {
-        const int i = i0 + tid + u * NT;
-        v[u] = i < m4 ? g4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+        for (int u = 0; u < GU; ++u) {
+          const int i = i0 + tid + u * NT;
+          v[u] = i < m4 ? g4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
 #pragma unroll
-      for (int u = 0; u < GU; ++u) {
-        const int i = i0 + tid + u * NT;
-        const bool ok = i < m4;
-        visit(to_key(v[u].x), is_prot(4 * i), ok);
-        visit(to_key(v[u].y), is_prot(4 * i + 1), ok);
-        visit(to_key(v[u].z), is_prot(4 * i + 2), ok);
-        visit(to_key(v[u].w), is_prot(4 * i + 3), ok);
+        for (int u = 0; u < GU; ++u) {
+          const int i = i0 + tid + u * NT;
+          const bool ok = i < m4;
+          visit_all(to_key(v[u].x), is_prot(4 * i), ok);
+          visit_all(to_key(v[u].y), is_prot(4 * i + 1), ok);
+          visit_all(to_key(v[u].z), is_prot(4 * i + 2), ok);
+          visit_all(to_key(v[u].w), is_prot(4 * i + 3), ok);
+        }
       }
-    }
-    for (int t0 = 4 * m4; t0 < n; t0 += NT) {   // uniform trip count
-      const int t = t0 + tid;
-      const bool ok = t < n;
-      visit(to_key(ok ? src[t] : 0.f), is_prot(t), ok);
+      for (int t0 = 4 * m4; t0 < n; t0 += NT) {   // uniform trip count
+        const int t = t0 + tid;
+        const bool ok = t < n;
+        visit_all(to_key(ok ? src[t] : 0.f), is_prot(t), ok);
+      }
+      acc.flush(sm);
+    } else {
+      for_scores(src, n, [&](float x, int t) { visit(to_key(x), is_prot(t)); });
     }
   }
-  acc.flush(sm);   // before the barrier below
   mn = last_lane(wave_scan_u32(mn, 0xffffffffu, OpMin()));
   mx = last_lane(wave_scan_u32(mx, 0u, OpMax()));
   cnt = last_lane(wave_scan_u32(cnt, 0u, OpAdd()));

@@ -192,8 +192,10 @@ int kv_select(const float* scores, const int32_t* ctx_len,
  * the budgeted per-head selection that evicts the low scorers.  Under a k or
  * kept-fraction budget with no protected tokens and N_max <= 32768 the
  * second score sweep also counts each head's scores by their top 11 key
- * bits, so the selection starts from that histogram and ranks only the
- * scores that share the k-th score's top bits.
+ * bits, so the selection starts from that histogram and resolves the lower
+ * key bits from the scores it holds in registers.  The scores of finite
+ * inputs are sums of exponentials (never negative), on which both orders
+ * agree; NaN inputs are outside the contract, as for kv_select.
  *
  * Arguments as kv_score (q_win ... scale) and kv_select (budget, kept_idx,
  * kept_count); workspace: kv_score_select_workspace_size() bytes (one

@@ -76,6 +76,14 @@ __device__ __forceinline__ uint32_t to_key(float s) {
 __device__ __forceinline__ float from_key(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
+// The same key for the scores the score kernels write, in one instruction:
+// those scores are sums of exponentials (+0.0 or positive, never -0.0 or
+// negative), and for these to_key only sets the top bit.  The score pass's
+// key histogram and the selection that reads it both use this mapping, so
+// the two agree on any value the pass can write.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  return __float_as_uint(s) | 0x80000000u;
+}
 // Bins of the top-digit key histogram (its top KEY_DIGIT bits).
 constexpr int KEY_DIGIT = 11;
 constexpr int KEY_BINS = 1 << KEY_DIGIT;

@@ -575,7 +575,7 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
 #pragma unroll
         for (int w2 = 0; w2 < NW; ++w2) s += red[tile % 3][w2][tid];
         a.scores[(size_t)head * a.N_max + t] = s;
-        if (a.hist) atomicAdd(&khist[to_key(s) >> (32 - KEY_DIGIT)], 1u);
+        if (a.hist) atomicAdd(&khist[score_key(s) >> (32 - KEY_DIGIT)], 1u);
       }
     }
   };

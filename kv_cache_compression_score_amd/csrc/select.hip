@@ -42,6 +42,12 @@ namespace {
 
 constexpr int NT = 1024;
 constexpr int NWV = NT / WAVE;
+
+// The calling thread's wave as a wave-uniform value (an SGPR), so that
+// conditions on it and on what derives from it branch instead of masking lanes.
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane((int)threadIdx.x / WAVE);
+}
 constexpr int LDS_KEYS = 32768;
 constexpr int NBINS = KEY_BINS;
 constexpr int DIGIT = KEY_DIGIT;
@@ -290,8 +296,8 @@ __device__ __forceinline__ void for_keys_all(const Keys<IN_LDS>& key, int n, con
 // nb-2-2t): it reads and clears them; a DPP wave scan and the wave totals
 // locate the bin.  All threads must call it.
 template <bool MASS>
-__device__ void resolve_digit(Smem& sm, int nb, unsigned long long rem) {
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+__device__ __forceinline__ void resolve_digit(Smem& sm, int nb, unsigned long long rem) {
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = wave_index();
   const int p0 = 2 * tid;
   uint32_t c0 = 0, c1 = 0;
   unsigned long long m0 = 0, m1 = 0;
@@ -316,14 +322,21 @@ __device__ void resolve_digit(Smem& sm, int nb, unsigned long long rem) {
     incl_c = wave_scan_u32(own_c, 0u, OpAdd());
     incl = incl_c;
   }
-  if (lane == WAVE - 1) { sm.f_m[wave] = incl; sm.f_c[wave] = incl_c; }
+  if (lane == WAVE - 1) {
+    if (MASS) sm.f_m[wave] = incl;
+    sm.f_c[wave] = incl_c;
+  }
   __syncthreads();
   unsigned long long wb = 0;
   uint32_t wbc = 0;
 #pragma unroll
   for (int w = 0; w < NWV; ++w) {
-    if (w < wave) { wb += sm.f_m[w]; wbc += sm.f_c[w]; }
+    if (w < wave) {
+      if (MASS) wb += sm.f_m[w];
+      wbc += sm.f_c[w];
+    }
   }
+  if (!MASS) wb = wbc;
   const unsigned long long before = wb + incl - own;
   if (before < rem && rem <= before + own) {   // exactly one thread
     const bool first = before + m0 >= rem;      // then m0 > 0
@@ -434,94 +447,155 @@ __device__ __forceinline__ int count_budget(const kv_budget& bu, int head, int n
   return min(max((int)cnt, lo), hi);   // threshold
 }
 
+constexpr int EPI = LDS_KEYS / NWV / (4 * WAVE);   // register steps per lane (seg <= EPI * 256)
+
+// One digit's histogram over a wave's register-held keys (segment [s0, s1),
+// key u of step j at token s0 + 256 j + 4 lane + u): keys whose bits from
+// `hi` up equal `prefix` add one to bin (key >> lo) of the bits below `hi`.
+// A step in which no lane has a matching key costs two VALU instructions
+// per key and a branch (the lower digits match a few keys of a head); a
+// wave whose sampled keys crowd into one bin aggregates its adds instead.
+__device__ __forceinline__ void count_regs(const uint4 (&ek)[EPI], int s0, int s1, int hi, int lo,
+                                           uint32_t prefix, Smem& sm) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const uint32_t bmask = (1u << (hi - lo)) - 1u;
+  const bool in0 = s0 + 4 * lane < s1 && (ek[0].x >> hi) == prefix;
+  if (crowded(in0, (int)((ek[0].x >> lo) & bmask))) {
+    HistAcc<false> acc;
+#pragma unroll
+    for (int j = 0; j < EPI; ++j) {
+      if (s0 + j * 4 * WAVE >= s1) break;   // uniform
+      const int t = s0 + j * 4 * WAVE + 4 * lane;
+      const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        acc.add(sm, t + u < s1 && (kk[u] >> hi) == prefix, (int)((kk[u] >> lo) & bmask), 0ull);
+    }
+    acc.flush(sm);
+    return;
+  }
+  // one step of 4 keys per lane; a full step (all 256 keys in the segment)
+  // takes its own copy, whose masks are plain compares
+  auto step = [&](const uint32_t (&kk)[4], bool m0, bool m1, bool m2, bool m3) {
+    if ((__ballot(m0) | __ballot(m1) | __ballot(m2) | __ballot(m3)) == 0) return;   // uniform
+    if (m0) atomicAdd(&sm.hist[(kk[0] >> lo) & bmask], 1u);
+    if (m1) atomicAdd(&sm.hist[(kk[1] >> lo) & bmask], 1u);
+    if (m2) atomicAdd(&sm.hist[(kk[2] >> lo) & bmask], 1u);
+    if (m3) atomicAdd(&sm.hist[(kk[3] >> lo) & bmask], 1u);
+  };
+#pragma unroll
+  for (int j = 0; j < EPI; ++j) {
+    const int base = s0 + j * 4 * WAVE;
+    if (base >= s1) break;   // uniform
+    const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
+    if (base + 4 * WAVE <= s1) {
+      step(kk, (kk[0] >> hi) == prefix, (kk[1] >> hi) == prefix, (kk[2] >> hi) == prefix,
+           (kk[3] >> hi) == prefix);
+    } else {
+      const int left = s1 - base - 4 * lane;   // this lane's keys left in the segment
+      step(kk, left > 0 && (kk[0] >> hi) == prefix, left > 1 && (kk[1] >> hi) == prefix,
+           left > 2 && (kk[2] >> hi) == prefix, left > 3 && (kk[3] >> hi) == prefix);
+    }
+  }
+}
+
 // Emit of the kept indices from keys held in registers: wave w holds the
 // keys of its segment [s0, s1) (seg a multiple of 256, four consecutive
 // tokens per lane per step) in ek.  keys_lds is free LDS of at least n words
-// (its old contents are no longer needed by any wave once each holds its
-// keys, which the first barrier below ensures).  Keeps key > T, and the first
+// once every wave holds its keys; LDS_BUSY: other waves may still read it
+// on entry (then a barrier comes first).  Keeps key > T, and the first
 // `quota` keys equal to T (eq_total of them in the head), ascending.
-constexpr int EPI = LDS_KEYS / NWV / (4 * WAVE);   // register steps per lane (seg <= EPI * 256)
+// Each step ranks its kept keys with one ballot per key and chained
+// v_mbcnt; a full step (all 256 keys in the segment) takes its own copy of
+// the step, whose masks are plain compares.
+template <bool LDS_BUSY>
 __device__ __forceinline__ void emit_regs(const uint4 (&ek)[EPI], int s0, int s1, int n, uint32_t T,
-                          uint32_t quota, uint32_t eq_total, uint32_t* keys_lds, Smem& sm,
-                          int32_t* dst) {
-  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
-  uint32_t slot = 0, eqr = 0;
-  // Every wave holds its segment's keys in registers, so after one barrier
-  // the key area of LDS is free: each wave compacts its kept indices into
-  // its own key range [s0, s1), then copies them out contiguously.
+                                          uint32_t quota, uint32_t eq_total, uint32_t* keys_lds,
+                                          Smem& sm, int32_t* dst) {
+  const int lane = threadIdx.x & (WAVE - 1), wave = wave_index();
   // When every key equal to T is kept (no tie to rank) the keep rule is
   // key >= T; otherwise waves first count their equal keys for the ranks.
   const bool all_ties = quota >= eq_total;
+  uint32_t eqr = 0;   // keys equal to T before this wave's next step
   if (!all_ties) {
     uint32_t eqw = 0;
 #pragma unroll
     for (int j = 0; j < EPI; ++j) {
-      if (s0 + j * 4 * WAVE < s1) {
-        const int t = s0 + j * 4 * WAVE + 4 * lane;
-        const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          eqw += (uint32_t)__popcll(__ballot(t + u < s1 && kk[u] == T));
-      }
+      const int base = s0 + j * 4 * WAVE;
+      if (base >= s1) break;   // uniform
+      const int left = s1 - base - 4 * lane;
+      eqw += (uint32_t)__popcll(__ballot(left > 0 && ek[j].x == T)) +
+             (uint32_t)__popcll(__ballot(left > 1 && ek[j].y == T)) +
+             (uint32_t)__popcll(__ballot(left > 2 && ek[j].z == T)) +
+             (uint32_t)__popcll(__ballot(left > 3 && ek[j].w == T));
     }
     if (lane == 0) sm.w_eq[wave] = eqw;
   }
-  __syncthreads();   // also: every wave holds its keys in registers now
+  if (LDS_BUSY || !all_ties) __syncthreads();
   if (!all_ties)
-    for (int w = 0; w < wave; ++w) eqr += sm.w_eq[w];   // ties before this wave
+    for (int w = 0; w < wave; ++w) eqr += sm.w_eq[w];
   uint32_t* stage = keys_lds + s0;
-  uint32_t nk = 0;
+  uint32_t nk = 0;   // kept keys of this wave so far (uniform)
+  // stage the kept ones of 4 keys per lane (token t + u), in token order
+  auto put = [&](int t, bool k0, bool k1, bool k2, bool k3) {
+    const uint64_t b0 = __ballot(k0), b1 = __ballot(k1), b2 = __ballot(k2), b3 = __ballot(k3);
+    uint32_t at = __builtin_amdgcn_mbcnt_lo((uint32_t)b0, nk);
+    at = __builtin_amdgcn_mbcnt_hi((uint32_t)(b0 >> 32), at);
+    at = __builtin_amdgcn_mbcnt_lo((uint32_t)b1, at);
+    at = __builtin_amdgcn_mbcnt_hi((uint32_t)(b1 >> 32), at);
+    at = __builtin_amdgcn_mbcnt_lo((uint32_t)b2, at);
+    at = __builtin_amdgcn_mbcnt_hi((uint32_t)(b2 >> 32), at);
+    at = __builtin_amdgcn_mbcnt_lo((uint32_t)b3, at);
+    at = __builtin_amdgcn_mbcnt_hi((uint32_t)(b3 >> 32), at);
+    if (k0) stage[at] = (uint32_t)t;
+    at += k0 ? 1u : 0u;
+    if (k1) stage[at] = (uint32_t)(t + 1);
+    at += k1 ? 1u : 0u;
+    if (k2) stage[at] = (uint32_t)(t + 2);
+    at += k2 ? 1u : 0u;
+    if (k3) stage[at] = (uint32_t)(t + 3);
+    nk += (uint32_t)(__popcll(b0) + __popcll(b1) + __popcll(b2) + __popcll(b3));
+  };
 #pragma unroll
   for (int j = 0; j < EPI; ++j) {
-    if (all_ties && s0 + j * 4 * WAVE < s1) {
-      const int t = s0 + j * 4 * WAVE + 4 * lane;
-      const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
-      uint32_t at = nk;
-      bool keep[4];
-      uint64_t bk[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        keep[u] = t + u < s1 && kk[u] >= T;
-        bk[u] = __ballot(keep[u]);
-        at += mbcnt(bk[u]);
+    const int base = s0 + j * 4 * WAVE;
+    if (base >= s1) break;   // uniform
+    const int t = base + 4 * lane;
+    const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
+    if (all_ties) {
+      if (base + 4 * WAVE <= s1) {
+        put(t, kk[0] >= T, kk[1] >= T, kk[2] >= T, kk[3] >= T);
+      } else {
+        const int left = s1 - t;
+        put(t, left > 0 && kk[0] >= T, left > 1 && kk[1] >= T, left > 2 && kk[2] >= T,
+            left > 3 && kk[3] >= T);
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (keep[u]) stage[at++] = (uint32_t)(t + u);
-        nk += (uint32_t)__popcll(bk[u]);
-      }
-    } else if (s0 + j * 4 * WAVE < s1) {
-      const int t = s0 + j * 4 * WAVE + 4 * lane;
-      const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
-      bool is_gt[4], is_eq[4], keep[4];
-      uint64_t be[4], bk[4];
+    } else {
+      // rank of each key equal to T among those of the head, in token order
+      const int left = s1 - t;
+      bool gt[4], eq[4];
+      uint64_t be[4];
       uint32_t r = eqr;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bool valid = t + u < s1;
-        is_gt[u] = valid && kk[u] > T;
-        is_eq[u] = valid && kk[u] == T;
-        be[u] = __ballot(is_eq[u]);
+        gt[u] = left > u && kk[u] > T;
+        eq[u] = left > u && kk[u] == T;
+        be[u] = __ballot(eq[u]);
         r += mbcnt(be[u]);
       }
-      uint32_t at = nk;
+      bool keep[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        keep[u] = is_gt[u] || (is_eq[u] && r < quota);
-        r += is_eq[u] ? 1u : 0u;
-        bk[u] = __ballot(keep[u]);
-        at += mbcnt(bk[u]);
+        keep[u] = gt[u] || (eq[u] && r < quota);
+        r += eq[u] ? 1u : 0u;
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (keep[u]) stage[at++] = (uint32_t)(t + u);
-        nk += (uint32_t)__popcll(bk[u]);
-        eqr += (uint32_t)__popcll(be[u]);
-      }
+      put(t, keep[0], keep[1], keep[2], keep[3]);
+      eqr += (uint32_t)(__popcll(be[0]) + __popcll(be[1]) + __popcll(be[2]) + __popcll(be[3]));
     }
   }
   if (lane == 0) sm.w_gt[wave] = nk;
   __syncthreads();
+  uint32_t slot = 0;
   for (int w = 0; w < wave; ++w) slot += sm.w_gt[w];
   for (uint32_t i = lane; i < nk; i += WAVE)
     if (slot + i < (uint32_t)n) dst[slot + i] = (int32_t)stage[i];
@@ -532,7 +606,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t keys_lds[IN_LDS ? LDS_KEYS : 4];
   __shared__ Smem sm;
   const int head = blockIdx.x, b = head / a.Hkv;
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = wave_index();
   const int n = a.n_head ? min(max(a.n_head[head], 0), a.N_max)
                         : (a.ctx ? min(max(a.ctx[b], 0), a.N_max) : a.N_max);
   const bool none = a.k_zero_ok && a.bud.mode == KV_BUDGET_K &&
@@ -798,7 +872,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       const int t = s0 + j * 4 * WAVE + 4 * lane;
       ek[j] = t < s1 ? *reinterpret_cast<const uint4*>(&keys_lds[t]) : make_uint4(0u, 0u, 0u, 0u);
     }
-    emit_regs(ek, s0, s1, n, T, quota, eq_total, keys_lds, sm, dst);
+    emit_regs<true>(ek, s0, s1, n, T, quota, eq_total, keys_lds, sm, dst);
   } else {
     // GU steps of the segment are loaded (16 bytes per lane each) before the
     // first is counted or written; s0 is a multiple of 256, so a lane's four
@@ -845,10 +919,10 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
 // head:
 //   1. the histogram gives the top digit b1 of the k-th key and the count of
 //      keys above it (the same scan as resolve_digit);
-//   2. each wave loads its segment's scores into registers as keys, and the
-//      keys whose top digit is b1 (the candidates, as many as the histogram
-//      counted in b1) are gathered into LDS;
-//   3. the descent resolves the remaining key bits over the candidates only;
+//   2. each wave loads its segment's scores into registers as keys (the
+//      loads are issued before the scan above and land during it);
+//   3. the second and third digits are counted straight from the registers
+//      (count_regs: only keys that carry the prefix found so far add);
 //   4. the emit runs from the registers, as select_kernel's does.
 // The k-th key T and the tie quota are those of select_kernel, so the kept
 // indices are the same.
@@ -856,9 +930,8 @@ template <bool VEC>   // VEC: 16-byte aligned scores with N_max a multiple of 4
 __global__ __launch_bounds__(NT) void select_hist_kernel(SelectArgs a, const uint32_t* hist) {
   __shared__ __attribute__((aligned(16))) uint32_t keys_lds[LDS_KEYS];
   __shared__ Smem sm;
-  __shared__ uint32_t cand_n;
   const int head = blockIdx.x, b = head / a.Hkv;
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = wave_index();
   const int n = a.ctx ? min(max(a.ctx[b], 0), a.N_max) : a.N_max;
   if (n == 0) {
     if (tid == 0) a.kept_count[head] = 0;
@@ -871,82 +944,59 @@ __global__ __launch_bounds__(NT) void select_hist_kernel(SelectArgs a, const uin
   // indices past the head are clamped onto it and the keys masked later).
   static_assert(NBINS == 2 * NT, "two bins per thread");
   const uint32_t h0 = hh[tid], h1 = hh[tid + NT];
-  // this wave's segment, loaded while the histogram is scanned
   const int seg = ((n + NWV - 1) / NWV + 4 * WAVE - 1) / (4 * WAVE) * (4 * WAVE);
   const int s0 = wave * seg, s1 = min(s0 + seg, n);
-  uint4 ek[EPI];
+  // this wave's segment, loaded while the histogram is scanned: whole 16-byte
+  // loads clamped onto the head's row (N_max - 4 is aligned) when the row
+  // allows, else scalar loads clamped onto the head; tokens at or past n are
+  // masked by their index
+  uint4 v4[VEC ? EPI : 1];
+  float v1[VEC ? 1 : EPI][4];
   if constexpr (VEC) {
-    // whole 16-byte loads, clamped onto the head's row (N_max - 4 is aligned);
-    // tokens at or past n are masked by their index
-    uint4 v[EPI];
 #pragma unroll
-    for (int j = 0; j < EPI; ++j) v[j] = ld16(src + min(s0 + j * 4 * WAVE + 4 * lane, a.N_max - 4));
-#pragma unroll
-    for (int j = 0; j < EPI; ++j)
-      ek[j] = make_uint4(to_key(__uint_as_float(v[j].x)), to_key(__uint_as_float(v[j].y)),
-                         to_key(__uint_as_float(v[j].z)), to_key(__uint_as_float(v[j].w)));
+    for (int j = 0; j < EPI; ++j) v4[j] = ld16(src + min(s0 + j * 4 * WAVE + 4 * lane, a.N_max - 4));
   } else {
-    float v[EPI][4];
 #pragma unroll
     for (int j = 0; j < EPI; ++j)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[j][u] = src[min(s0 + j * 4 * WAVE + 4 * lane + u, n - 1)];
-#pragma unroll
-    for (int j = 0; j < EPI; ++j)
-      ek[j] = make_uint4(to_key(v[j][0]), to_key(v[j][1]), to_key(v[j][2]), to_key(v[j][3]));
+      for (int u = 0; u < 4; ++u) v1[j][u] = src[min(s0 + j * 4 * WAVE + 4 * lane + u, n - 1)];
   }
   sm.hist[tid] = h0;
   sm.hist[tid + NT] = h1;
-  if (tid == 0) cand_n = 0u;
   __syncthreads();
   resolve_digit<false>(sm, NBINS, (unsigned long long)k);   // leaves sm.hist cleared
-  const uint32_t b1 = sm.bin, above1 = sm.cnt_above;
-
-  // candidates: this wave's count first, one LDS atomic per wave, then the writes
-  auto is_cand = [&](uint32_t kk, int t) { return t < s1 && (kk >> (32 - DIGIT)) == b1; };
-  uint32_t wc = 0;
+  // keys as the score pass histogrammed them (score_key: scores written by
+  // the score pass are never negative, so these order them as to_key does)
+  uint4 ek[EPI];
 #pragma unroll
   for (int j = 0; j < EPI; ++j) {
-    const int t = s0 + j * 4 * WAVE + 4 * lane;
-    wc += (uint32_t)__popcll(__ballot(is_cand(ek[j].x, t))) +
-          (uint32_t)__popcll(__ballot(is_cand(ek[j].y, t + 1))) +
-          (uint32_t)__popcll(__ballot(is_cand(ek[j].z, t + 2))) +
-          (uint32_t)__popcll(__ballot(is_cand(ek[j].w, t + 3)));
+    if constexpr (VEC)
+      ek[j] = make_uint4(score_key(__uint_as_float(v4[j].x)), score_key(__uint_as_float(v4[j].y)),
+                         score_key(__uint_as_float(v4[j].z)), score_key(__uint_as_float(v4[j].w)));
+    else
+      ek[j] = make_uint4(score_key(v1[j][0]), score_key(v1[j][1]), score_key(v1[j][2]),
+                         score_key(v1[j][3]));
   }
-  uint32_t at = 0;
-  if (lane == 0 && wc) at = atomicAdd(&cand_n, wc);
-  at = __builtin_amdgcn_readfirstlane(at);
-#pragma unroll
-  for (int j = 0; j < EPI; ++j) {
-    const int t = s0 + j * 4 * WAVE + 4 * lane;
-    const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bool c = is_cand(kk[u], t + u);
-      const uint64_t bc = __ballot(c);
-      if (c) keys_lds[at + mbcnt(bc)] = kk[u];
-      at += (uint32_t)__popcll(bc);
-    }
-  }
+  // The lower digits count straight from the registers: a key takes part
+  // when its bits above the digit equal the prefix found so far.
+  unsigned long long rem = (unsigned long long)(k - sm.cnt_above);
+  uint32_t prefix = sm.bin;   // the top DIGIT bits of the k-th largest key
+  count_regs(ek, s0, s1, 32 - DIGIT, 32 - 2 * DIGIT, prefix, sm);
   __syncthreads();
-  const int nc = (int)cand_n;
-
-  // the remaining key bits over the candidates (all share the top digit b1)
-  uint32_t T, quota, eq_total = 0;
-  {
-    Keys<true> key{keys_lds, nullptr, 0, INT32_MAX};
-    uint32_t above;
-    unsigned long long rem;
-    auto nofx = [](uint32_t) { return 0ull; };
-    // the candidates already share their top digit: plain adds (hist_add
-    // still aggregates a crowded bin)
-    T = descend<false, true, decltype(nofx), false>(key, nc, DIGIT, b1 << (32 - DIGIT),
-                                                    (unsigned long long)(k - above1), sm, nofx,
-                                                    &above, &rem, false, &eq_total);
-    quota = (uint32_t)rem;
-  }
+  resolve_digit<false>(sm, NBINS, rem);
+  rem -= sm.cnt_above;
+  prefix = prefix << DIGIT | sm.bin;   // the top 2 * DIGIT bits
+  count_regs(ek, s0, s1, 32 - 2 * DIGIT, 0, prefix, sm);
+  __syncthreads();
+  resolve_digit<false>(sm, 1 << (32 - 2 * DIGIT), rem);
+  rem -= sm.cnt_above;
+  const uint32_t T = prefix << (32 - 2 * DIGIT) | sm.bin;   // the k-th largest key
+  const uint32_t quota = (uint32_t)rem;                    // keys equal to T to keep
+  const uint32_t eq_total = sm.bin_cnt;                    // keys equal to T in the head
   if (tid == 0) a.kept_count[head] = k;
-  emit_regs(ek, s0, s1, n, T, quota, eq_total, keys_lds, sm, a.kept_idx + (size_t)head * a.N_max);
+  // keys_lds serves only as the emit's staging area here (no barrier needed)
+  emit_regs<false>(ek, s0, s1, n, T, quota, eq_total, keys_lds, sm,
+                   a.kept_idx + (size_t)head * a.N_max);
 }
 
 // ---------------------------------------------------------------------------
@@ -991,7 +1041,7 @@ size_t part_workspace(int H, int P) {
 
 // Sum over the block of one value per thread (every thread gets it).
 __device__ __forceinline__ uint32_t block_sum(uint32_t v, Smem& sm) {
-  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int lane = threadIdx.x & (WAVE - 1), wave = wave_index();
   v = last_lane(wave_scan_u32(v, 0u, OpAdd()));
   if (lane == 0) sm.f_c[wave] = v;
   __syncthreads();
@@ -1007,7 +1057,7 @@ __global__ __launch_bounds__(NT) void select_part_kernel(PartArgs pa) {
   __shared__ Smem sm;
   const SelectArgs& a = pa.s;
   const int part = blockIdx.x, head = blockIdx.y, b = head / a.Hkv;
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = wave_index();
   const int n = a.ctx ? min(max(a.ctx[b], 0), a.N_max) : a.N_max;
   if (n == 0) {
     if (PHASE == 4 && part == 0 && tid == 0) a.kept_count[head] = 0;

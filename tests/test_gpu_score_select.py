@@ -76,6 +76,18 @@ def test_all_scores_tied():
             assert np.array_equal(idx[b, h, :k], np.arange(k))
 
 
+def test_half_the_tokens_tied():
+    # every other key row is one repeated row: half of a head's scores are
+    # equal (one crowded bin at every digit) and the rest spread; the k-th
+    # key falls inside the tied block at some ratios and outside at others
+    lay = wl.random_case(10, B=2, Hq=8, Hkv=2, d=128, N_max=6000, W=16, ctx=[6000, 4099])
+    lay.k[:, :, 1::2] = lay.k[:, :, :1]
+    for b, n in enumerate([6000, 4099]):
+        lay.k[b, :, n:] = 0
+    for r in (0.05, 0.3, 0.5, 0.7, 0.95):
+        both(lay, RATIO(r))
+
+
 @pytest.mark.parametrize("budget", [
     api.Budget(api.BUDGET_THRESHOLD, tau=0.01, min_ratio=0.02, max_ratio=0.5),
     api.Budget(api.BUDGET_MASS, mass=0.9, min_ratio=0.02, max_ratio=0.5),

@@ -383,8 +383,9 @@ int kv_vector_decode(const void* q, const void* k_c, const void* v_c, const int3
  * totals (host array, caller-owned), returning the number of distinct
  * kernels (or a negative kv_status).  kv_timing_only(name) restricts the
  * recording to launches of that kernel name (one of "score_rowstats",
- * "score_fold" (launched only when row LSEs are requested or pass 1 has
- * more than 16 chunks per head), "score_colsum", "select", "compact",
+ * "score_fold" (launched only when row LSEs are requested or heads are so
+ * long, and so few, that pass 1 cuts a head into more than 16 pieces),
+ * "score_colsum", "select", "compact",
  * "compact_decode", "decode_split",
  * "decode_merge", "vector_counts", "vector_pool", "vector_residual",
  * "vector_apx", "vector_vmap", "vector_copy", "vector_decode_split",

@@ -41,10 +41,11 @@ namespace {
 
 constexpr int TOK = 64;          // tokens per LDS tile
 constexpr int RBW = 2;           // 32-row blocks per wave
-constexpr int SLOTS_1 = 256 * 2; // pass-1 chunking target: resident workgroups on 256 CUs
-constexpr int RANGE_HEADS = 256;  // most heads (B * Hkv) the balanced pass-2 ranges take
-constexpr int TAB_MAX = 2048;     // most pass-2 workgroups in that mode
-constexpr int SELF_MERGE = 16;    // pass 2 merges pass 1's partials itself up to this many chunks
+constexpr int SLOTS_1 = 256 * 2; // pass-1 partition target (resident workgroups on 256 CUs);
+                                 // fixed, so the pass-1 partition, its merge order and the
+                                 // result never depend on the device
+constexpr int MIN_SPAN = 4;      // fewest tiles per piece span
+constexpr int SELF_MERGE = 16;   // pass 2 merges pass 1's partials itself up to this many per head
 
 template <typename T> struct FragT;
 template <> struct FragT<__bf16> { using vec = bf16x8; };   // 8 elements = 16 B
@@ -142,17 +143,17 @@ struct ScoreArgs {
   const void* k;
   const int32_t* ctx;
   float* scores;
-  float2* part;     // [B*Hkv][n_chunks][R_pad] per-chunk (max, sum of exp2) per row
+  float2* part;     // [max(SLOTS_1, B*Hkv)][R_pad] per-piece (max, sum of exp2) per row
   float* lse2;      // [B*Hkv][R_pad] base-2 row log-sum-exp (+inf: row adds nothing)
   float* row_lse;   // [B][Hq][W] natural log, optional
   const float* lse_in;  // [B][Hq][W] natural-log row LSE given by the caller (one-pass), or null
   int B, Hq, Hkv, N_max, W, G, R, R_pad, causal;
-  int TC, n_chunks;    // pass-1 token chunks (fixed by the sizes: sets the merge order)
-  int TC2, n_chunks2;  // pass-2 token chunks (free: no cross-chunk arithmetic)
-  int ranges;          // pass 2: balanced tile ranges over G2 workgroups (see score_pass)
-  int G2;              // pass-2 workgroups in that mode
-  int4* tab;           // [TAB_MAX] the ranges, written by pass 1: {head, t0, t1, n}
-  int self_merge;      // pass 2 merges the pass-1 partials (n_chunks <= SELF_MERGE); else the fold's lse2
+  int L1_min;          // pass-1 span floor (fixed by the sizes)
+  int3 dense1, dense2;   // pieces per head if every head held N_max tokens, and the
+                         // quotient and remainder of their split (pass 1, pass 2;
+                         // see dense_piece)
+  int G2;              // pass-2 partition target (the device's resident workgroups)
+  int self_merge;      // pass 2 merges the pass-1 partials itself (at most SELF_MERGE per head); else the fold's lse2
   float c;             // scale * log2(e)
   // Optional [B*Hkv][KEY_BINS] histogram of the top key bits of each head's
   // scores (the first radix digit of the selection): pass 1 clears it, pass
@@ -160,55 +161,161 @@ struct ScoreArgs {
   uint32_t* hist;
 };
 
-// Pass-2 work ranges, built by one workgroup of pass 1 so that pass 2 reads
-// its range with one load.  Each head's 64-token tiles are cut into ranges
-// of L tiles, L = ceil(T / G) if that leaves at most G ranges, else
-// ceil(T / (G - H)) (T tiles in all, G = a.G2 workgroups, H heads), and range
-// i goes to workgroup i in (sequence, head, range) order: with ragged lengths
-// no workgroup gets more than about T / (G - H) tiles, where chunks sized for
-// N_max leave some CUs whole heads and others nothing; with equal lengths the
-// ranges are those chunks.  Unused entries get head -1.  `scr` is LDS for
-// 2 B + 3 ints (B <= RANGE_HEADS).
-__device__ void build_ranges(const ScoreArgs& a, int* scr) {
-  const int tid = threadIdx.x, nt_thr = blockDim.x;
-  const int B = a.B, Hkv = a.Hkv, H = B * Hkv, G = a.G2;
-  int* seqr = scr;              // ranges per head of sequence b
-  int* seqpre = scr + B;        // ranges before sequence b (B + 1 entries)
-  int* tot = scr + 2 * B + 1;   // tiles, ranges
-  auto len = [&](int bb) { return a.ctx ? min(max(a.ctx[bb], 0), a.N_max) : a.N_max; };
-  if (tid == 0) { tot[0] = 0; tot[1] = 0; }
-  __syncthreads();
-  for (int bb = tid; bb < B; bb += nt_thr) atomicAdd(&tot[0], Hkv * ((len(bb) + TOK - 1) / TOK));
-  __syncthreads();
-  const int total = tot[0];
-  int L = max(1, (total + G - 1) / G);
-  for (int bb = tid; bb < B; bb += nt_thr)
-    atomicAdd(&tot[1], Hkv * (((len(bb) + TOK - 1) / TOK + L - 1) / L));
-  __syncthreads();
-  if (tot[1] > G) L = max(1, (total + (G - H) - 1) / (G - H));
-  for (int bb = tid; bb < B; bb += nt_thr) seqr[bb] = ((len(bb) + TOK - 1) / TOK + L - 1) / L;
-  __syncthreads();
-  if (tid == 0) {
-    seqpre[0] = 0;
-    for (int bb = 0; bb < B; ++bb) seqpre[bb + 1] = seqpre[bb] + Hkv * seqr[bb];
+// Work partition of both score passes.  Head (b, h) holds t_b =
+// ceil(n_b / TOK) tiles.  With span L it is cut into k_b = ceil(t_b / L)
+// pieces of near-equal length (with q = t_b / k_b and r = t_b mod k_b, piece
+// j starts at tile j q + min(j, r): the first r pieces take q + 1 tiles),
+// numbered in (sequence, head, piece) order, and piece i goes to workgroup i.
+// L is the smallest span of at least `floor` tiles that gives at most
+// C = max(G, heads) pieces: one round of C workgroups takes every piece, and
+// no workgroup gets more than L tiles, where chunks sized for N_max leave some
+// workgroups whole heads and others nothing (L = ceil(T / C) when the heads
+// divide evenly).  Pass 1 takes G = SLOTS_1 and a floor fixed by the sizes,
+// so its pieces, whose per-row partials merge in piece order, depend on the
+// lengths and the sizes only.  Pass 2 has no cross-tile arithmetic, so any
+// partition gives the same scores; it takes G = the device's resident
+// workgroups.  Each wave computes all of this itself, in scalar code.
+// A sequence length through the constant address space: the lengths are
+// never written while the score kernels run, and a uniform index then takes
+// a scalar load (even after the inline asm of the K tile loads, which
+// clobbers memory as far as the compiler knows).
+__device__ __forceinline__ int ctx_len_at(const ScoreArgs& a, int b) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+      reinterpret_cast<uintptr_t>(a.ctx + b));
+}
+__device__ __forceinline__ int seq_tiles(const ScoreArgs& a, int b) {
+  const int n = a.ctx ? min(max(ctx_len_at(a, b), 0), a.N_max) : a.N_max;
+  return (n + TOK - 1) / TOK;
+}
+// Each wave computes the partition itself, one sequence per lane (64 at a
+// time), and keeps the results in SGPRs.
+__device__ __forceinline__ int wave_total(int v) {
+  return __builtin_amdgcn_readlane((int)wave_scan_u32((uint32_t)v, 0u, OpAdd()), WAVE - 1);
+}
+__device__ __forceinline__ int lane_tiles(const ScoreArgs& a, int b) {
+  return b < a.B ? seq_tiles(a, min(b, a.B - 1)) : 0;
+}
+// Length (clamped to [0, N_max]) of sequence `lane` for the first 64
+// sequences, 0 past B, from scalar loads (clamped onto the array, 16 issued
+// together, then placed into lanes): their counter is not the one the K tile
+// loads in flight use, so waiting for them does not wait for those.
+__device__ __forceinline__ int first_lens(const ScoreArgs& a) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  int v = 0;
+  for (int g = 0; g < min(a.B, WAVE); g += 16) {
+    int n[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      n[u] = a.ctx ? min(max(ctx_len_at(a, min(g + u, a.B - 1)), 0), a.N_max) : a.N_max;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v = lane == g + u ? n[u] : v;
   }
-  __syncthreads();
-  const int R = seqpre[B];
-  for (int i = tid; i < G; i += nt_thr) {
-    int4 e = make_int4(-1, 0, 0, 0);
-    if (i < R) {
-      int lo = 0, hi = B - 1;   // largest b with seqpre[b] <= i (empty sequences are passed over)
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (seqpre[mid] <= i) lo = mid; else hi = mid - 1;
-      }
-      const int q = i - seqpre[lo], rb = seqr[lo];
-      const int nb = len(lo);
-      const int t0 = (q % rb) * L * TOK;
-      e = make_int4(lo * Hkv + q / rb, t0, min(t0 + L * TOK, nb), nb);
+  return lane < a.B ? v : 0;
+}
+// Whether every sequence holds N_max tokens (then the partition is the
+// dense one the host worked out); decided for at most 64 sequences.
+__device__ __forceinline__ bool equal_lengths(const ScoreArgs& a, int n0) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  return a.B <= WAVE && __ballot(lane < a.B && n0 != a.N_max) == 0;
+}
+// Tiles of sequence b0 + lane: the first 64 sequences' lengths come in once,
+// as `n0` (first_lens), and later ones are loaded where needed.
+__device__ __forceinline__ int lane_tiles(const ScoreArgs& a, int b0, int n0) {
+  return b0 == 0 ? (n0 + TOK - 1) / TOK : lane_tiles(a, b0 + (int)(threadIdx.x & (WAVE - 1)));
+}
+// Pieces of all heads for span L.
+__device__ __forceinline__ int piece_count(const ScoreArgs& a, int n0, int L) {
+  int total = 0;
+  for (int b0 = 0; b0 < a.B; b0 += WAVE) total += wave_total((lane_tiles(a, b0, n0) + L - 1) / L);
+  return total * a.Hkv;
+}
+// The smallest span L >= max(floor, ceil(T / C)) with at most C pieces.
+// Starting from that bound, each probe that gives too many pieces raises L
+// in proportion to the excess (count(L) shrinks about as 1 / L), so a few
+// probes find a span with at most C pieces; a bisection between the last
+// span that gave too many and that one then finds the smallest.
+__device__ __forceinline__ int piece_span(const ScoreArgs& a, int n0, int G, int floor_tiles) {
+  int T = 0, t_max = 0;
+  for (int b0 = 0; b0 < a.B; b0 += WAVE) {
+    const int t = lane_tiles(a, b0, n0);
+    T += wave_total(t);
+    t_max = max(t_max, __builtin_amdgcn_readlane((int)wave_scan_u32((uint32_t)t, 0u, OpMax()), WAVE - 1));
+  }
+  const int C = max(G, a.B * a.Hkv);
+  int lo = max(floor_tiles, (T * a.Hkv + C - 1) / C);   // T * Hkv < 2^31 / TOK
+  int c = piece_count(a, n0, lo);
+  if (c <= C) return lo;
+  int hi = lo;
+  while (c > C && hi < t_max) {   // count(t_max) = non-empty heads <= C
+    lo = hi;
+    hi = min(t_max, max(hi + 1, (int)(((int64_t)hi * c + C - 1) / C)));
+    c = piece_count(a, n0, hi);
+  }
+  while (hi - lo > 1) {   // count(lo) > C >= count(hi)
+    const int mid = (lo + hi) >> 1;
+    if (piece_count(a, n0, mid) <= C) hi = mid;
+    else lo = mid;
+  }
+  return hi;
+}
+struct Piece {
+  int b, h, n;      // head (b, h) of n tokens (no piece: b < 0)
+  int t0, t1;       // its tokens [t0, t1)
+  int j;            // index of the piece within the head
+  int first, k;     // the head's first piece and its piece count
+};
+// The same piece with every field in SGPRs (the values are wave-uniform by
+// construction; readfirstlane tells the compiler so).
+__device__ __forceinline__ Piece uniform(Piece p) {
+  return Piece{__builtin_amdgcn_readfirstlane(p.b), __builtin_amdgcn_readfirstlane(p.h),
+               __builtin_amdgcn_readfirstlane(p.n), __builtin_amdgcn_readfirstlane(p.t0),
+               __builtin_amdgcn_readfirstlane(p.t1), __builtin_amdgcn_readfirstlane(p.j),
+               __builtin_amdgcn_readfirstlane(p.first), __builtin_amdgcn_readfirstlane(p.k)};
+}
+// Piece i of the partition with span L.
+__device__ __forceinline__ Piece piece_of(const ScoreArgs& a, int n0, int L, int i) {
+  int before = 0;   // pieces of the sequences before this chunk of lanes
+  for (int b0 = 0; b0 < a.B; b0 += WAVE) {
+    const int t = lane_tiles(a, b0, n0);
+    const int kk = (t + L - 1) / L;
+    const int incl = (int)wave_scan_u32((uint32_t)(kk * a.Hkv), 0u, OpAdd());
+    const uint64_t hit = __ballot(before + incl > i);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      const int b = b0 + l;
+      const int k = __builtin_amdgcn_readlane(kk, l), tl = __builtin_amdgcn_readlane(t, l);
+      const int start = before + __builtin_amdgcn_readlane(incl, l) - k * a.Hkv;
+      const int off = i - start, h = off / k, j = off - h * k;
+      const int n = a.ctx ? min(max(ctx_len_at(a, b), 0), a.N_max) : a.N_max;
+      const int q = tl / k, r = tl - q * k;
+      const int tile0 = j * q + min(j, r), tile1 = tile0 + q + (j < r ? 1 : 0);
+      return Piece{b, h, n, tile0 * TOK, min(tile1 * TOK, n), j, start + h * k, k};
     }
-    a.tab[i] = e;
+    before += __builtin_amdgcn_readlane(incl, WAVE - 1);
   }
+  return Piece{-1, 0, 0, 0, 0, 0, 0, 0};
+}
+// Piece i of the partition if every head held N_max tokens, from the sizes
+// alone (no loads): d = (pieces per head k, tiles / k, tiles mod k), which
+// the host works out (dense_params).  With every length equal to N_max this
+// is piece_of(a, piece_span(...), i).
+__device__ __forceinline__ Piece dense_piece(const ScoreArgs& a, int3 d, int i) {
+  const int k = d.x, H = a.B * a.Hkv;
+  if (i >= H * k) return Piece{-1, 0, 0, 0, 0, 0, 0, 0};
+  const int hd = i / k, j = i - hd * k, b = hd / a.Hkv;
+  const int tile0 = j * d.y + min(j, d.z), tile1 = tile0 + d.y + (j < d.z ? 1 : 0);
+  return Piece{b, hd - b * a.Hkv, a.N_max, tile0 * TOK, min(tile1 * TOK, a.N_max), j, hd * k, k};
+}
+// The first piece of head (b, h) and the head's piece count, for span L.
+__device__ __forceinline__ int2 head_pieces(const ScoreArgs& a, int n0, int L, int b, int h) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  int before = 0, k = 0;
+  for (int b0 = 0; b0 < a.B && b0 <= b; b0 += WAVE) {
+    const int t = lane_tiles(a, b0, n0), kk = (t + L - 1) / L;
+    before += wave_total(b0 + lane < b ? kk : 0);
+    if (b - b0 < WAVE) k = __builtin_amdgcn_readlane(kk, b - b0);
+  }
+  return make_int2(before * a.Hkv + h * k, k);
 }
 
 template <typename T, int D, int NW, int PASS>
@@ -232,145 +339,34 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int hf = lane >> 5, l32 = lane & 31;
 
-  // The workgroup's tokens [t0, t1) of head (b, h).  Chunk mode: chunk
-  // blockIdx.x of head (blockIdx.z, blockIdx.y).  Balanced mode (pass 2,
-  // a.ranges): range blockIdx.x of the table that one workgroup of pass 1
-  // built (build_ranges), read with one scalar load.
-  int b, h, c, t0, t1, n;
-  if (PASS == 1 && a.ranges && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) {
-    build_ranges(a, reinterpret_cast<int*>(&ktile[0][0]));   // LDS not in use yet
-    __syncthreads();
-  }
-  if (PASS == 2 && a.ranges) {
-    const int4 e = a.tab[blockIdx.x];
-    const int hd = __builtin_amdgcn_readfirstlane(e.x);
-    if (hd < 0) return;   // fewer ranges than workgroups
-    // the division runs on the VALU: bring the quotient back to SGPRs
-    b = __builtin_amdgcn_readfirstlane(hd / a.Hkv); h = hd - b * a.Hkv; c = 0;
-    t0 = __builtin_amdgcn_readfirstlane(e.y);
-    t1 = __builtin_amdgcn_readfirstlane(e.z);
-    n = __builtin_amdgcn_readfirstlane(e.w);
-  } else {
-    c = blockIdx.x; h = blockIdx.y; b = blockIdx.z;
-    if (PASS == 1 && a.hist && c == 0)   // the head's key histogram starts empty
-      for (int i = tid; i < KEY_BINS; i += NT) a.hist[(size_t)(b * a.Hkv + h) * KEY_BINS + i] = 0u;
-    n = a.ctx ? min(max(a.ctx[b], 0), a.N_max) : a.N_max;
-    const int TC = PASS == 1 ? a.TC : a.TC2;
-    t0 = c * TC;
-    if (t0 >= n) {
-      if (PASS == 1)
-        for (int r = tid; r < a.R_pad; r += NT)
-          a.part[((size_t)(b * a.Hkv + h) * a.n_chunks + c) * a.R_pad + r] = make_float2(-INFINITY, 0.f);
-      return;
-    }
-    t1 = min(t0 + TC, n);
-  }
-  const int head = b * a.Hkv + h;
-  const int ntiles = (t1 - t0 + TOK - 1) / TOK;
-  const char* kh = static_cast<const char*>(a.k) + (size_t)head * a.N_max * ROWB;
-  const int last_w0 = n - a.W;   // position of window row 0; row w sits at last_w0 + w
-  // Leading tiles whose every token exists and is visible to every row.
-  int clean_tiles = (t1 - t0) / TOK;
-  if (a.causal) clean_tiles = min(clean_tiles, max(0, (last_w0 + 1 - t0) / TOK));
-  const float cc = a.c;
+  // The workgroup's piece of the partition (see piece_span): tokens
+  // [t0, t1) of head (b, h), n tokens in the head.  (Set by take().)
+  int b = 0, h = 0, n = 0, t0 = 0, t1 = 0, head = 0, ntiles = 0;
+  const char* kh = nullptr;
+  auto take = [&](const Piece& p) __attribute__((always_inline)) {
+    b = p.b; h = p.h; n = p.n; t0 = p.t0; t1 = p.t1;
+    head = b * a.Hkv + h;
+    ntiles = (t1 - t0 + TOK - 1) / TOK;
+    kh = static_cast<const char*>(a.k) + (size_t)head * a.N_max * ROWB;
+  };
 
-  // Q fragments of this wave's row blocks (zero for padding rows).
-  // Loads are branch-free (clamped row, then a select) so they all issue at once.
+  // Q fragments of this wave's row blocks.  A padding row (r >= R) takes row
+  // R - 1 (the loads are branch-free and issue at once, and the fragments
+  // stay the loads' own registers): its logits are finite, pass 2 gives it
+  // the normaliser -inf (so it adds exactly 0 to every column), and no merge
+  // of pass 1's partials reads a row at or past R.
   V qf[RBW][KS];
-#pragma unroll
-  for (int i = 0; i < RBW; ++i) {
-    const int r = (wave * RBW + i) * 32 + l32;
-    const int rc = min(r, a.R - 1);
-    const int j = h * a.G + rc / a.W, w = rc % a.W;
-    const char* qp = static_cast<const char*>(a.q) +
-                     ((((size_t)b * a.Hq + j) * a.W + w) * D + 8 * hf) * sizeof(T);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const V v = load_frag<T>(qp + ks * 16 * sizeof(T));
-      qf[i][ks] = r < a.R ? v : V{};
-    }
-  }
-
-  // Causal limits: p_row[i] = position of the lane's pass-1 row (row block i);
-  // rowpos[r] = window position (r mod W) of every row, for the pass-2 masks.
-  int p_row[RBW];
-#pragma unroll
-  for (int i = 0; i < RBW; ++i) {
-    const int r = (wave * RBW + i) * 32 + l32;
-    p_row[i] = a.causal ? last_w0 + (r % a.W) : 0x7fffffff;
-  }
-  if (PASS == 2 && a.causal)
-    for (int r = tid; r < NW * RBW * 32; r += NT) rowpos[r] = r % a.W;
-  if (PASS == 2 && a.hist)   // cleared before tile 0's barrier, counted after it
-    for (int i = tid; i < KEY_BINS; i += NT) khist[i] = 0u;
-
-  // Pass-1 running state (per row owned by the lane) / pass-2 negated row lse2.
-  float m_run[RBW], s_run[RBW];
-  float nl2[RBW][16];
-  const float inv_w = 1.0f / (float)a.W;
-  if (PASS == 1) {
-#pragma unroll
-    for (int i = 0; i < RBW; ++i) { m_run[i] = -INFINITY; s_run[i] = 0.f; }
-  } else if (a.lse_in) {
+  auto load_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < RBW; ++i) {
+      const int rc = min((wave * RBW + i) * 32 + l32, a.R - 1);
+      const int j = h * a.G + rc / a.W, w = rc % a.W;
+      const char* qp = static_cast<const char*>(a.q) +
+                       ((((size_t)b * a.Hq + j) * a.W + w) * D + 8 * hf) * sizeof(T);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = (wave * RBW + i) * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
-        // caller's natural-log LSE of row (j, w), to base 2;
-        // rc / W by a float reciprocal: exact for rc < 1024 (error < 0.5/W)
-        const int rc = min(r, a.R - 1);
-        const int jw = (int)(((float)rc + 0.5f) * inv_w);
-        const int j = h * a.G + jw, w = rc - jw * a.W;
-        const float v = a.lse_in[((size_t)b * a.Hq + j) * a.W + w] * (float)LOG2E_D;
-        nl2[i][e] = r < a.R ? -v : -INFINITY;
-      }
+      for (int ks = 0; ks < KS; ++ks) qf[i][ks] = load_frag<T>(qp + ks * 16 * sizeof(T));
     }
-  } else if (!a.self_merge) {   // the fold's row LSEs
-#pragma unroll
-    for (int i = 0; i < RBW; ++i) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = (wave * RBW + i) * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
-        nl2[i][e] = r < a.R ? -a.lse2[(size_t)head * a.R_pad + min(r, a.R_pad - 1)] : -INFINITY;
-      }
-    }
-  } else {
-    // Base-2 LSE of each row from pass 1's per-chunk (m, sum) partials of
-    // this head (at most 16, loads all issued at once): M = max of the m's,
-    // then the sum of sum * 2^(m - M).  Staged in `red` (not in use before
-    // tile 0).
-    float* lse_s = &red[0][0][0];
-    for (int r = tid; r < NW * RBW * 32; r += NT) {
-      float v = INFINITY;
-      if (r < a.R) {
-        const float2* src = a.part + (size_t)head * a.n_chunks * a.R_pad + r;
-        float2 pk[SELF_MERGE];
-#pragma unroll
-        for (int u = 0; u < SELF_MERGE; ++u)   // chunk u of the row: lanes read consecutive rows
-          pk[u] = u < a.n_chunks ? src[(size_t)u * a.R_pad] : make_float2(-INFINITY, 0.f);
-        float M = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < SELF_MERGE; ++u) M = fmaxf(M, pk[u].x);
-        if (M != -INFINITY) {
-          float S = 0.f;
-#pragma unroll
-          for (int u = 0; u < SELF_MERGE; ++u) S = fmaf(pk[u].y, fast_exp2(pk[u].x - M), S);
-          if (S > 0.f) v = M + log2f(S);
-        }
-      }
-      lse_s[r] = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < RBW; ++i) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = (wave * RBW + i) * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
-        nl2[i][e] = r < a.R ? -lse_s[r] : -INFINITY;
-      }
-    }
-  }
+  };
 
   // K tile staging.  Piece v of a tile (16 bytes) sits at LDS slot v: row
   // v / VPR, column v % VPR, and holds the row's global column
@@ -424,6 +420,152 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
       vm_wait<0>();
     }
   };
+
+  // Pass 1 first takes the piece it would get if every head held N_max
+  // tokens (dense_piece, from the sizes alone) and issues that piece's Q
+  // loads and first K tiles; then it loads the lengths and works out its
+  // piece.  With equal lengths the two agree and the lengths' load and the
+  // work on them overlap the Q and K loads; otherwise it waits for those
+  // loads (the K tiles write only this wave's LDS slots, which no wave reads
+  // yet) and issues its own piece's.  Pass 2 (its K tiles go out after the
+  // prologue below) takes its piece directly; it needs pass 1's span only to
+  // find the partials it merges.
+  int L1 = 0;
+  int2 hp = make_int2(0, 0);   // pass 2, self-merge: the head's pass-1 pieces
+  Piece pc;
+  if (PASS == 1) {
+    const Piece guess = uniform(dense_piece(a, a.dense1, (int)blockIdx.x));
+    const bool spec = guess.b >= 0;
+    if (spec) {
+      take(guess);
+      load_q();
+      for (int p = 0; p < NB - 1; ++p)
+        if (p < ntiles) gload_lds(p, p);
+    }
+    const int n0 = first_lens(a);
+    if (equal_lengths(a, n0)) {
+      pc = guess;
+      if (pc.b < 0) return;   // fewer pieces than workgroups (nothing was issued)
+    } else {
+      L1 = piece_span(a, n0, SLOTS_1, a.L1_min);
+      pc = uniform(piece_of(a, n0, L1, (int)blockIdx.x));
+      const bool same = spec && pc.b == guess.b && pc.h == guess.h && pc.n == guess.n &&
+                        pc.t0 == guess.t0 && pc.t1 == guess.t1;
+      if (!same) {
+        if (spec) vm_wait<0>();   // no load of the guess may land later
+        if (pc.b < 0) return;     // fewer pieces than workgroups
+        take(pc);
+        load_q();
+        for (int p = 0; p < NB - 1; ++p)
+          if (p < ntiles) gload_lds(p, p);
+      }
+    }
+    if (a.hist && pc.j == 0)   // the head's key histogram starts empty
+      for (int i = tid; i < KEY_BINS; i += NT) a.hist[(size_t)head * KEY_BINS + i] = 0u;
+  } else {
+    const int n0 = first_lens(a);
+    if (equal_lengths(a, n0)) {
+      pc = uniform(dense_piece(a, a.dense2, (int)blockIdx.x));
+      if (pc.b < 0) return;   // fewer pieces than workgroups
+      take(pc);
+      load_q();
+      const int k1 = a.dense1.x;
+      hp = make_int2((b * a.Hkv + h) * k1, k1);
+    } else {
+      if (!a.lse_in && a.self_merge) L1 = piece_span(a, n0, SLOTS_1, a.L1_min);
+      pc = uniform(piece_of(a, n0, piece_span(a, n0, a.G2, MIN_SPAN), (int)blockIdx.x));
+      if (pc.b < 0) return;   // fewer pieces than workgroups
+      take(pc);
+      load_q();
+      if (L1) hp = head_pieces(a, n0, L1, b, h);
+    }
+  }
+  const int last_w0 = n - a.W;   // position of window row 0; row w sits at last_w0 + w
+  // Leading tiles whose every token exists and is visible to every row.
+  int clean_tiles = (t1 - t0) / TOK;
+  if (a.causal) clean_tiles = min(clean_tiles, max(0, (last_w0 + 1 - t0) / TOK));
+  const float cc = a.c;
+
+  // Causal limits: p_row[i] = position of the lane's pass-1 row (row block i);
+  // rowpos[r] = window position (r mod W) of every row, for the pass-2 masks.
+  int p_row[RBW];
+#pragma unroll
+  for (int i = 0; i < RBW; ++i) {
+    const int r = (wave * RBW + i) * 32 + l32;
+    p_row[i] = a.causal ? last_w0 + (r % a.W) : 0x7fffffff;
+  }
+  if (PASS == 2 && a.causal)
+    for (int r = tid; r < NW * RBW * 32; r += NT) rowpos[r] = r % a.W;
+  if (PASS == 2 && a.hist)   // cleared before tile 0's barrier, counted after it
+    for (int i = tid; i < KEY_BINS; i += NT) khist[i] = 0u;
+
+  // Pass-1 running state (per row owned by the lane) / pass-2 negated row lse2.
+  float m_run[RBW], s_run[RBW];
+  float nl2[RBW][16];
+  const float inv_w = 1.0f / (float)a.W;
+  if (PASS == 1) {
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) { m_run[i] = -INFINITY; s_run[i] = 0.f; }
+  } else if (a.lse_in) {
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = (wave * RBW + i) * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+        // caller's natural-log LSE of row (j, w), to base 2;
+        // rc / W by a float reciprocal: exact for rc < 1024 (error < 0.5/W)
+        const int rc = min(r, a.R - 1);
+        const int jw = (int)(((float)rc + 0.5f) * inv_w);
+        const int j = h * a.G + jw, w = rc - jw * a.W;
+        const float v = a.lse_in[((size_t)b * a.Hq + j) * a.W + w] * (float)LOG2E_D;
+        nl2[i][e] = r < a.R ? -v : -INFINITY;
+      }
+    }
+  } else if (!a.self_merge) {   // the fold's row LSEs
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = (wave * RBW + i) * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+        nl2[i][e] = r < a.R ? -a.lse2[(size_t)head * a.R_pad + min(r, a.R_pad - 1)] : -INFINITY;
+      }
+    }
+  } else {
+    // Base-2 LSE of each row from pass 1's per-piece (m, sum) partials of
+    // this head (at most SELF_MERGE, consecutive, loads all issued at once),
+    // in piece order: M = max of the m's, then the sum of sum * 2^(m - M).
+    // Staged in `red` (not in use before tile 0).
+    float* lse_s = &red[0][0][0];
+    for (int r = tid; r < NW * RBW * 32; r += NT) {
+      float v = INFINITY;
+      if (r < a.R) {
+        const float2* src = a.part + (size_t)hp.x * a.R_pad + r;
+        float2 pk[SELF_MERGE];
+#pragma unroll
+        for (int u = 0; u < SELF_MERGE; ++u)   // piece u of the row: lanes read consecutive rows
+          pk[u] = u < hp.y ? src[(size_t)u * a.R_pad] : make_float2(-INFINITY, 0.f);
+        float M = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < SELF_MERGE; ++u) M = fmaxf(M, pk[u].x);
+        if (M != -INFINITY) {
+          float S = 0.f;
+#pragma unroll
+          for (int u = 0; u < SELF_MERGE; ++u) S = fmaf(pk[u].y, fast_exp2(pk[u].x - M), S);
+          if (S > 0.f) v = M + log2f(S);
+        }
+      }
+      lse_s[r] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = (wave * RBW + i) * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+        nl2[i][e] = r < a.R ? -lse_s[r] : -INFINITY;
+      }
+    }
+  }
 
   // ---- software pipeline over 32-token blocks j (two per 64-token tile) ----
   // The two 32-row blocks of the wave alternate between the matrix core and
@@ -581,11 +723,12 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
   };
   auto masked_tile = [&](int tile) { return tile >= clean_tiles; };
 
-  // Tiles 0 .. NB-2 requested up front; at tile t (after its barrier, which
-  // also tells that every wave is done with tile t-1) tile t + NB - 1 goes
-  // into the buffer tile t-1 used.
-  for (int p = 0; p < NB - 1; ++p)
-    if (p < ntiles) gload_lds(p, p);
+  // Tiles 0 .. NB-2 requested up front (pass 1 did so with its piece); at
+  // tile t (after its barrier, which also tells that every wave is done with
+  // tile t-1) tile t + NB - 1 goes into the buffer tile t-1 used.
+  if (PASS == 2)
+    for (int p = 0; p < NB - 1; ++p)
+      if (p < ntiles) gload_lds(p, p);
   // tile 0
   wait_tile(0);
   __syncthreads();
@@ -651,7 +794,7 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
       if (mn != -INFINITY) s = s_run[i] * fast_exp2(m_run[i] - mn) + so * fast_exp2(mo - mn);
       const int r = (wave * RBW + i) * 32 + l32;
       if (hf == 0 && r < a.R_pad)
-        a.part[((size_t)head * a.n_chunks + c) * a.R_pad + r] = make_float2(mn, s);
+        a.part[(size_t)blockIdx.x * a.R_pad + r] = make_float2(mn, s);
     }
   }
 }
@@ -663,9 +806,9 @@ __device__ __forceinline__ void merge(float& m, float& s, float pm, float ps) {
   m = mn;
 }
 
-// FOLD_LANES lanes per row (four rows per wave): the lanes merge chunks
-// c = l, l + FOLD_LANES, ... in order, then a fixed butterfly merges the
-// lanes; deterministic for fixed sizes.
+// FOLD_LANES lanes per row (four rows per wave): the lanes merge the head's
+// pass-1 pieces c = l, l + FOLD_LANES, ... in order, then a fixed butterfly
+// merges the lanes; deterministic for fixed lengths and sizes.
 constexpr int FOLD_LANES = 16;
 
 __global__ __launch_bounds__(256) void score_fold(ScoreArgs a) {
@@ -674,9 +817,19 @@ __global__ __launch_bounds__(256) void score_fold(ScoreArgs a) {
   const bool live = row_id < a.B * a.Hkv * a.R_pad;   // the butterfly needs every lane
   const int head = row_id / a.R_pad, r = row_id % a.R_pad;
   float m = -INFINITY, s = 0.f;
+  // the head's pass-1 pieces (per lane: the four rows of a wave may belong
+  // to different heads)
+  const int L1 = piece_span(a, first_lens(a), SLOTS_1, a.L1_min);
+  int first = 0, k = 0;
+  if (live) {
+    const int b = head / a.Hkv;
+    for (int bb = 0; bb < b; ++bb) first += (seq_tiles(a, bb) + L1 - 1) / L1;
+    k = (seq_tiles(a, b) + L1 - 1) / L1;
+    first = first * a.Hkv + (head - b * a.Hkv) * k;
+  }
   if (live && r < a.R) {
-    const float2* src = a.part + (size_t)head * a.n_chunks * a.R_pad + r;
-    for (int c = l; c < a.n_chunks; c += FOLD_LANES) {
+    const float2* src = a.part + (size_t)first * a.R_pad + r;
+    for (int c = l; c < k; c += FOLD_LANES) {
       const float2 p = src[(size_t)c * a.R_pad];
       merge(m, s, p.x, p.y);
     }
@@ -706,24 +859,31 @@ __global__ __launch_bounds__(256) void score_fold(ScoreArgs a) {
 }
 
 struct ScorePlan {
-  int G, R, R_pad, NW, TC, n_chunks;
-  size_t off_lse, off_tab, bytes;
+  int G, R, R_pad, NW;
+  int L1_min;       // pass-1 span floor
+  int self_merge;   // see plan_score
+  int3 dense1;      // pass-1 pieces per head at full length, tiles per piece (dense_params)
+  int C1;           // pass-1 workgroups: max(SLOTS_1, heads)
+  size_t off_lse, bytes;
 };
 
-// Tokens per workgroup: the tile count per chunk (at least `min_tiles`) that
-// minimises rounds * tiles-per-chunk when `slots` workgroups are resident,
-// i.e. the fewest tile-times for the whole grid; ties go to bigger chunks.
-int chunk_tokens(int64_t heads, int N_max, int64_t slots, int min_tiles) {
-  const int64_t tiles = ceil_div64(N_max, TOK);
-  int64_t best = tiles, best_cost = INT64_MAX;
-  for (int64_t tpc = std::min<int64_t>(min_tiles, tiles); tpc <= tiles; ++tpc) {
-    const int64_t wgs = heads * ceil_div64(tiles, tpc);
-    const int64_t cost = ceil_div64(wgs, slots) * tpc;
-    if (cost <= best_cost) { best_cost = cost; best = tpc; }
-  }
-  return (int)(best * TOK);
+// The partition piece_span finds when every head holds N_max tokens (tiles
+// of them): the smallest L >= lo = max(floor, ceil(H tiles / C)) with
+// H ceil(tiles / L) <= C, i.e. with ceil(tiles / L) <= floor(C / H); as
+// (pieces per head k, tiles / k, tiles mod k).
+int3 dense_params(int64_t H, int64_t tiles, int64_t C, int64_t floor_tiles) {
+  const int64_t lo = std::max<int64_t>(floor_tiles, ceil_div64(H * tiles, C));
+  const int64_t L = std::max<int64_t>(lo, ceil_div64(tiles, C / H));
+  const int64_t k = ceil_div64(tiles, L);
+  return make_int3((int)k, (int)(tiles / k), (int)(tiles - (tiles / k) * k));
 }
 
+// Sizes-only decisions, so that the pass-1 partition, and the result bit for
+// bit, never depend on the device.  Spans are at least MIN_SPAN tiles.  When
+// a floor of ceil(tiles(N_max) / SELF_MERGE) tiles costs nothing at full
+// length (it does not exceed the full-length span), pass 1 takes it: a head
+// then has at most SELF_MERGE partials, which pass 2 merges itself;
+// otherwise (many tiles per head, few heads) the fold merges them.
 bool plan_score(int B, int Hq, int Hkv, int N_max, int W, int d, ScorePlan* p) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || N_max < 1 || W < 1 || W > N_max) return false;
   if (d != 64 && d != 128) return false;
@@ -736,15 +896,16 @@ bool plan_score(int B, int Hq, int Hkv, int N_max, int W, int d, ScorePlan* p) {
   p->R_pad = RB * 32;
   const int nw = ceil_div(RB, RBW);
   p->NW = nw <= 1 ? 1 : nw <= 2 ? 2 : nw <= 4 ? 4 : nw <= 8 ? 8 : 16;
-  // Pass-1 chunking depends on the sizes only, so the merge order (and the
-  // result, bit for bit) does not depend on the device.
-  p->TC = chunk_tokens((int64_t)B * Hkv, N_max, SLOTS_1, 4);
-  p->n_chunks = ceil_div(N_max, p->TC);
-  const size_t part = (size_t)B * Hkv * p->n_chunks * p->R_pad * sizeof(float2);
+  const int64_t H = (int64_t)B * Hkv, tiles = ceil_div64(N_max, TOK);
+  p->C1 = (int)std::max<int64_t>(SLOTS_1, H);
+  const int64_t full_span = std::max<int64_t>(MIN_SPAN, ceil_div64(H * tiles, p->C1));
+  const int64_t merge_floor = ceil_div64(tiles, SELF_MERGE);
+  p->self_merge = merge_floor <= full_span ? 1 : 0;
+  p->L1_min = (int)(p->self_merge ? std::max<int64_t>(MIN_SPAN, merge_floor) : MIN_SPAN);
+  p->dense1 = dense_params(H, tiles, p->C1, p->L1_min);
+  const size_t part = (size_t)p->C1 * p->R_pad * sizeof(float2);
   p->off_lse = (part + 255) & ~size_t(255);
-  const size_t lse_end = p->off_lse + (size_t)B * Hkv * p->R_pad * sizeof(float);
-  p->off_tab = (lse_end + 255) & ~size_t(255);
-  p->bytes = p->off_tab + (size_t)TAB_MAX * sizeof(int4);
+  p->bytes = p->off_lse + (size_t)H * p->R_pad * sizeof(float);
   return true;
 }
 
@@ -769,27 +930,19 @@ int resident_slots(K kernel, int threads, std::atomic<int>* cache) {
 template <typename T, int D, int NW>
 void launch_score(ScoreArgs a, hipStream_t st) {
   static std::atomic<int> slots_cache[MAX_DEVICES];   // zero: not yet known
-  const int slots2 = resident_slots(score_pass<T, D, NW, 2>, NW * WAVE, slots_cache);
-  a.TC2 = chunk_tokens((int64_t)a.B * a.Hkv, a.N_max, slots2, 4);
-  a.n_chunks2 = ceil_div(a.N_max, a.TC2);
-  const dim3 grid1(a.n_chunks, a.Hkv, a.B);
-  dim3 grid2(a.n_chunks2, a.Hkv, a.B);
-  // Balanced pass-2 ranges (two-pass path): one workgroup per resident slot,
-  // at least two per head; pass 1 writes the table
+  a.G2 = resident_slots(score_pass<T, D, NW, 2>, NW * WAVE, slots_cache);
   const int H = a.B * a.Hkv;
-  a.G2 = std::min(slots2, TAB_MAX);
-  a.ranges = a.tab && !a.lse_in && H <= RANGE_HEADS && 2 * H <= a.G2 ? 1 : 0;
-  if (a.ranges) grid2 = dim3((unsigned)a.G2, 1, 1);
-  a.self_merge = a.n_chunks <= SELF_MERGE ? 1 : 0;
+  a.dense2 = dense_params(H, ceil_div64(a.N_max, TOK), std::max(a.G2, H), MIN_SPAN);
+  const dim3 grid1((unsigned)std::max(SLOTS_1, H)), grid2((unsigned)std::max(a.G2, H));
   if (a.lse_in) {   // row LSEs given: the column-sum pass alone
     launch("score_colsum", score_pass<T, D, NW, 2>, grid2, dim3(NW * WAVE), 0, st, a);
     return;
   }
   launch("score_rowstats", score_pass<T, D, NW, 1>, grid1, dim3(NW * WAVE), 0, st, a);
-  // with few chunks pass 2 merges the partials of its own head, and the fold
-  // runs only to hand the caller the row LSEs
+  // in self-merge mode pass 2 merges the partials of its own head, and the
+  // fold runs only to hand the caller the row LSEs
   if (a.row_lse || !a.self_merge) {
-    const int rows = a.B * a.Hkv * a.R_pad;
+    const int rows = H * a.R_pad;
     launch("score_fold", score_fold, dim3(ceil_div(rows, 256 / FOLD_LANES)), dim3(256), 0, st, a);
   }
   launch("score_colsum", score_pass<T, D, NW, 2>, grid2, dim3(NW * WAVE), 0, st, a);
@@ -825,10 +978,10 @@ ScoreArgs two_pass_args(const void* q_win, const void* k, const int32_t* ctx_len
   a.lse_in = nullptr;
   a.part = static_cast<float2*>(ws);
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_lse);
-  a.tab = reinterpret_cast<int4*>(static_cast<char*>(ws) + p.off_tab);
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N_max = N_max; a.W = W; a.G = p.G;
-  a.R = p.R; a.R_pad = p.R_pad; a.TC = p.TC; a.n_chunks = p.n_chunks;
-  a.TC2 = p.TC; a.n_chunks2 = p.n_chunks;
+  a.R = p.R; a.R_pad = p.R_pad; a.L1_min = p.L1_min; a.self_merge = p.self_merge;
+  a.dense1 = p.dense1;
+  a.G2 = SLOTS_1;   // set at launch
   a.causal = causal ? 1 : 0;
   a.c = (float)((scale > 0.f ? (double)scale : 1.0 / sqrt((double)d)) * LOG2E_D);
   a.hist = nullptr;
@@ -935,10 +1088,11 @@ extern "C" int kv_score_from_lse(const void* q_win, const void* k, const int32_t
 
   ScoreArgs a;
   a.q = q_win; a.k = k; a.ctx = ctx_len; a.scores = scores; a.row_lse = nullptr;
-  a.lse_in = row_lse_in; a.part = nullptr; a.lse2 = nullptr; a.tab = nullptr;
+  a.lse_in = row_lse_in; a.part = nullptr; a.lse2 = nullptr;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N_max = N_max; a.W = W; a.G = p.G;
-  a.R = p.R; a.R_pad = p.R_pad; a.TC = p.TC; a.n_chunks = p.n_chunks;
-  a.TC2 = p.TC; a.n_chunks2 = p.n_chunks;
+  a.R = p.R; a.R_pad = p.R_pad; a.L1_min = p.L1_min; a.self_merge = p.self_merge;
+  a.dense1 = p.dense1;
+  a.G2 = SLOTS_1;   // set at launch
   a.causal = causal ? 1 : 0;
   a.c = (float)((scale > 0.f ? (double)scale : 1.0 / sqrt((double)d)) * LOG2E_D);
   a.hist = nullptr;

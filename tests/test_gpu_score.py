@@ -40,6 +40,57 @@ def test_score_small(case):
     log(f"  max rel score err {err:.3e}")
 
 
+PARTITION_CASES = [
+    # id, B, Hq, Hkv, W, N_max, ctx (None: random lengths in [0, N_max], seeded)
+    ("equal_tiles_unequal_lengths", 2, 4, 2, 4, 64, [64, 33]),
+    ("uniform_with_lengths", 3, 8, 2, 16, 700, [700, 700, 700]),
+    ("uniform_without_lengths", 3, 8, 2, 16, 700, "none"),
+    ("20_sequences", 20, 4, 2, 8, 600, None),                 # two groups of 16 lengths
+    ("70_sequences_560_heads", 70, 8, 8, 4, 200, None),       # past 64 sequences and 512 heads
+    ("one_long_head_among_short", 5, 8, 2, 16, 20000, [20000, 70, 0, 300, 64]),
+]
+
+
+@pytest.mark.parametrize("case", PARTITION_CASES, ids=lambda c: c[0])
+def test_score_partition_shapes(case):
+    # The score passes split the heads' tiles into pieces from the lengths
+    # (pieces never cross a head; equal lengths take the precomputed
+    # partition): scores and row LSEs against the oracle, and kv_score_select
+    # equal to kv_score + kv_select bit for bit.
+    name, B, Hq, Hkv, W, N, ctx = case
+    log(f"score partition {name}")
+    if ctx is None:
+        rng = np.random.default_rng(B * 1000 + N)
+        ctx = [int(x) for x in rng.integers(W, N + 1, size=B)]
+        ctx[0] = N
+        ctx[-1] = W
+    ctx_arg = None if ctx == "none" else ctx
+    lay = wl.random_case(31, B=B, Hq=Hq, Hkv=Hkv, d=64, N_max=N, W=W, dtype=torch.bfloat16,
+                         ctx=ctx_arg)
+    c = None if ctx_arg is None else dev(lay.ctx_len)
+    s_gpu, lse_gpu = api.kv_score(dev(lay.q_win), dev(lay.k), c, with_row_lse=True)
+    budget = api.Budget(api.BUDGET_RATIO, ratio_scalar=0.2)
+    s2, lse2, i2, n2 = api.kv_score_select(dev(lay.q_win), dev(lay.k), c, budget, with_row_lse=True)
+    i1, n1 = api.kv_select(s_gpu, c, budget)
+    torch.cuda.synchronize()
+    lens = lay.ctx_len.numpy()
+    nz = np.flatnonzero(lens > 0)   # the oracle takes the non-empty sequences
+    s_ref, lse_ref = orc.window_scores(lay.q_win[nz], lay.k[nz], lay.ctx_len[nz])
+    check_scores(s_gpu.cpu().numpy()[nz], s_ref, lens[nz], W, Hq // Hkv)
+    np.testing.assert_allclose(lse_gpu.cpu().numpy()[nz], lse_ref, atol=1e-3, rtol=0)
+    if len(nz) < B:   # an empty sequence has no pieces: its rows see nothing
+        assert np.all(np.isneginf(lse_gpu.cpu().numpy()[lens == 0]))
+    for b, n in enumerate(lens):
+        assert torch.equal(s_gpu[b, :, :n].view(torch.int32), s2[b, :, :n].view(torch.int32))
+    assert torch.equal(lse_gpu.view(torch.int32), lse2.view(torch.int32))
+    assert torch.equal(n1, n2)
+    a1, a2, cnt = i1.cpu().numpy(), i2.cpu().numpy(), n1.cpu().numpy()
+    for b in range(B):
+        for h in range(Hkv):
+            k = int(cnt[b * Hkv + h])
+            assert np.array_equal(a1[b, h, :k], a2[b, h, :k]), (b, h)
+
+
 def test_score_scale_argument():
     lay = wl.random_case(3, B=1, Hq=4, Hkv=2, d=64, N_max=400, W=8)
     s_gpu, _ = api.kv_score(dev(lay.q_win), dev(lay.k), None, scale=0.3)

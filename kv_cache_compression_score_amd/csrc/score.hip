@@ -44,7 +44,7 @@ constexpr int RBW = 2;           // 32-row blocks per wave
 constexpr int SLOTS_1 = 256 * 2; // pass-1 partition target (resident workgroups on 256 CUs);
                                  // fixed, so the pass-1 partition, its merge order and the
                                  // result never depend on the device
-constexpr int MIN_SPAN = 4;      // fewest tiles per piece span
+constexpr int MIN_SPAN = 4;      // fewest tiles per pass-1 piece span (pass 2: one)
 constexpr int SELF_MERGE = 16;   // pass 2 merges pass 1's partials itself up to this many per head
 
 template <typename T> struct FragT;
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
       hp = make_int2((b * a.Hkv + h) * k1, k1);
     } else {
       if (!a.lse_in && a.self_merge) L1 = piece_span(a, n0, SLOTS_1, a.L1_min);
-      pc = uniform(piece_of(a, n0, piece_span(a, n0, a.G2, MIN_SPAN), (int)blockIdx.x));
+      pc = uniform(piece_of(a, n0, piece_span(a, n0, a.G2, 1), (int)blockIdx.x));
       if (pc.b < 0) return;   // fewer pieces than workgroups
       take(pc);
       load_q();
@@ -932,7 +932,7 @@ void launch_score(ScoreArgs a, hipStream_t st) {
   static std::atomic<int> slots_cache[MAX_DEVICES];   // zero: not yet known
   a.G2 = resident_slots(score_pass<T, D, NW, 2>, NW * WAVE, slots_cache);
   const int H = a.B * a.Hkv;
-  a.dense2 = dense_params(H, ceil_div64(a.N_max, TOK), std::max(a.G2, H), MIN_SPAN);
+  a.dense2 = dense_params(H, ceil_div64(a.N_max, TOK), std::max(a.G2, H), 1);
   const dim3 grid1((unsigned)std::max(SLOTS_1, H)), grid2((unsigned)std::max(a.G2, H));
   if (a.lse_in) {   // row LSEs given: the column-sum pass alone
     launch("score_colsum", score_pass<T, D, NW, 2>, grid2, dim3(NW * WAVE), 0, st, a);

@@ -14,9 +14,12 @@ timing starts.  Prints one JSON line:
               the 256 MB Infinity Cache hold nothing of the step's data
               (step_ms_warm: the same steps back to back)
   roofline    the kernel with the most GPU time: algorithmic FLOPs (MFMA
-              kernels) or bytes (HBM kernels) per launch / its mean duration
-              over the timed steps, durations from hipEvents that the
-              library's dispatches stamp on their own stream; `traffic` is the
+              kernels) or bytes (HBM kernels) per launch / its mean duration,
+              from hipEvents that the library's dispatches stamp on their own
+              stream, over a second run of as many cold steps right after the
+              timed ones (stamped dispatches lengthen a step by a few us, so
+              the steps that give `value` carry none; that run's step times
+              are step_ms_cold_kernel_events); `traffic` is the
               HBM bytes per launch that rocprofv3's FETCH_SIZE + WRITE_SIZE
               counters read for that kernel (scaled by the ratio of known to
               counted bytes of a plain device copy), taken from the committed
@@ -152,15 +155,20 @@ class Pipeline:
                            workspace=self.ws_d)
 
 
-def settle_clocks(step, seconds: float = 0.1) -> int:
+def settle_clocks(step, seconds: float = 0.1, flush=None) -> int:
     """Run the step untimed for about `seconds` of wall time.  From a cold
     start the GPU needs a few tens of ms of sustained load before its clocks
     settle (the first steps run up to 20% slower), so the warmup steps alone
-    would leave the timed region on the ramp.  Returns the steps run."""
+    would leave the timed region on the ramp.  The clocks settle again when
+    the load changes: with `flush`, each step is preceded by it, as in the
+    cold timed steps (after back-to-back steps, the first 40 or so flushed
+    steps run 3-6% slower).  Returns the steps run."""
     n = 0
     t_end = time.perf_counter() + seconds
     while time.perf_counter() < t_end:
         for _ in range(10):
+            if flush is not None:
+                flush()
             step()
         n += 10
         torch.cuda.synchronize()
@@ -481,13 +489,21 @@ def measure_headline(lay: wl.Layer, args, extras: bool) -> dict:
     # The timed region: K cold steps (a 1 GiB read before each, outside its
     # events), events on the roofline kernel's dispatches.
     flush = Flush()
-    settle_clocks(pipe.step)
+    settle_clocks(pipe.step, flush=flush)
     for _ in range(args.warmup):
         flush()
         pipe.step()
     torch.cuda.synchronize()
-    log(f"bench: {args.warmup} warmup steps, timing {args.steps} cold steps (events on {dom})")
-    cold, wall_cold, kt_dom = step_distribution(pipe.step, args.steps, flush, only=dom)
+    log(f"bench: {args.warmup} warmup steps, timing {args.steps} cold steps")
+    cold, wall_cold, _ = step_distribution(pipe.step, args.steps, flush)
+    # The roofline kernel's own dispatch-stamped events, over as many cold
+    # steps again: stamping a dispatch lengthens the step by a few us, so
+    # the steps above carry no stamps.  The first 40 or so stamped steps
+    # run slower than the rest (that kernel up to 3 us), so 40 stamped
+    # steps go first, untimed.
+    step_distribution(pipe.step, 40, flush, only=dom)
+    log(f"bench: {args.steps} more cold steps with events on {dom}'s dispatches")
+    cold_ev, _, kt_dom = step_distribution(pipe.step, args.steps, flush, only=dom)
     bound, amount = work[dom]
     t_dom = kt_dom[dom][0] * 1e-3
     if bound == "mfma":
@@ -520,6 +536,7 @@ def measure_headline(lay: wl.Layer, args, extras: bool) -> dict:
                      "traffic": measured_traffic(dom, cfg.name)},
         "targets": stage_targets({k: v[0] for k, v in kt.items()}, acc, peak_f),
         "step_ms_cold": cold,
+        "step_ms_cold_kernel_events": cold_ev,
         "step_ms_warm": warm,
         "warm_back_to_back_ms_per_step": ms_b2b,
         "timed_region_wall_ms": wall_cold,
@@ -575,6 +592,7 @@ def measure_workload(lay: wl.Layer, steps: int) -> dict:
     settle_clocks(pipe.step)
     _, kt = timed_steps(pipe.step, steps)
     flush = Flush()
+    settle_clocks(pipe.step, flush=flush)
     cold, _, _ = step_distribution(pipe.step, steps, flush)
     settle_clocks(pipe.step)
     warm, _, _ = step_distribution(pipe.step, steps)

@@ -10,7 +10,8 @@
 // rebuilds the item list from the offsets in LDS and walks it grid-stride,
 // so ragged heads balance by rows, not by head count.  Inside an item a group
 // of d*sizeof(T)/16 lanes owns one row at a time (16 bytes of K and of V per
-// lane, RPG rows in flight), forms the G dot products (bf16: v_dot2 against
+// lane; RPS rows per stage, the next stage in flight while one is computed),
+// forms the G dot products (bf16: v_dot2 against
 // the packed query) with a DPP reduction inside the group, and keeps a
 // base-2 (max, sum, o) per query head.  Groups merge through LDS in a fixed
 // order into one partial per item; a second kernel merges each head's items
@@ -27,8 +28,9 @@ namespace kvcc {
 namespace {
 
 constexpr int DT = 256;
-constexpr int CH = 256;          // rows per work item (two passes of NG*RPG rows)
-constexpr int RPG = 8;           // rows per lane group per pass over an item
+constexpr int CH = 256;          // rows per work item
+constexpr int RPG = 8;           // rows per lane group per pass (routed cache)
+constexpr int RPS = 4;           // rows per lane group per stage (plain and fused split)
 constexpr int MAX_HEADS = 4096;
 constexpr int GRID_MAX = 1024;   // most split workgroups per query-head group
 
@@ -283,18 +285,25 @@ struct GroupMerge {
 // FUSED: the rows come from the full cache through the kept indices and are
 // written to the packed cache on the way (kv_compact_decode); the arithmetic
 // is the same, so the result equals kv_compact followed by kv_decode_attn.
+// An item is walked in stages of NG * RPS rows, two register sets deep: the
+// next stage's loads are in flight while this one is computed.  Every load is
+// branch-free (a row past the item re-reads the item's last row, an index
+// outside [0, N_max) reads token 0; both are masked or zeroed afterwards), so
+// waiting for one stage never waits for the next.
 template <typename T, int D, int GT, bool FUSED>
 __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
   constexpr int EPL = 16 / (int)sizeof(T);     // elements per lane
   constexpr int LPR = D / EPL;                 // lanes per row (power of two, <= 32)
   constexpr int NG = DT / LPR;                 // row groups per workgroup
-  constexpr int PASS = NG * RPG;               // rows per pass over an item
+  constexpr int PS = NG * RPS;                 // rows per stage
   constexpr int ROWB = D * (int)sizeof(T);
+  static_assert(CH % (2 * PS) == 0, "an item is a whole number of stage pairs");
   typedef GroupMerge<NG, GT, D> Merge;
 
   __shared__ int wtot[DT / WAVE];
   __shared__ float sm_m[NG][GT], sm_l[NG][GT];
   __shared__ float sm_o[NG][GT][D];
+  __shared__ int sidx[CH];             // fused: the item's kept indices (-1 past its end)
   extern __shared__ long long dyn[];   // off[H+1] (int64) then ist[H+1] (int32)
   const int H = a.B * a.Hkv;
   long long* off = dyn;
@@ -317,42 +326,53 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
     qs.template load<D>(a, b, h, qsub, sub);
     RowState<GT, EPL> st;
     st.reset();
-    // fused: the kept indices of a pass are loaded while the previous pass's
-    // rows are in flight
-    int tn[RPG];
-    auto load_idx = [&](long long base) __attribute__((always_inline)) {
-#pragma unroll
-      for (int u = 0; u < RPG; ++u) {
-        const long long row = base + grp + (long long)u * NG;
+    if constexpr (FUSED) {   // one round trip for the item's indices
+      for (int i = tid; i < CH; i += DT) {
+        const long long row = r0 + i;
         const long long r = row - off[head];
-        tn[u] = row < r1 && r < a.N_max ? a.idx[(size_t)head * a.N_max + r] : -1;
+        sidx[i] = row < r1 && r < a.N_max ? a.idx[(size_t)head * a.N_max + r] : -1;
+      }
+      __syncthreads();
+    }
+    // row u of a stage at `base` is base + grp + u * NG
+    auto issue = [&](uint4 (&kr)[RPS], uint4 (&vr)[RPS], long long base)
+        __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < RPS; ++u) {
+        const long long row = base + grp + (long long)u * NG;
+        size_t src;
+        if constexpr (FUSED) {
+          const int t = sidx[(int)(row - r0)];
+          src = ((size_t)head * a.N_max + ((unsigned)t < (unsigned)a.N_max ? t : 0)) * ROWB;
+        } else {
+          src = (size_t)min(row, r1 - 1) * ROWB;
+        }
+        const char* kb = FUSED ? a.ksrc : a.kc;
+        const char* vb = FUSED ? a.vsrc : a.vc;
+        kr[u] = ld16(kb + src + sub * 16);
+        vr[u] = ld16(vb + src + sub * 16);
       }
     };
-    if constexpr (FUSED) load_idx(r0);
-    for (long long base = r0; base < r1; base += PASS) {
-      uint4 kr[RPG], vr[RPG];
-      bool ok[RPG];
+    auto process = [&](uint4 (&kr)[RPS], uint4 (&vr)[RPS], long long base)
+        __attribute__((always_inline)) {
+      bool ok[RPS];
+#pragma unroll
+      for (int u = 0; u < RPS; ++u) ok[u] = base + grp + (long long)u * NG < r1;
       if constexpr (FUSED) {
-        int t[RPG];
+        int t[RPS];
 #pragma unroll
-        for (int u = 0; u < RPG; ++u) t[u] = tn[u];
-#pragma unroll
-        for (int u = 0; u < RPG; ++u) {
+        for (int u = 0; u < RPS; ++u) {
+          t[u] = sidx[(int)(base + grp + (long long)u * NG - r0)];
           // an index outside [0, N_max) packs a zero K/V row (as kv_compact
           // does), which the attention then reads like any other row
-          ok[u] = base + grp + (long long)u * NG < r1;
-          kr[u] = make_uint4(0, 0, 0, 0);
-          vr[u] = make_uint4(0, 0, 0, 0);
-          if ((unsigned)t[u] < (unsigned)a.N_max) {
-            const size_t src = ((size_t)head * a.N_max + t[u]) * ROWB + sub * 16;
-            kr[u] = ld16(a.ksrc + src);
-            vr[u] = ld16(a.vsrc + src);
+          if ((unsigned)t[u] >= (unsigned)a.N_max) {
+            kr[u] = make_uint4(0, 0, 0, 0);
+            vr[u] = make_uint4(0, 0, 0, 0);
           }
         }
-        if (base + PASS < r1) load_idx(base + PASS);
         if (qsub == 0) {
 #pragma unroll
-          for (int u = 0; u < RPG; ++u) {
+          for (int u = 0; u < RPS; ++u) {
             const long long row = base + grp + (long long)u * NG;
             if (ok[u]) {
               st16(a.kc_w + (size_t)row * ROWB + sub * 16, kr[u]);
@@ -361,22 +381,10 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
             }
           }
         }
-      } else {
-#pragma unroll
-        for (int u = 0; u < RPG; ++u) {
-          const long long row = base + grp + (long long)u * NG;
-          ok[u] = row < r1;
-          kr[u] = make_uint4(0, 0, 0, 0);
-          vr[u] = make_uint4(0, 0, 0, 0);
-          if (ok[u]) {
-            kr[u] = ld16(a.kc + (size_t)row * ROWB + sub * 16);
-            vr[u] = ld16(a.vc + (size_t)row * ROWB + sub * 16);
-          }
-        }
       }
-      float sc[RPG][GT];
+      float sc[RPS][GT];
 #pragma unroll
-      for (int u = 0; u < RPG; ++u)
+      for (int u = 0; u < RPS; ++u)
 #pragma unroll
         for (int g = 0; g < GT; ++g) {
           sc[u][g] = group_sum<LPR>(qs.score(g, kr[u], a.c));
@@ -384,13 +392,23 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
         }
       st.cover(sc, ok);
 #pragma unroll
-      for (int u = 0; u < RPG; ++u) {
+      for (int u = 0; u < RPS; ++u) {
         if (ok[u]) {
           float vx[EPL];
           unpack16<T>(vr[u], vx);
           st.add(sc[u], vx);
         }
       }
+    };
+    uint4 kr0[RPS], vr0[RPS], kr1[RPS], vr1[RPS];
+    issue(kr0, vr0, r0);
+    for (long long base = r0; base < r1; base += 2 * PS) {
+      const long long b1 = base + PS;
+      if (b1 < r1) issue(kr1, vr1, b1);
+      process(kr0, vr0, base);
+      if (b1 >= r1) break;
+      if (b1 + PS < r1) issue(kr0, vr0, b1 + PS);
+      process(kr1, vr1, b1);
     }
 
     // merge the row groups (fixed order) into this item's partial

@@ -286,10 +286,12 @@ struct GroupMerge {
 // written to the packed cache on the way (kv_compact_decode); the arithmetic
 // is the same, so the result equals kv_compact followed by kv_decode_attn.
 // An item is walked in stages of NG * RPS rows, two register sets deep: the
-// next stage's loads are in flight while this one is computed.  Every load is
-// branch-free (a row past the item re-reads the item's last row, an index
-// outside [0, N_max) reads token 0; both are masked or zeroed afterwards), so
-// waiting for one stage never waits for the next.
+// next stage's loads go out once this stage's rows have landed (and, fused,
+// been stored) and stay in flight while this stage is computed.  Every load
+// is branch-free and every stage issues the next one (a row past the item
+// re-reads the item's last row, an index outside [0, N_max) reads token 0;
+// both are masked or zeroed afterwards), so the wait for a stage's rows never
+// covers the next stage's.
 template <typename T, int D, int GT, bool FUSED>
 __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
   constexpr int EPL = 16 / (int)sizeof(T);     // elements per lane
@@ -339,13 +341,13 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
         __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < RPS; ++u) {
-        const long long row = base + grp + (long long)u * NG;
+        const long long row = min(base + grp + (long long)u * NG, r1 - 1);
         size_t src;
         if constexpr (FUSED) {
           const int t = sidx[(int)(row - r0)];
           src = ((size_t)head * a.N_max + ((unsigned)t < (unsigned)a.N_max ? t : 0)) * ROWB;
         } else {
-          src = (size_t)min(row, r1 - 1) * ROWB;
+          src = (size_t)row * ROWB;
         }
         const char* kb = FUSED ? a.ksrc : a.kc;
         const char* vb = FUSED ? a.vsrc : a.vc;
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
         vr[u] = ld16(vb + src + sub * 16);
       }
     };
-    auto process = [&](uint4 (&kr)[RPS], uint4 (&vr)[RPS], long long base)
+    auto process = [&](uint4 (&kr)[RPS], uint4 (&vr)[RPS], long long base, auto&& next)
         __attribute__((always_inline)) {
       bool ok[RPS];
 #pragma unroll
@@ -382,6 +384,7 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
           }
         }
       }
+      next();
       float sc[RPS][GT];
 #pragma unroll
       for (int u = 0; u < RPS; ++u)
@@ -404,11 +407,9 @@ __global__ __launch_bounds__(DT) void decode_split(DecodeArgs a) {
     issue(kr0, vr0, r0);
     for (long long base = r0; base < r1; base += 2 * PS) {
       const long long b1 = base + PS;
-      if (b1 < r1) issue(kr1, vr1, b1);
-      process(kr0, vr0, base);
+      process(kr0, vr0, base, [&]() __attribute__((always_inline)) { issue(kr1, vr1, b1); });
       if (b1 >= r1) break;
-      if (b1 + PS < r1) issue(kr0, vr0, b1 + PS);
-      process(kr1, vr1, b1);
+      process(kr1, vr1, b1, [&]() __attribute__((always_inline)) { issue(kr0, vr0, b1 + PS); });
     }
 
     // merge the row groups (fixed order) into this item's partial

@@ -535,6 +535,10 @@ __device__ __forceinline__ void emit_regs(const uint4 (&ek)[EPI], int s0, int s1
   if (!all_ties)
     for (int w = 0; w < wave; ++w) eqr += sm.w_eq[w];
   uint32_t* stage = keys_lds + s0;
+  // one spare word per thread in sm.hmass, which no caller reads after the
+  // emit (the mass sums are done by then, and its first barrier, with
+  // LDS_BUSY, orders this after their last reads)
+  uint32_t* const spare = reinterpret_cast<uint32_t*>(sm.hmass) + threadIdx.x;
   uint32_t nk = 0;   // kept keys of this wave so far (uniform)
   // stage the kept ones of 4 keys per lane (token t + u), in token order
   auto put = [&](int t, bool k0, bool k1, bool k2, bool k3) {
@@ -547,13 +551,15 @@ __device__ __forceinline__ void emit_regs(const uint4 (&ek)[EPI], int s0, int s1
     at = __builtin_amdgcn_mbcnt_hi((uint32_t)(b2 >> 32), at);
     at = __builtin_amdgcn_mbcnt_lo((uint32_t)b3, at);
     at = __builtin_amdgcn_mbcnt_hi((uint32_t)(b3 >> 32), at);
-    if (k0) stage[at] = (uint32_t)t;
+    // a key not kept writes its token to the lane's own spare word instead
+    // (no branch and no exec-mask change per key)
+    *(k0 ? stage + at : spare) = (uint32_t)t;
     at += k0 ? 1u : 0u;
-    if (k1) stage[at] = (uint32_t)(t + 1);
+    *(k1 ? stage + at : spare) = (uint32_t)(t + 1);
     at += k1 ? 1u : 0u;
-    if (k2) stage[at] = (uint32_t)(t + 2);
+    *(k2 ? stage + at : spare) = (uint32_t)(t + 2);
     at += k2 ? 1u : 0u;
-    if (k3) stage[at] = (uint32_t)(t + 3);
+    *(k3 ? stage + at : spare) = (uint32_t)(t + 3);
     nk += (uint32_t)(__popcll(b0) + __popcll(b1) + __popcll(b2) + __popcll(b3));
   };
 #pragma unroll

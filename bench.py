@@ -12,7 +12,8 @@ timing starts.  Prints one JSON line:
               step time with cold caches: before every timed step, outside
               its events, a 1 GiB buffer is read so that the L2 caches and
               the 256 MB Infinity Cache hold nothing of the step's data
-              (step_ms_warm: the same steps back to back)
+              (step_ms_warm: the same steps back to back; step_ms_warm_graph:
+              the step captured once as a HIP graph and replayed back to back)
   roofline    the kernel with the most GPU time: algorithmic FLOPs (MFMA
               kernels) or bytes (HBM kernels) per launch / its mean duration,
               from hipEvents that the library's dispatches stamp on their own
@@ -28,6 +29,9 @@ timing starts.  Prints one JSON line:
   targets     the stage-level fractions: score (both passes) against the
               bf16 MFMA peak, select + compact + decode against HBM
   copy_gbps   a 1 GiB device-to-device copy (read + write bytes / time)
+  launch_shapes  workgroups and threads per workgroup of each kernel's launch
+  gpu         device name, ROCm and torch versions, and the clocks amd-smi
+              reports while the step runs back to back
   unfused     the same step with kv_compact and kv_decode_attn as two calls;
               decode_hbm_gbps is that decode's rate; score_then_select:
               kv_score and kv_select as two calls
@@ -189,8 +193,9 @@ def _timing_stop() -> dict:
     L.kv_timing_only(None)
     if n < 0:
         raise RuntimeError(f"kv_timing_read failed: {n}")
-    return {buf[i].name.decode(): (buf[i].total_ms / buf[i].launches, buf[i].launches)
-            for i in range(n)}
+    # name -> (mean ms, launches, (workgroups, threads per workgroup) of the last launch)
+    return {buf[i].name.decode(): (buf[i].total_ms / buf[i].launches, buf[i].launches,
+                                   (int(buf[i].grid), int(buf[i].block))) for i in range(n)}
 
 
 def timed_steps(step, steps: int, only=None, events: bool = True):
@@ -252,6 +257,55 @@ def step_distribution(step, steps: int, flush=None, only=None):
     wall = (time.perf_counter() - t0) * 1e3
     kt = _timing_stop() if only is not None else {}
     return _spread([a.elapsed_time(b) for a, b in ev]), wall, kt
+
+
+def graph_steps(step, steps: int) -> dict:
+    """The step captured once as a HIP graph (static buffers: the library
+    allocates nothing and records no memset) and replayed back to back,
+    each replay between events on the current stream."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    settle_clocks(g.replay)
+    spread, _, _ = step_distribution(g.replay, steps)
+    del g
+    return spread
+
+
+def gpu_clocks(step):
+    """The GPU's clocks as amd-smi reports them (a child process, 30 s at
+    most) while `step` runs back to back, so the reading is taken under the
+    bench's own load; None values with the reason if the tool fails."""
+    import subprocess
+    cmd = ["amd-smi", "metric", "--clock", "--json"]
+    try:
+        p = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+    except OSError as e:
+        return {"tool": None, "error": str(e)}
+    t_end = time.perf_counter() + 30.0
+    while p.poll() is None and time.perf_counter() < t_end:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+    if p.poll() is None:
+        p.kill()
+    out, err = p.communicate()
+    if p.returncode != 0:
+        return {"tool": "amd-smi", "error": f"exit {p.returncode}: {err.strip()[:200]}"}
+    try:
+        clk = json.loads(out)["gpu_data"][0]["clock"]
+        return {"tool": "amd-smi", "sampled": "while the step ran back to back",
+                "mhz": {k: v["clk"]["value"] for k, v in clk.items()
+                        if isinstance(v, dict) and isinstance(v.get("clk"), dict)}}
+    except (ValueError, KeyError, IndexError, TypeError):
+        return {"tool": "amd-smi", "report": out.strip()[:2000]}
 
 
 def one_pass_score_ms(pipe: Pipeline, steps: int) -> float:
@@ -515,6 +569,8 @@ def measure_headline(lay: wl.Layer, args, extras: bool) -> dict:
     settle_clocks(pipe.step)
     warm, _, _ = step_distribution(pipe.step, args.steps)
     ms_b2b, _ = timed_steps(pipe.step, args.steps, events=False)
+    warm_graph = graph_steps(pipe.step, args.steps)
+    clocks = gpu_clocks(pipe.step)
     res = {
         "metric": METRIC,
         "value": tokens / (cold["median"] * 1e-3),
@@ -542,6 +598,10 @@ def measure_headline(lay: wl.Layer, args, extras: bool) -> dict:
         "timed_region_wall_ms": wall_cold,
         "copy_gbps": copy_bw,
         "kernels_ms": {k: v[0] for k, v in kt.items()},
+        "step_ms_warm_graph": warm_graph,
+        "launch_shapes": {k: {"workgroups": v[2][0], "threads": v[2][1]} for k, v in kt.items()},
+        "gpu": {"name": torch.cuda.get_device_name(0), "rocm": torch.version.hip,
+                "torch": torch.__version__, "clocks": clocks},
         "cpu_baseline": None,
     }
     if extras:

@@ -378,10 +378,10 @@ int kv_vector_decode(const void* q, const void* k_c, const void* v_c, const int3
  * kv_timing_enable(1) clears earlier records and makes every kernel the
  * library launches afterwards carry a start/stop hipEvent pair that its
  * dispatch stamps at kernel start and end, on that launch's own stream;
- * kv_timing_enable(0) stops recording.  kv_timing_read
- * waits for the recorded events and writes up to max_entries per-kernel
- * totals (host array, caller-owned), returning the number of distinct
- * kernels (or a negative kv_status).  kv_timing_only(name) restricts the
+ * kv_timing_enable(0) stops recording.  kv_timing_read waits for the
+ * recorded events and writes up to max_entries per-kernel totals, each
+ * with its last launch's shape (host array, caller-owned), returning the
+ * number of distinct kernels (or a negative kv_status).  kv_timing_only(name) restricts the
  * recording to launches of that kernel name (one of "score_rowstats",
  * "score_fold" (launched only when row LSEs are requested or heads are so
  * long, and so few, that pass 1 cuts a head into more than 16 pieces),
@@ -398,6 +398,8 @@ typedef struct kv_kernel_time {
   char name[40];
   int64_t launches;
   double total_ms;
+  int32_t grid;    /* workgroups of the kernel's last recorded launch */
+  int32_t block;   /* threads per workgroup of that launch */
 } kv_kernel_time;
 int kv_timing_enable(int on);
 int kv_timing_only(const char* name);

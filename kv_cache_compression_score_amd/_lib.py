@@ -23,7 +23,8 @@ class KvBudget(ctypes.Structure):
 
 
 class KvKernelTime(ctypes.Structure):
-    _fields_ = [("name", ctypes.c_char * 40), ("launches", c_int64), ("total_ms", ctypes.c_double)]
+    _fields_ = [("name", ctypes.c_char * 40), ("launches", c_int64), ("total_ms", ctypes.c_double),
+                ("grid", ctypes.c_int32), ("block", ctypes.c_int32)]
 
 
 # name -> (restype, argtypes)

@@ -38,7 +38,7 @@ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // timing_events hands out a start/stop event pair for one launch, and
 // timing_done files the pair under `name`.
 bool timing_events(const char* name, hipEvent_t* start, hipEvent_t* stop);
-void timing_done(const char* name, hipEvent_t start, hipEvent_t stop);
+void timing_done(const char* name, hipEvent_t start, hipEvent_t stop, dim3 grid, dim3 block);
 
 // kernel<<<grid, block, shmem, st>>>(args...).  While timing is on for
 // `name`, the launch carries an event pair that the dispatch itself stamps at
@@ -50,7 +50,7 @@ inline void launch(const char* name, K kernel, dim3 grid, dim3 block, uint32_t s
   hipEvent_t e0, e1;
   if (timing_events(name, &e0, &e1)) {
     hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, e0, e1, 0, args...);
-    timing_done(name, e0, e1);
+    timing_done(name, e0, e1, grid, block);
   } else {
     hipLaunchKernelGGL(kernel, grid, block, shmem, st, args...);
   }

@@ -1272,7 +1272,7 @@ void select_parts(const SelectArgs& s, int P, void* ws, hipStream_t st) {
   hipLaunchKernelGGL(select_part_kernel<3>, grid, block, 0, st, pa);
   if (timed) {
     hipExtLaunchKernelGGL(select_part_kernel<4>, grid, block, 0, st, nullptr, e1, 0, pa);
-    timing_done("select", e0, e1);
+    timing_done("select", e0, e1, grid, block);   // five launches of this shape
   } else {
     hipLaunchKernelGGL(select_part_kernel<4>, grid, block, 0, st, pa);
   }

@@ -15,6 +15,7 @@ namespace {
 struct Record {
   const char* name;
   hipEvent_t start, stop;
+  int32_t grid, block;   // workgroups and threads per workgroup of the launch
 };
 
 std::mutex g_mu;
@@ -50,9 +51,10 @@ bool timing_events(const char* name, hipEvent_t* start, hipEvent_t* stop) {
   return true;
 }
 
-void timing_done(const char* name, hipEvent_t start, hipEvent_t stop) {
+void timing_done(const char* name, hipEvent_t start, hipEvent_t stop, dim3 grid, dim3 block) {
   std::lock_guard<std::mutex> lk(g_mu);
-  g_records.push_back(Record{name, start, stop});
+  g_records.push_back(Record{name, start, stop, (int32_t)(grid.x * grid.y * grid.z),
+                             (int32_t)(block.x * block.y * block.z)});
 }
 
 }  // namespace kvcc
@@ -96,6 +98,8 @@ extern "C" int kv_timing_read(kv_kernel_time* out, int max_entries) {
     }
     acc[i].launches += 1;
     acc[i].total_ms += ms;
+    acc[i].grid = r.grid;     // the last launch's shape
+    acc[i].block = r.block;
   }
   const int n = (int)acc.size();
   for (int i = 0; i < n && i < max_entries; ++i) out[i] = acc[i];

@@ -1,7 +1,9 @@
 """One score -> select -> compact -> decode step captured in a HIP graph.
 
-The library allocates nothing and records no memset, so the four calls can
-be captured with static buffers.  Every replay, with eager steps and
+The library allocates nothing and records no memset, so the step's calls
+(kv_score, kv_select, kv_compact, kv_decode_attn; or the two fused calls
+kv_score_select and kv_compact_decode, the step the benchmark times and
+replays) can be captured with static buffers.  Every replay, with eager steps and
 synchronisations in between, must reproduce the eager step bit for bit
 (every kernel sums in a fixed order, so repeated runs are bit-identical).
 """
@@ -20,8 +22,9 @@ from gpu_helpers import dev, log
 pytestmark = pytest.mark.gpu
 
 
-def static_step(cfg, lay):
-    """Inputs, outputs and workspaces allocated once; returns (step, buffers)."""
+def static_step(cfg, lay, fused=False):
+    """Inputs, outputs and workspaces allocated once; returns (step, buffers).
+    fused: kv_score_select + kv_compact_decode instead of the four calls."""
     q, k, v, c, qd = dev(lay.q_win), dev(lay.k), dev(lay.v), dev(lay.ctx_len), dev(lay.q_dec[0])
     B, Hkv, N, d = lay.k.shape
     if cfg.budget_mode == wl.BUDGET_MASS:
@@ -34,7 +37,8 @@ def static_step(cfg, lay):
     f32, i32 = torch.float32, torch.int32
     buf = dict(
         scores=torch.empty(B, Hkv, N, device="cuda", dtype=f32),
-        ws_s=torch.zeros(api.kv_score_workspace_size(B, cfg.Hq, Hkv, N, cfg.W, d),
+        ws_s=torch.zeros((api.kv_score_select_workspace_size if fused else
+                          api.kv_score_workspace_size)(B, cfg.Hq, Hkv, N, cfg.W, d),
                          device="cuda", dtype=torch.uint8),
         idx=torch.empty(B, Hkv, N, device="cuda", dtype=i32),
         cnt=torch.empty(B * Hkv, device="cuda", dtype=i32),
@@ -47,6 +51,13 @@ def static_step(cfg, lay):
         ws_d=torch.zeros(api.kv_decode_workspace_size(B, cfg.Hq, Hkv, d, cap),
                          device="cuda", dtype=torch.uint8))
 
+    def fused_step():
+        api.kv_score_select(q, k, c, bud, scores=buf["scores"], kept_idx=buf["idx"],
+                            kept_count=buf["cnt"], workspace=buf["ws_s"])
+        api.kv_compact_decode(k, v, buf["idx"], buf["cnt"], cap, qd,
+                              out=(buf["k_c"], buf["v_c"], buf["pos"], buf["off"]),
+                              attn_out=buf["out"], lse=buf["lse"], workspace=buf["ws_d"])
+
     def step():
         api.kv_score(q, k, c, scores=buf["scores"], workspace=buf["ws_s"])
         api.kv_select(buf["scores"], c, bud, kept_idx=buf["idx"], kept_count=buf["cnt"])
@@ -54,7 +65,7 @@ def static_step(cfg, lay):
                        out=(buf["k_c"], buf["v_c"], buf["pos"], buf["off"]))
         api.kv_decode_attn(qd, buf["k_c"], buf["v_c"], buf["off"], Hkv, out=buf["out"],
                            lse=buf["lse"], workspace=buf["ws_d"])
-    return step, buf
+    return (fused_step if fused else step), buf
 
 
 def snapshot(buf, ctx):
@@ -81,12 +92,15 @@ def assert_same(a, b):
             assert torch.equal(a[key], b[key]), key
 
 
-@pytest.mark.parametrize("name", ["tiny", "llama8b_layer", "ragged_adaptive"])
-def test_graph_replay_matches_eager(name):
+@pytest.mark.parametrize("name,fused", [("tiny", False), ("llama8b_layer", False),
+                                        ("ragged_adaptive", False), ("tiny", True),
+                                        ("llama8b_layer", True), ("ragged_adaptive", True),
+                                        ("needle32k", True)])
+def test_graph_replay_matches_eager(name, fused):
     cfg = wl.CONFIGS[name]
-    log(f"graph capture: {name}")
+    log(f"graph capture: {name} ({'fused calls' if fused else 'four calls'})")
     lay = wl.make_layer(cfg)
-    step, buf = static_step(cfg, lay)
+    step, buf = static_step(cfg, lay, fused)
     step()
     torch.cuda.synchronize()
     ref = snapshot(buf, lay.ctx_len)

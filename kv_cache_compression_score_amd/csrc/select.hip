@@ -449,23 +449,24 @@ __device__ __forceinline__ int count_budget(const kv_budget& bu, int head, int n
 
 constexpr int EPI = LDS_KEYS / NWV / (4 * WAVE);   // register steps per lane (seg <= EPI * 256)
 
-// One digit's histogram over a wave's register-held keys (segment [s0, s1),
-// key u of step j at token s0 + 256 j + 4 lane + u): keys whose bits from
-// `hi` up equal `prefix` add one to bin (key >> lo) of the bits below `hi`.
-// A step in which no lane has a matching key costs two VALU instructions
-// per key and a branch (the lower digits match a few keys of a head); a
-// wave whose sampled keys crowd into one bin aggregates its adds instead.
-__device__ __forceinline__ void count_regs(const uint4 (&ek)[EPI], int s0, int s1, int hi, int lo,
-                                           uint32_t prefix, Smem& sm) {
-  const int lane = threadIdx.x & (WAVE - 1);
+// One digit's histogram over a wave's register-held keys, each lane holding
+// a run of R = 4 * JR consecutive tokens (key 4 j + u of the lane is token
+// tl + 4 j + u, valid below s1; `full`: every key of the wave is valid):
+// keys whose bits from `hi` up equal `prefix` add one to bin (key >> lo) of
+// the bits below `hi`.  A step in which no lane has a matching key costs two
+// VALU instructions per key and a branch (the lower digits match a few keys
+// of a head); a wave whose sampled keys crowd into one bin aggregates its
+// adds instead.
+__device__ __forceinline__ void count_runs(const uint4 (&ek)[EPI], int tl, int s1, int JR, bool full,
+                                           int hi, int lo, uint32_t prefix, Smem& sm) {
   const uint32_t bmask = (1u << (hi - lo)) - 1u;
-  const bool in0 = s0 + 4 * lane < s1 && (ek[0].x >> hi) == prefix;
+  const bool in0 = tl < s1 && (ek[0].x >> hi) == prefix;
   if (crowded(in0, (int)((ek[0].x >> lo) & bmask))) {
     HistAcc<false> acc;
 #pragma unroll
     for (int j = 0; j < EPI; ++j) {
-      if (s0 + j * 4 * WAVE >= s1) break;   // uniform
-      const int t = s0 + j * 4 * WAVE + 4 * lane;
+      if (j >= JR) break;   // uniform
+      const int t = tl + 4 * j;
       const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -474,8 +475,8 @@ __device__ __forceinline__ void count_regs(const uint4 (&ek)[EPI], int s0, int s
     acc.flush(sm);
     return;
   }
-  // one step of 4 keys per lane; a full step (all 256 keys in the segment)
-  // takes its own copy, whose masks are plain compares
+  // one step of 4 keys per lane; a full wave's steps take their own copy,
+  // whose masks are plain compares
   auto step = [&](const uint32_t (&kk)[4], bool m0, bool m1, bool m2, bool m3) {
     if ((__ballot(m0) | __ballot(m1) | __ballot(m2) | __ballot(m3)) == 0) return;   // uniform
     if (m0) atomicAdd(&sm.hist[(kk[0] >> lo) & bmask], 1u);
@@ -485,18 +486,81 @@ __device__ __forceinline__ void count_regs(const uint4 (&ek)[EPI], int s0, int s
   };
 #pragma unroll
   for (int j = 0; j < EPI; ++j) {
-    const int base = s0 + j * 4 * WAVE;
-    if (base >= s1) break;   // uniform
+    if (j >= JR) break;   // uniform
     const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
-    if (base + 4 * WAVE <= s1) {
+    if (full) {
       step(kk, (kk[0] >> hi) == prefix, (kk[1] >> hi) == prefix, (kk[2] >> hi) == prefix,
            (kk[3] >> hi) == prefix);
     } else {
-      const int left = s1 - base - 4 * lane;   // this lane's keys left in the segment
+      const int left = s1 - tl - 4 * j;   // this lane's keys left in the segment
       step(kk, left > 0 && (kk[0] >> hi) == prefix, left > 1 && (kk[1] >> hi) == prefix,
            left > 2 && (kk[2] >> hi) == prefix, left > 3 && (kk[3] >> hi) == prefix);
     }
   }
+}
+
+// Emit from register-held runs (the layout of count_runs; the wave's
+// segment starts at s0): keeps key > T, and the first `quota` keys equal to
+// T (eq_total of them in the head), ascending.  Each lane gathers its kept
+// keys into a bit mask (bit b: token tl + b), a wave scan of the masks'
+// popcounts places each lane's tokens in the wave's stretch of keys_lds
+// (free LDS of at least n words), and the wave copies its stretch out
+// contiguously at the offset the earlier waves leave.  Ties: the equal keys
+// before each lane (a wave scan plus the earlier waves' counts) decide how
+// many of the lane's equal keys, lowest tokens first, are kept.
+__device__ __forceinline__ void emit_runs(const uint4 (&ek)[EPI], int s0, int tl, int s1, int JR,
+                                          bool full, int n, uint32_t T, uint32_t quota,
+                                          uint32_t eq_total, uint32_t* keys_lds, Smem& sm,
+                                          int32_t* dst) {
+  const int lane = threadIdx.x & (WAVE - 1), wave = wave_index();
+  const bool all_ties = quota >= eq_total;   // then the keep rule is key >= T
+  uint32_t keep = 0u, eqm = 0u;
+#pragma unroll
+  for (int j = 0; j < EPI; ++j) {
+    if (j >= JR) break;   // uniform
+    const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int b = 4 * j + u;
+      const bool ok = full || tl + b < s1;
+      if (all_ties) {
+        keep |= (ok && kk[u] >= T ? 1u : 0u) << b;
+      } else {
+        keep |= (ok && kk[u] > T ? 1u : 0u) << b;
+        eqm |= (ok && kk[u] == T ? 1u : 0u) << b;
+      }
+    }
+  }
+  if (!all_ties) {
+    const uint32_t ne = (uint32_t)__popc(eqm);
+    const uint32_t incl = wave_scan_u32(ne, 0u, OpAdd());
+    if (lane == WAVE - 1) sm.w_eq[wave] = incl;
+    __syncthreads();
+    uint32_t before = incl - ne;
+    for (int w = 0; w < wave; ++w) before += sm.w_eq[w];
+    // the lane keeps min(max(quota - before, 0), ne) of its equal keys,
+    // worked out in signed 64-bit arithmetic (no unsigned wrap to reason about)
+    const int64_t avail = (int64_t)quota - (int64_t)before;
+    const uint32_t m = (uint32_t)(avail <= 0 ? 0 : (avail < (int64_t)ne ? avail : (int64_t)ne));
+    uint32_t rest = eqm;
+    for (uint32_t i = 0; i < m; ++i) rest &= rest - 1u;   // drop the lowest m
+    keep |= eqm ^ rest;
+  }
+  const uint32_t nk = (uint32_t)__popc(keep);
+  const uint32_t incl = wave_scan_u32(nk, 0u, OpAdd());
+  const uint32_t wave_nk = last_lane(incl);
+  if (lane == 0) sm.w_gt[wave] = wave_nk;
+  uint32_t* stage = keys_lds + s0;
+  uint32_t at = incl - nk;
+  while (keep) {
+    stage[at++] = (uint32_t)(tl + __builtin_ctz(keep));
+    keep &= keep - 1u;
+  }
+  __syncthreads();
+  uint32_t slot = 0;
+  for (int w = 0; w < wave; ++w) slot += sm.w_gt[w];
+  for (uint32_t i = lane; i < wave_nk; i += WAVE)
+    if (slot + i < (uint32_t)n) dst[slot + i] = (int32_t)stage[i];
 }
 
 // Emit of the kept indices from keys held in registers: wave w holds the
@@ -925,11 +989,13 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
 // head:
 //   1. the histogram gives the top digit b1 of the k-th key and the count of
 //      keys above it (the same scan as resolve_digit);
-//   2. each wave loads its segment's scores into registers as keys (the
-//      loads are issued before the scan above and land during it);
+//   2. each wave loads its segment's scores into registers as keys, each
+//      lane a run of consecutive tokens (the loads are issued before the
+//      scan above and land during it);
 //   3. the second and third digits are counted straight from the registers
-//      (count_regs: only keys that carry the prefix found so far add);
-//   4. the emit runs from the registers, as select_kernel's does.
+//      (count_runs: only keys that carry the prefix found so far add);
+//   4. the emit runs from the registers (emit_runs: per-lane bit masks of
+//      the kept tokens, placed by one wave scan).
 // The k-th key T and the tie quota are those of select_kernel, so the kept
 // indices are the same.
 template <bool VEC>   // VEC: 16-byte aligned scores with N_max a multiple of 4
@@ -952,10 +1018,18 @@ __global__ __launch_bounds__(NT) void select_hist_kernel(SelectArgs a, const uin
   const uint32_t h0 = hh[tid], h1 = hh[tid + NT];
   const int seg = ((n + NWV - 1) / NWV + 4 * WAVE - 1) / (4 * WAVE) * (4 * WAVE);
   const int s0 = wave * seg, s1 = min(s0 + seg, n);
+  // Lane l ends up holding the run of R = seg / 64 consecutive tokens from
+  // tl = s0 + l R (R a multiple of 4, at most 4 EPI): key 4 j + u is token
+  // tl + 4 j + u.  The scores are loaded coalesced (step j of lane l: the 16
+  // bytes of tokens s0 + 256 j + 4 l) and turned into runs through the
+  // wave's own stretch of keys_lds (below).
+  const int JR = seg / (4 * WAVE);   // 16-byte steps per lane (uniform)
+  const int tl = s0 + lane * (4 * JR);
+  const bool full = s0 + seg <= n;   // every key of the wave is in the head
   // this wave's segment, loaded while the histogram is scanned: whole 16-byte
   // loads clamped onto the head's row (N_max - 4 is aligned) when the row
   // allows, else scalar loads clamped onto the head; tokens at or past n are
-  // masked by their index
+  // masked by their index, and steps past the segment go unused
   uint4 v4[VEC ? EPI : 1];
   float v1[VEC ? 1 : EPI][4];
   if constexpr (VEC) {
@@ -973,26 +1047,42 @@ __global__ __launch_bounds__(NT) void select_hist_kernel(SelectArgs a, const uin
   resolve_digit<false>(sm, NBINS, (unsigned long long)k);   // leaves sm.hist cleared
   // keys as the score pass histogrammed them (score_key: scores written by
   // the score pass are never negative, so these order them as to_key does)
+  // Coalesced steps to runs through the wave's stretch of keys_lds (only
+  // this wave touches it, so no barrier): 16-byte chunk c of the stretch
+  // (tokens s0 + 4 c .. + 3) sits at slot c ^ ((c >> 3) & 7), so that the
+  // chunk writes (lane l: c = 64 j + l) and the run reads (lane l: c = JR l
+  // + j) of eight consecutive lanes fall on eight different 16-byte bank
+  // groups.
   uint4 ek[EPI];
+  {
+    uint4* stretch = reinterpret_cast<uint4*>(keys_lds + s0);
+    auto slot = [](int c) { return c ^ ((c >> 3) & 7); };
 #pragma unroll
-  for (int j = 0; j < EPI; ++j) {
-    if constexpr (VEC)
-      ek[j] = make_uint4(score_key(__uint_as_float(v4[j].x)), score_key(__uint_as_float(v4[j].y)),
+    for (int j = 0; j < EPI; ++j) {
+      if (j * 4 * WAVE >= seg) break;   // uniform
+      uint4 key;
+      if constexpr (VEC)
+        key = make_uint4(score_key(__uint_as_float(v4[j].x)), score_key(__uint_as_float(v4[j].y)),
                          score_key(__uint_as_float(v4[j].z)), score_key(__uint_as_float(v4[j].w)));
-    else
-      ek[j] = make_uint4(score_key(v1[j][0]), score_key(v1[j][1]), score_key(v1[j][2]),
+      else
+        key = make_uint4(score_key(v1[j][0]), score_key(v1[j][1]), score_key(v1[j][2]),
                          score_key(v1[j][3]));
+      stretch[slot(j * WAVE + lane)] = key;
+    }
+#pragma unroll
+    for (int j = 0; j < EPI; ++j)   // steps past the run (j >= JR, uniform) are never read
+      ek[j] = j < JR ? stretch[slot(lane * JR + j)] : make_uint4(0u, 0u, 0u, 0u);
   }
   // The lower digits count straight from the registers: a key takes part
   // when its bits above the digit equal the prefix found so far.
   unsigned long long rem = (unsigned long long)(k - sm.cnt_above);
   uint32_t prefix = sm.bin;   // the top DIGIT bits of the k-th largest key
-  count_regs(ek, s0, s1, 32 - DIGIT, 32 - 2 * DIGIT, prefix, sm);
+  count_runs(ek, tl, s1, JR, full, 32 - DIGIT, 32 - 2 * DIGIT, prefix, sm);
   __syncthreads();
   resolve_digit<false>(sm, NBINS, rem);
   rem -= sm.cnt_above;
   prefix = prefix << DIGIT | sm.bin;   // the top 2 * DIGIT bits
-  count_regs(ek, s0, s1, 32 - 2 * DIGIT, 0, prefix, sm);
+  count_runs(ek, tl, s1, JR, full, 32 - 2 * DIGIT, 0, prefix, sm);
   __syncthreads();
   resolve_digit<false>(sm, 1 << (32 - 2 * DIGIT), rem);
   rem -= sm.cnt_above;
@@ -1001,8 +1091,8 @@ __global__ __launch_bounds__(NT) void select_hist_kernel(SelectArgs a, const uin
   const uint32_t eq_total = sm.bin_cnt;                    // keys equal to T in the head
   if (tid == 0) a.kept_count[head] = k;
   // keys_lds serves only as the emit's staging area here (no barrier needed)
-  emit_regs<false>(ek, s0, s1, n, T, quota, eq_total, keys_lds, sm,
-                   a.kept_idx + (size_t)head * a.N_max);
+  emit_runs(ek, s0, tl, s1, JR, full, n, T, quota, eq_total, keys_lds, sm,
+            a.kept_idx + (size_t)head * a.N_max);
 }
 
 // ---------------------------------------------------------------------------

@@ -696,7 +696,7 @@ class LongContext:
         self.budget = budget_of(cfg)
         self.cap = capacity_of(cfg, B, Hkv, N)
         self.scores = torch.empty(B, Hkv, N, device=DEV, dtype=torch.float32)
-        self.ws_s = torch.zeros(api.kv_score_workspace_size(B, cfg.Hq, Hkv, N, cfg.W, D),
+        self.ws_s = torch.zeros(api.kv_score_select_workspace_size(B, cfg.Hq, Hkv, N, cfg.W, D),
                                 device=DEV, dtype=torch.uint8)
         self.idx = torch.empty(B, Hkv, N, device=DEV, dtype=torch.int32)
         self.cnt = torch.empty(B * Hkv, device=DEV, dtype=torch.int32)
@@ -713,9 +713,8 @@ class LongContext:
 
     def compress(self):
         for lay, cache in zip(self.lays, self.caches):
-            api.kv_score(lay.q_win, lay.k, None, scores=self.scores, workspace=self.ws_s)
-            api.kv_select(self.scores, None, self.budget, kept_idx=self.idx,
-                          kept_count=self.cnt)
+            api.kv_score_select(lay.q_win, lay.k, None, self.budget, scores=self.scores,
+                                kept_idx=self.idx, kept_count=self.cnt, workspace=self.ws_s)
             api.kv_compact(lay.k, lay.v, self.idx, self.cnt, self.cap, out=cache)
 
     def decode(self, steps: int):

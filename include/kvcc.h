@@ -190,10 +190,11 @@ int kv_select(const float* scores, const int32_t* ctx_len,
  * attention-based importance of "A Simple Plug-in for Improving
  * Eviction-Based KV Cache Compression", section "Enonce du Probleme"), then
  * the budgeted per-head selection that evicts the low scorers.  Under a k or
- * kept-fraction budget with no protected tokens and N_max <= 32768 the
- * second score sweep also counts each head's scores by their top 11 key
- * bits, so the selection starts from that histogram and resolves the lower
- * key bits from the scores it holds in registers.  The scores of finite
+ * kept-fraction budget with no protected tokens the second score sweep also
+ * counts each head's scores by their top 11 key bits, so the selection
+ * starts from that histogram: for N_max <= 32768 one workgroup per head
+ * resolves the lower key bits from the scores it holds in registers; longer
+ * heads skip the first of the part path's launches.  The scores of finite
  * inputs are sums of exponentials (never negative), on which both orders
  * agree; NaN inputs are outside the contract, as for kv_select.
  *

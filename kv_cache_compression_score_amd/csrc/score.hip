@@ -1037,13 +1037,16 @@ extern "C" int kv_score_select(const void* q_win, const void* k, const int32_t* 
   ScoreArgs a = two_pass_args(q_win, k, ctx_len, scores, row_lse, B, Hq, Hkv, N_max, W, d, causal,
                               scale, p, ws);
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + q.off_hist);
-  const bool fast = select_hist_eligible(*budget, N_max);
-  if (fast) a.hist = hist;
+  // Count budgets without protected tokens start from the histogram of each
+  // head's top key digits that score pass 2 counts (one workgroup per head
+  // up to 32768 tokens, the part path's last four launches above).
+  const bool with_hist = select_hist_budget(*budget);
+  if (with_hist) a.hist = hist;
   launch_score_any(a, dtype, d, p.NW, st);
-  if (fast)
+  if (with_hist && select_hist_eligible(*budget, N_max))
     select_hist_launch(scores, ctx_len, hist, B, Hkv, N_max, *budget, kept_idx, kept_count, st);
   else if (!select_parts_launch(scores, ctx_len, B, Hkv, N_max, *budget, kept_idx, kept_count,
-                                ws + q.off_sel, q.sel_bytes, st))
+                                ws + q.off_sel, q.sel_bytes, st, with_hist ? hist : nullptr))
     select_launch(scores, ctx_len, nullptr, B, Hkv, N_max, *budget, false, kept_idx, kept_count,
                   st, "select");
   return launch_status();

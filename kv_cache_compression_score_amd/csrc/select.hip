@@ -1101,7 +1101,9 @@ __global__ __launch_bounds__(NT) void select_hist_kernel(SelectArgs a, const uin
 // head is cut into parts of PT tokens, one workgroup each, and the descent
 // runs as five launches over the (part, head) grid with fixed digits of 11,
 // 11 and 10 key bits:
-//   0: each part histograms the top digit of its keys and counts keys >= tau;
+//   0: each part histograms the top digit of its keys and counts keys >= tau
+//      (skipped when the score pass has counted the head's top digits:
+//      launch 1 then starts from that histogram);
 //   1, 2: every workgroup of a head sums the parts' histograms of the last
 //         digit, resolves it exactly as resolve_digit does for one workgroup
 //         (so all of them agree), and histograms the next digit of its part;
@@ -1122,6 +1124,8 @@ struct PartState {
 
 struct PartArgs {
   SelectArgs s;
+  const uint32_t* head_hist;   // [H][NBINS] top-digit histogram of each head's keys from the
+                               // score pass (count budgets, no protected tokens), or null
   int P;                 // parts per head
   uint32_t* hist;        // [H][3][P][NBINS]
   uint32_t* pstat;       // [H][P][4]: count >= tau, count > T, count == T
@@ -1221,13 +1225,20 @@ __global__ __launch_bounds__(NT) void select_part_kernel(PartArgs pa) {
   }
 
   if (PHASE == 1) {
-    uint32_t cnt = 0;
-    for (int q = 0; q < P; ++q) cnt += pstat_h[q * 4 + 0];
+    uint32_t cnt = 0;   // keys >= tau (threshold budgets; launch 0 counted them)
+    if (!pa.head_hist)
+      for (int q = 0; q < P; ++q) cnt += pstat_h[q * 4 + 0];
     int lo, hi;
     budget_clamps(bu, n, &lo, &hi);
     int k = count_budget(bu, head, n, cnt, lo, hi);
     k = min(max(k, n_prot), n);
-    sum_parts(0, NBINS);
+    if (pa.head_hist) {   // the head's top digits as the score pass counted them
+      const uint32_t* hh = pa.head_hist + (size_t)head * NBINS;
+      for (int i = tid; i < NBINS; i += NT) sm.hist[i] = hh[i];
+      __syncthreads();
+    } else {
+      sum_parts(0, NBINS);
+    }
     resolve_digit<false>(sm, NBINS, (unsigned long long)k);
     const uint32_t bin = sm.bin;
     const uint32_t rem = (uint32_t)k - sm.cnt_above;
@@ -1342,9 +1353,11 @@ __global__ __launch_bounds__(NT) void select_part_kernel(PartArgs pa) {
 
 // The five launches of the part path; per-kernel timing sees them as one
 // "select" (start stamped by the first dispatch, stop by the last).
-void select_parts(const SelectArgs& s, int P, void* ws, hipStream_t st) {
+void select_parts(const SelectArgs& s, int P, void* ws, const uint32_t* head_hist,
+                  hipStream_t st) {
   PartArgs pa;
   pa.s = s;
+  pa.head_hist = head_hist;
   pa.P = P;
   const int H = s.B * s.Hkv;
   pa.hist = static_cast<uint32_t*>(ws);
@@ -1353,16 +1366,21 @@ void select_parts(const SelectArgs& s, int P, void* ws, hipStream_t st) {
   const dim3 grid(P, H), block(NT);
   hipEvent_t e0, e1;
   const bool timed = timing_events("select", &e0, &e1);
-  if (timed)
-    hipExtLaunchKernelGGL(select_part_kernel<0>, grid, block, 0, st, e0, nullptr, 0, pa);
+  if (!head_hist) {
+    if (timed)
+      hipExtLaunchKernelGGL(select_part_kernel<0>, grid, block, 0, st, e0, nullptr, 0, pa);
+    else
+      hipLaunchKernelGGL(select_part_kernel<0>, grid, block, 0, st, pa);
+  }
+  if (timed && head_hist)
+    hipExtLaunchKernelGGL(select_part_kernel<1>, grid, block, 0, st, e0, nullptr, 0, pa);
   else
-    hipLaunchKernelGGL(select_part_kernel<0>, grid, block, 0, st, pa);
-  hipLaunchKernelGGL(select_part_kernel<1>, grid, block, 0, st, pa);
+    hipLaunchKernelGGL(select_part_kernel<1>, grid, block, 0, st, pa);
   hipLaunchKernelGGL(select_part_kernel<2>, grid, block, 0, st, pa);
   hipLaunchKernelGGL(select_part_kernel<3>, grid, block, 0, st, pa);
   if (timed) {
     hipExtLaunchKernelGGL(select_part_kernel<4>, grid, block, 0, st, nullptr, e1, 0, pa);
-    timing_done("select", e0, e1, grid, block);   // five launches of this shape
+    timing_done("select", e0, e1, grid, block);   // four or five launches of this shape
   } else {
     hipLaunchKernelGGL(select_part_kernel<4>, grid, block, 0, st, pa);
   }
@@ -1421,7 +1439,8 @@ size_t kvcc::select_part_workspace(int B, int Hkv, int N_max) {
 
 bool kvcc::select_parts_launch(const float* scores, const int32_t* ctx, int B, int Hkv, int N_max,
                                const kv_budget& bud, int32_t* kept_idx, int32_t* kept_count,
-                               void* workspace, size_t workspace_bytes, hipStream_t st) {
+                               void* workspace, size_t workspace_bytes, hipStream_t st,
+                               const uint32_t* head_hist) {
   const int P = ceil_div(N_max, PT);
   if (N_max <= LDS_KEYS || bud.mode == KV_BUDGET_MASS || !workspace ||
       workspace_bytes < part_workspace(B * Hkv, P))
@@ -1430,13 +1449,17 @@ bool kvcc::select_parts_launch(const float* scores, const int32_t* ctx, int B, i
   a.scores = scores; a.ctx = ctx; a.n_head = nullptr; a.B = B; a.Hkv = Hkv; a.N_max = N_max;
   a.k_zero_ok = 0;
   a.bud = bud; a.kept_idx = kept_idx; a.kept_count = kept_count;
-  select_parts(a, P, workspace, st);
+  select_parts(a, P, workspace, head_hist, st);
   return true;
 }
 
+bool kvcc::select_hist_budget(const kv_budget& bud) {
+  return (bud.mode == KV_BUDGET_K || bud.mode == KV_BUDGET_RATIO) && bud.n_sink == 0 &&
+         bud.n_recent == 0;
+}
+
 bool kvcc::select_hist_eligible(const kv_budget& bud, int N_max) {
-  return N_max <= LDS_KEYS && (bud.mode == KV_BUDGET_K || bud.mode == KV_BUDGET_RATIO) &&
-         bud.n_sink == 0 && bud.n_recent == 0;
+  return N_max <= LDS_KEYS && select_hist_budget(bud);
 }
 
 void kvcc::select_hist_launch(const float* scores, const int32_t* ctx, const uint32_t* hist, int B,

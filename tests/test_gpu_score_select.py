@@ -98,9 +98,24 @@ def test_fallback_budgets(budget):
     both(lay, budget)
 
 
-def test_heads_above_32k_fall_back_to_the_part_path():
+def test_heads_above_32k_take_the_part_path_from_the_histogram():
+    # above 32768 tokens the part path starts from the score pass's
+    # histogram (its first launch skipped) under k and kept-fraction budgets
     lay = wl.random_case(12, B=1, Hq=8, Hkv=2, d=128, N_max=40000, W=16)
     both(lay, RATIO(0.1))
+    # ragged lengths (one head below 32K, one not a multiple of 4), N_max
+    # odd (scalar loads), half of every head tied, per-head k and fractions
+    log("score_select: part path, ragged, tied")
+    lay = wl.random_case(13, B=2, Hq=8, Hkv=2, d=128, N_max=70001, W=16, ctx=[70001, 20003])
+    lay.k[:, :, 1::2] = lay.k[:, :, :1]
+    for b, n in enumerate([70001, 20003]):
+        lay.k[b, :, n:] = 0
+    for r in (0.02, 0.3, 0.5, 0.95, 1.0):
+        both(lay, RATIO(r))
+    ks = np.array([1, 35001, 70001, 0], dtype=np.int32)
+    both(lay, api.Budget(api.BUDGET_K, k=dev(torch.from_numpy(ks))))
+    rs = np.array([0.1, 0.6, 0.25, 0.0], dtype=np.float32)
+    both(lay, api.Budget(api.BUDGET_RATIO, ratio=dev(torch.from_numpy(rs))))
 
 
 @pytest.mark.parametrize("name", ["needle32k", "llama8b_layer"])

@@ -1039,7 +1039,7 @@ extern "C" int kv_score_select(const void* q_win, const void* k, const int32_t* 
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + q.off_hist);
   // Count budgets without protected tokens start from the histogram of each
   // head's top key digits that score pass 2 counts (one workgroup per head
-  // up to 32768 tokens, the part path's last four launches above).
+  // up to 32768 tokens, the part path's last three launches above).
   const bool with_hist = select_hist_budget(*budget);
   if (with_hist) a.hist = hist;
   launch_score_any(a, dtype, d, p.NW, st);

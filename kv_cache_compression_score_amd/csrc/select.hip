@@ -449,6 +449,16 @@ __device__ __forceinline__ int count_budget(const kv_budget& bu, int head, int n
 
 constexpr int EPI = LDS_KEYS / NWV / (4 * WAVE);   // register steps per lane (seg <= EPI * 256)
 
+// Of e keys equal to T that follow `before` earlier ones (in token order),
+// how many are kept when the first `quota` of them are: min(max(quota -
+// before, 0), e), in signed 64-bit arithmetic (the unsigned form
+// `quota > before ? min(quota - before, e) : 0` once compiled to an
+// unguarded subtraction).
+__device__ __forceinline__ uint32_t ties_kept(uint32_t quota, uint32_t before, uint32_t e) {
+  const int64_t avail = (int64_t)quota - (int64_t)before;
+  return (uint32_t)(avail <= 0 ? 0 : (avail < (int64_t)e ? avail : (int64_t)e));
+}
+
 // One digit's histogram over a wave's register-held keys, each lane holding
 // a run of R = 4 * JR consecutive tokens (key 4 j + u of the lane is token
 // tl + 4 j + u, valid below s1; `full`: every key of the wave is valid):
@@ -538,10 +548,8 @@ __device__ __forceinline__ void emit_runs(const uint4 (&ek)[EPI], int s0, int tl
     __syncthreads();
     uint32_t before = incl - ne;
     for (int w = 0; w < wave; ++w) before += sm.w_eq[w];
-    // the lane keeps min(max(quota - before, 0), ne) of its equal keys,
-    // worked out in signed 64-bit arithmetic (no unsigned wrap to reason about)
-    const int64_t avail = (int64_t)quota - (int64_t)before;
-    const uint32_t m = (uint32_t)(avail <= 0 ? 0 : (avail < (int64_t)ne ? avail : (int64_t)ne));
+    // the lane keeps the first ties_kept(...) of its equal keys
+    const uint32_t m = ties_kept(quota, before, ne);
     uint32_t rest = eqm;
     for (uint32_t i = 0; i < m; ++i) rest &= rest - 1u;   // drop the lowest m
     keep |= eqm ^ rest;
@@ -1099,7 +1107,7 @@ __global__ __launch_bounds__(NT) void select_hist_kernel(SelectArgs a, const uin
 // Heads longer than LDS_KEYS tokens under a count budget.  One workgroup per
 // head would leave most CUs idle and re-read the head on every sweep, so the
 // head is cut into parts of PT tokens, one workgroup each, and the descent
-// runs as five launches over the (part, head) grid with fixed digits of 11,
+// runs as four launches over the (part, head) grid with fixed digits of 11,
 // 11 and 10 key bits:
 //   0: each part histograms the top digit of its keys and counts keys >= tau
 //      (skipped when the score pass has counted the head's top digits:
@@ -1108,9 +1116,10 @@ __global__ __launch_bounds__(NT) void select_hist_kernel(SelectArgs a, const uin
 //         digit, resolves it exactly as resolve_digit does for one workgroup
 //         (so all of them agree), and histograms the next digit of its part;
 //   3: the last digit gives T and the number of keys equal to T to keep;
-//         each part counts its keys above T and equal to T;
-//   4: each part writes its kept indices at the offset the earlier parts
-//      leave, ties going to the earliest tokens.
+//      each part writes its kept indices at the offset the earlier parts
+//      leave (their counts above T and equal to T come from what launch 2
+//      published: keys above the 22-bit prefix and the last digit's bins),
+//      ties going to the earliest tokens.
 // Part 0 of a head publishes the resolved state of each launch.
 constexpr int PT = 16384;             // tokens per part
 constexpr int PQ = PT / (4 * NT);     // float4 loads per thread (4)
@@ -1128,7 +1137,8 @@ struct PartArgs {
                                // score pass (count budgets, no protected tokens), or null
   int P;                 // parts per head
   uint32_t* hist;        // [H][3][P][NBINS]
-  uint32_t* pstat;       // [H][P][4]: count >= tau, count > T, count == T
+  uint32_t* pstat;       // [H][P][4]: count >= tau, (unused), (unused), count above the
+                         // 22-bit prefix
   PartState* state;      // [H][4]: after launches 0..3
 };
 
@@ -1160,7 +1170,7 @@ __global__ __launch_bounds__(NT) void select_part_kernel(PartArgs pa) {
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = wave_index();
   const int n = a.ctx ? min(max(a.ctx[b], 0), a.N_max) : a.N_max;
   if (n == 0) {
-    if (PHASE == 4 && part == 0 && tid == 0) a.kept_count[head] = 0;
+    if (PHASE == 3 && part == 0 && tid == 0) a.kept_count[head] = 0;
     return;
   }
   const kv_budget& bu = a.bud;
@@ -1191,11 +1201,28 @@ __global__ __launch_bounds__(NT) void select_part_kernel(PartArgs pa) {
   }
   auto valid = [&](int u, int e) { return t0 + 4 * (tid + u * NT) + e < t1; };
   auto sum_parts = [&](int d, int nb) {   // sm.hist = sum over parts of digit d
-    for (int i = tid; i < nb; i += NT) {
-      uint32_t c = 0;
-      for (int q = 0; q < P; ++q) c += hist_h[((size_t)d * P + q) * NBINS + i];
-      sm.hist[i] = c;
+    // bins tid and tid + NT (nb <= 2 NT), the parts' loads issued eight at a
+    // time before any is added
+    static_assert(NBINS <= 2 * NT, "two bins per thread");
+    const uint32_t* hd = hist_h + (size_t)d * P * NBINS;
+    const bool two = tid + NT < nb;
+    uint32_t c0 = 0, c1 = 0;
+    for (int q0 = 0; q0 < P; q0 += 8) {
+      uint32_t v0[8], v1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const size_t row = (size_t)min(q0 + u, P - 1) * NBINS;
+        v0[u] = hd[row + tid];
+        v1[u] = two ? hd[row + tid + NT] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        c0 += q0 + u < P ? v0[u] : 0u;
+        c1 += q0 + u < P ? v1[u] : 0u;
+      }
     }
+    if (tid < nb) sm.hist[tid] = c0;
+    if (two) sm.hist[tid + NT] = c1;
     __syncthreads();
   };
   auto publish = [&](int d, int nb) {     // this part's histogram of digit d
@@ -1259,45 +1286,52 @@ __global__ __launch_bounds__(NT) void select_part_kernel(PartArgs pa) {
     const uint32_t prefix = ps.prefix | (sm.bin << 10);
     const uint32_t rem = ps.rem - sm.cnt_above;
     if (part == 0 && tid == 0) st_h[2] = PartState{ps.k, prefix, rem, 0u};
+    uint32_t above = 0;   // keys above every key that carries the prefix
 #pragma unroll
     for (int u = 0; u < PQ; ++u)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+      for (int e = 0; e < 4; ++e) {
         if (valid(u, e) && (kk[u][e] >> 10) == (prefix >> 10)) atomicAdd(&sm.hist[kk[u][e] & 1023], 1u);
+        above += valid(u, e) && (kk[u][e] >> 10) > (prefix >> 10) ? 1u : 0u;
+      }
+    above = block_sum(above, sm);
+    if (tid == 0) pstat_h[part * 4 + 3] = above;
     publish(2, 1024);
     return;
   }
 
-  if (PHASE == 3) {
-    const PartState ps = st_h[2];
-    sum_parts(2, 1024);
-    resolve_digit<false>(sm, 1024, (unsigned long long)ps.rem);
-    const uint32_t T = ps.prefix | sm.bin;
-    const uint32_t quota = ps.rem - sm.cnt_above;
-    if (part == 0 && tid == 0) st_h[3] = PartState{ps.k, T, quota, 0u};
-    uint32_t gt = 0, eq = 0;
-#pragma unroll
-    for (int u = 0; u < PQ; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (valid(u, e)) { gt += kk[u][e] > T ? 1u : 0u; eq += kk[u][e] == T ? 1u : 0u; }
-    gt = block_sum(gt, sm);
-    eq = block_sum(eq, sm);
-    if (tid == 0) { pstat_h[part * 4 + 1] = gt; pstat_h[part * 4 + 2] = eq; }
-    return;
-  }
-
-  // PHASE 4: emit.  The part's tokens form PQ * NWV chunks of 4 * WAVE
-  // consecutive tokens, chunk (u, w) = lanes of wave w at load u, in token
-  // order u-major; each chunk's kept tokens go out in lane order.
-  const PartState ps = st_h[3];
-  const uint32_t T = ps.prefix, quota = ps.rem;
+  // PHASE 3: the last digit gives T and the number of keys equal to T to
+  // keep; then the emit.  Part q keeps its keys above T, g_q = (its keys
+  // above the 22-bit prefix, counted in launch 2) + (its digit-3 bins above
+  // T's), and its share of the ties, e_q = its bin of T: the earlier parts'
+  // (g_q, e_q) place this part's kept tokens, ties going to the earliest.
+  // The part's tokens form PQ * NWV chunks of 4 * WAVE consecutive tokens,
+  // chunk (u, w) = lanes of wave w at load u, in token order u-major; each
+  // chunk's kept tokens go out in lane order.
+  const PartState ps = st_h[2];
+  sum_parts(2, 1024);
+  resolve_digit<false>(sm, 1024, (unsigned long long)ps.rem);
+  const uint32_t b3 = sm.bin;
+  const uint32_t T = ps.prefix | b3;
+  const uint32_t quota = ps.rem - sm.cnt_above;
+  __shared__ uint32_t pg[NWV], pe[NWV];
   uint32_t off = 0, eqb = 0;   // kept by, and ties in, the earlier parts
-  for (int q = 0; q < part; ++q) {
-    const uint32_t g = pstat_h[q * 4 + 1], e = pstat_h[q * 4 + 2];
-    const uint32_t left = quota > eqb ? quota - eqb : 0u;
-    off += g + min(left, e);
-    eqb += e;
+  for (int q0 = 0; q0 < part; q0 += NWV) {   // sixteen earlier parts per round, one per wave
+    const int q = q0 + wave;
+    if (q < part) {
+      const uint32_t* h3 = hist_h + ((size_t)2 * P + q) * NBINS;
+      uint32_t g = 0;
+#pragma unroll
+      for (int i = lane; i < 1024; i += WAVE) g += i > (int)b3 ? h3[i] : 0u;
+      g = last_lane(wave_scan_u32(g, 0u, OpAdd()));
+      if (lane == 0) { pg[wave] = g + pstat_h[q * 4 + 3]; pe[wave] = h3[b3]; }
+    }
+    __syncthreads();
+    for (int w = 0; w < NWV && q0 + w < part; ++w) {   // in part order (uniform)
+      off += pg[w] + ties_kept(quota, eqb, pe[w]);
+      eqb += pe[w];
+    }
+    __syncthreads();
   }
   if (part == 0 && tid == 0) a.kept_count[head] = ps.k;
   __shared__ uint32_t cg[PQ][NWV], ce[PQ][NWV];
@@ -1312,17 +1346,24 @@ __global__ __launch_bounds__(NT) void select_part_kernel(PartArgs pa) {
     if (lane == 0) { cg[u][wave] = g; ce[u][wave] = e; }
   }
   __syncthreads();
+  // Exclusive prefix sums over the part's chunks in token order (chunk c =
+  // (c / NWV, c % NWV), one lane each): G_c keys above T and E_c keys equal
+  // to T before chunk c.  The ties kept before it are the first of the
+  // part's eqb + E_c, i.e. ties_kept(quota, eqb, E_c) of the part's own.
+  static_assert(PQ * NWV == WAVE, "one lane per chunk");
+  __shared__ uint32_t gx[PQ * NWV], ex[PQ * NWV];
+  if (wave == 0) {
+    const uint32_t g = cg[lane / NWV][lane % NWV], e = ce[lane / NWV][lane % NWV];
+    gx[lane] = wave_scan_u32(g, 0u, OpAdd()) - g;
+    ex[lane] = wave_scan_u32(e, 0u, OpAdd()) - e;
+  }
+  __syncthreads();
   int32_t* dst = a.kept_idx + (size_t)head * a.N_max;
 #pragma unroll
   for (int u = 0; u < PQ; ++u) {
     // slot and tie rank at the start of chunk (u, wave)
-    uint32_t slot = off, r = eqb;
-    for (int c = 0; c < u * NWV + wave; ++c) {
-      const uint32_t g = cg[c / NWV][c % NWV], e = ce[c / NWV][c % NWV];
-      const uint32_t left = quota > r ? quota - r : 0u;
-      slot += g + min(left, e);
-      r += e;
-    }
+    const int c = u * NWV + wave;
+    uint32_t slot = off + gx[c] + ties_kept(quota, eqb, ex[c]), r = eqb + ex[c];
     bool is_gt[4], is_eq[4], keep[4];
     uint64_t be[4], bk[4];
 #pragma unroll
@@ -1351,8 +1392,9 @@ __global__ __launch_bounds__(NT) void select_part_kernel(PartArgs pa) {
   }
 }
 
-// The five launches of the part path; per-kernel timing sees them as one
-// "select" (start stamped by the first dispatch, stop by the last).
+// The launches of the part path (four, or three when the score pass gave the
+// top-digit histogram); per-kernel timing sees them as one "select" (start
+// stamped by the first dispatch, stop by the last).
 void select_parts(const SelectArgs& s, int P, void* ws, const uint32_t* head_hist,
                   hipStream_t st) {
   PartArgs pa;
@@ -1377,12 +1419,11 @@ void select_parts(const SelectArgs& s, int P, void* ws, const uint32_t* head_his
   else
     hipLaunchKernelGGL(select_part_kernel<1>, grid, block, 0, st, pa);
   hipLaunchKernelGGL(select_part_kernel<2>, grid, block, 0, st, pa);
-  hipLaunchKernelGGL(select_part_kernel<3>, grid, block, 0, st, pa);
   if (timed) {
-    hipExtLaunchKernelGGL(select_part_kernel<4>, grid, block, 0, st, nullptr, e1, 0, pa);
-    timing_done("select", e0, e1, grid, block);   // four or five launches of this shape
+    hipExtLaunchKernelGGL(select_part_kernel<3>, grid, block, 0, st, nullptr, e1, 0, pa);
+    timing_done("select", e0, e1, grid, block);   // three or four launches of this shape
   } else {
-    hipLaunchKernelGGL(select_part_kernel<4>, grid, block, 0, st, pa);
+    hipLaunchKernelGGL(select_part_kernel<3>, grid, block, 0, st, pa);
   }
 }
 

@@ -280,32 +280,48 @@ def graph_steps(step, steps: int) -> dict:
 
 
 def gpu_clocks(step):
-    """The GPU's clocks as amd-smi reports them (a child process, 30 s at
-    most) while `step` runs back to back, so the reading is taken under the
-    bench's own load; None values with the reason if the tool fails."""
+    """The GPU's clocks while `step` runs back to back (each tool a child
+    process, 30 s at most): rocm-smi's sclk / mclk, and amd-smi's per-XCD
+    figures as it reports them (on this part its `clk` field read 196 MHz,
+    below its own 500 MHz minimum, under a sustained matmul load while
+    rocm-smi read 1566 MHz, so rocm-smi's sclk is the reading to use)."""
     import subprocess
-    cmd = ["amd-smi", "metric", "--clock", "--json"]
+
+    def under_load(cmd):
+        try:
+            p = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+        except OSError as e:
+            return None, str(e)
+        t_end = time.perf_counter() + 30.0
+        while p.poll() is None and time.perf_counter() < t_end:
+            for _ in range(20):
+                step()
+            torch.cuda.synchronize()
+        if p.poll() is None:
+            p.kill()
+        out, err = p.communicate()
+        if p.returncode != 0:
+            return None, f"{cmd[0]} exit {p.returncode}: {err.strip()[:200]}"
+        try:
+            return json.loads(out), None
+        except ValueError:
+            return None, f"{cmd[0]}: no JSON"
+
+    res = {"sampled": "while the step ran back to back"}
+    rep, err = under_load(["rocm-smi", "--showclocks", "--json"])
+    if rep:
+        card = next(iter(rep.values()))
+        res["rocm_smi"] = {k.rstrip(":"): v for k, v in card.items() if "clock" in k}
+    else:
+        res["rocm_smi_error"] = err
+    rep, err = under_load(["amd-smi", "metric", "--clock", "--json"])
     try:
-        p = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
-    except OSError as e:
-        return {"tool": None, "error": str(e)}
-    t_end = time.perf_counter() + 30.0
-    while p.poll() is None and time.perf_counter() < t_end:
-        for _ in range(20):
-            step()
-        torch.cuda.synchronize()
-    if p.poll() is None:
-        p.kill()
-    out, err = p.communicate()
-    if p.returncode != 0:
-        return {"tool": "amd-smi", "error": f"exit {p.returncode}: {err.strip()[:200]}"}
-    try:
-        clk = json.loads(out)["gpu_data"][0]["clock"]
-        return {"tool": "amd-smi", "sampled": "while the step ran back to back",
-                "mhz": {k: v["clk"]["value"] for k, v in clk.items()
-                        if isinstance(v, dict) and isinstance(v.get("clk"), dict)}}
-    except (ValueError, KeyError, IndexError, TypeError):
-        return {"tool": "amd-smi", "report": out.strip()[:2000]}
+        clk = rep["gpu_data"][0]["clock"]
+        res["amd_smi_clk_mhz"] = {k: v["clk"]["value"] for k, v in clk.items()
+                                  if isinstance(v, dict) and isinstance(v.get("clk"), dict)}
+    except (TypeError, KeyError, IndexError):
+        res["amd_smi_error"] = err
+    return res
 
 
 def one_pass_score_ms(pipe: Pipeline, steps: int) -> float:

@@ -116,6 +116,12 @@ def test_heads_above_32k_take_the_part_path_from_the_histogram():
     both(lay, api.Budget(api.BUDGET_K, k=dev(torch.from_numpy(ks))))
     rs = np.array([0.1, 0.6, 0.25, 0.0], dtype=np.float32)
     both(lay, api.Budget(api.BUDGET_RATIO, ratio=dev(torch.from_numpy(rs))))
+    # 19 parts: the last launch places each part after the earlier ones
+    # sixteen parts at a time (two rounds)
+    log("score_select: part path, 300001 tokens")
+    lay = wl.random_case(14, B=1, Hq=4, Hkv=1, d=128, N_max=300001, W=16)
+    for r in (0.1, 0.6):
+        both(lay, RATIO(r))
 
 
 @pytest.mark.parametrize("name", ["needle32k", "llama8b_layer"])

@@ -191,15 +191,20 @@ def test_select_protected(kind, shape):
 
 
 
+@pytest.mark.parametrize("shape", [(2, 2, 70001, [70001, 40000]), (1, 2, 300001, [300001])],
+                         ids=["N70001", "N300001"])
 @pytest.mark.parametrize("kind", KINDS)
-def test_select_long_heads_parts_equal_one_workgroup(kind):
+def test_select_long_heads_parts_equal_one_workgroup(kind, shape):
     # Heads above 32768 tokens under a count budget are split over several
     # workgroups when the workspace is given; without it one workgroup per
     # head selects.  Both must give the same kept indices, bit for bit, and
-    # match the oracle.
+    # match the oracle.  300001 tokens make 19 parts: the last launch places
+    # each part after the earlier ones sixteen parts at a time, so it takes
+    # two rounds there.
     from kv_cache_compression_score_amd import _lib
     import ctypes
-    B, Hkv, N, ctx = 2, 2, 70001, [70001, 40000]
+    B, Hkv, N, ctx = shape
+    log(f"select parts {kind} {shape[:3]}")
     s_np = synth_scores(KINDS.index(kind) * 7919 + 5, B, Hkv, N, ctx, kind)
     s = torch.from_numpy(s_np).cuda()
     c = torch.tensor(ctx, dtype=torch.int32).cuda()

@@ -385,7 +385,7 @@ int kv_vector_decode(const void* q, const void* k_c, const void* v_c, const int3
  * number of distinct kernels (or a negative kv_status).  kv_timing_only(name) restricts the
  * recording to launches of that kernel name (one of "score_rowstats",
  * "score_fold" (launched only when row LSEs are requested or heads are so
- * long, and so few, that pass 1 cuts a head into more than 16 pieces),
+ * long, and so few, that pass 1 cuts a head into more than 32 pieces),
  * "score_colsum", "select", "compact",
  * "compact_decode", "decode_split",
  * "decode_merge", "vector_counts", "vector_pool", "vector_residual",

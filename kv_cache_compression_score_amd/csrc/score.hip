@@ -45,7 +45,8 @@ constexpr int SLOTS_1 = 256 * 2; // pass-1 partition target (resident workgroups
                                  // fixed, so the pass-1 partition, its merge order and the
                                  // result never depend on the device
 constexpr int MIN_SPAN = 4;      // fewest tiles per pass-1 piece span (pass 2: one)
-constexpr int SELF_MERGE = 16;   // pass 2 merges pass 1's partials itself up to this many per head
+constexpr int SELF_MERGE = 32;   // pass 2 merges pass 1's partials itself up to this many per head
+constexpr int MERGE_CHUNK = 16;  // ... loading them this many at a time
 
 template <typename T> struct FragT;
 template <> struct FragT<__bf16> { using vec = bf16x8; };   // 8 elements = 16 B
@@ -532,27 +533,35 @@ __global__ __launch_bounds__(NW * WAVE) void score_pass(ScoreArgs a) {
     }
   } else {
     // Base-2 LSE of each row from pass 1's per-piece (m, sum) partials of
-    // this head (at most SELF_MERGE, consecutive, loads all issued at once),
-    // in piece order: M = max of the m's, then the sum of sum * 2^(m - M).
+    // this head (at most SELF_MERGE, consecutive), in piece order, a chunk
+    // of MERGE_CHUNK at a time (its loads all issued at once): M = the
+    // largest m so far, the running sum rescaled when M rises, then the
+    // chunk's sum * 2^(m - M) added.  A head of at most MERGE_CHUNK pieces
+    // takes one chunk: M = max of the m's, then the sum of sum * 2^(m - M).
     // Staged in `red` (not in use before tile 0).
     float* lse_s = &red[0][0][0];
     for (int r = tid; r < NW * RBW * 32; r += NT) {
       float v = INFINITY;
       if (r < a.R) {
         const float2* src = a.part + (size_t)hp.x * a.R_pad + r;
-        float2 pk[SELF_MERGE];
+        float M = -INFINITY, S = 0.f;
 #pragma unroll
-        for (int u = 0; u < SELF_MERGE; ++u)   // piece u of the row: lanes read consecutive rows
-          pk[u] = u < hp.y ? src[(size_t)u * a.R_pad] : make_float2(-INFINITY, 0.f);
-        float M = -INFINITY;
+        for (int c0 = 0; c0 < SELF_MERGE; c0 += MERGE_CHUNK) {
+          if (c0 >= hp.y) break;   // uniform
+          float2 pk[MERGE_CHUNK];
 #pragma unroll
-        for (int u = 0; u < SELF_MERGE; ++u) M = fmaxf(M, pk[u].x);
-        if (M != -INFINITY) {
-          float S = 0.f;
+          for (int u = 0; u < MERGE_CHUNK; ++u)   // piece c0 + u: lanes read consecutive rows
+            pk[u] = c0 + u < hp.y ? src[(size_t)(c0 + u) * a.R_pad] : make_float2(-INFINITY, 0.f);
+          float Mc = M;
 #pragma unroll
-          for (int u = 0; u < SELF_MERGE; ++u) S = fmaf(pk[u].y, fast_exp2(pk[u].x - M), S);
-          if (S > 0.f) v = M + log2f(S);
+          for (int u = 0; u < MERGE_CHUNK; ++u) Mc = fmaxf(Mc, pk[u].x);
+          if (Mc == -INFINITY) continue;
+          if (Mc != M) S = M == -INFINITY ? 0.f : S * fast_exp2(M - Mc);
+#pragma unroll
+          for (int u = 0; u < MERGE_CHUNK; ++u) S = fmaf(pk[u].y, fast_exp2(pk[u].x - Mc), S);
+          M = Mc;
         }
+        if (M != -INFINITY && S > 0.f) v = M + log2f(S);
       }
       lse_s[r] = v;
     }

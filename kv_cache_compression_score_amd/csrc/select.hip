@@ -34,6 +34,8 @@
 // histogram sum exact and independent of the order of the atomic adds.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -295,8 +297,15 @@ __device__ __forceinline__ void for_keys_all(const Keys<IN_LDS>& key, int n, con
 // the bins.  Thread t owns descending positions 2t and 2t+1 (bins nb-1-2t,
 // nb-2-2t): it reads and clears them; a DPP wave scan and the wave totals
 // locate the bin.  All threads must call it.
-template <bool MASS>
-__device__ __forceinline__ void resolve_digit(Smem& sm, int nb, unsigned long long rem) {
+// RF (optional): rem = rf(total), the digit's total (masses with MASS,
+// else counts) worked out from the wave totals before the search, for a
+// first digit whose target depends on the total of every key.
+struct KeepRem {
+  __device__ unsigned long long operator()(unsigned long long) const { return 0ull; }
+};
+template <bool MASS, class RF = KeepRem>
+__device__ __forceinline__ void resolve_digit(Smem& sm, int nb, unsigned long long rem,
+                                              RF rf = RF()) {
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = wave_index();
   const int p0 = 2 * tid;
   uint32_t c0 = 0, c1 = 0;
@@ -329,6 +338,12 @@ __device__ __forceinline__ void resolve_digit(Smem& sm, int nb, unsigned long lo
   __syncthreads();
   unsigned long long wb = 0;
   uint32_t wbc = 0;
+  if constexpr (!std::is_same<RF, KeepRem>::value) {
+    unsigned long long total = 0;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) total += MASS ? sm.f_m[w] : (unsigned long long)sm.f_c[w];
+    rem = rf(total);
+  }
 #pragma unroll
   for (int w = 0; w < NWV; ++w) {
     if (w < wave) {
@@ -357,17 +372,27 @@ __device__ __forceinline__ void resolve_digit(Smem& sm, int nb, unsigned long lo
 // digit's first barrier, so one set of fields serves every digit.
 // REG: count the wave's first-key bin in registers (HistAcc), for key sets
 // that may crowd into one bin; otherwise every key goes through hist_add.
-template <bool MASS, bool IN_LDS, class FX, bool REG = true>
+// RF: as resolve_digit's, for the first digit (rem is then ignored).
+// EX: after each digit, ex(keys above the prefix found so far, keys that
+// carry it) may end the descent early (returns true; the result is then
+// not the key the full descent gives).
+struct NoExit {
+  __device__ bool operator()(uint32_t, uint32_t) const { return false; }
+};
+template <bool MASS, bool IN_LDS, class FX, bool REG = true, class RF = KeepRem,
+          class EX = NoExit>
 __device__ __forceinline__ uint32_t descend(const Keys<IN_LDS>& key, int n, int cp, uint32_t lo_key,
                             unsigned long long rem, Smem& sm, const FX& fx,
                             uint32_t* cnt_above_out, unsigned long long* rem_out,
-                            bool top_ready = false, uint32_t* eq_out = nullptr) {
+                            bool top_ready = false, uint32_t* eq_out = nullptr, RF first_rf = RF(),
+                            EX ex = EX()) {
   if (top_ready) cp = 0;   // sm.hist already holds the top DIGIT bits of every key
   uint32_t pmask = cp <= 0 ? 0u : (cp >= 32 ? ~0u : ~0u << (32 - cp));
   uint32_t prefix = lo_key & pmask, cnt_above = 0;
   int left = cp >= 32 ? 0 : 32 - cp;
   bool ready = top_ready;
   uint32_t pref_cnt = (uint32_t)n;   // keys matching the current prefix
+  bool first = true;
 #pragma unroll 1
   while (left > 0) {
     const int bits = min(DIGIT, left);
@@ -402,15 +427,27 @@ __device__ __forceinline__ uint32_t descend(const Keys<IN_LDS>& key, int n, int 
                        MASS && in ? fx(kk) : 0ull);
       });
     }
-    ready = false;
     __syncthreads();
-    resolve_digit<MASS>(sm, nb, rem);
+    bool plain = true;
+    if constexpr (!std::is_same<RF, KeepRem>::value) {
+      if (first) {   // the first digit's target from its total
+        resolve_digit<MASS>(sm, nb, rem, [&](unsigned long long total) {
+          rem = first_rf(total);
+          return rem;
+        });
+        plain = false;
+      }
+    }
+    if (plain) resolve_digit<MASS>(sm, nb, rem);
+    first = false;
+    ready = false;
     rem -= MASS ? sm.mass_above : (unsigned long long)sm.cnt_above;
     cnt_above += sm.cnt_above;
     pref_cnt = sm.bin_cnt;
     prefix |= sm.bin << shift;
     pmask |= (uint32_t)(nb - 1) << shift;
     left -= bits;
+    if (left > 0 && ex(cnt_above, pref_cnt)) break;   // uniform
   }
   *cnt_above_out = cnt_above;
   *rem_out = rem;
@@ -833,6 +870,8 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   int lo, hi;
   budget_clamps(bu, n, &lo, &hi);
   int k = 1;
+  bool mass_done = false;   // the mass descent gave the k-th key and the quota
+  uint32_t mass_T = 0, mass_quota = 0, mass_eq = 0;
   if (bu.mode != KV_BUDGET_MASS) {
     k = count_budget(bu, head, n, cnt, lo, hi);
   } else if (tot > 0.0) {
@@ -842,6 +881,48 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       const double v = kk == PROTECTED_KEY ? 0.0 : (double)from_key(kk) * scale;
       return v > 0.0 ? (unsigned long long)v : 0ull;
     };
+    if (n_prot == 0 && cp < 32) {
+      // No protected tokens: the first digit's histogram of the mass descent
+      // sums every key's mass, so the target f * total comes from that sum
+      // (no sweep of its own).  An unclamped count leaves the k-th key and
+      // the tie quota known (the count descent below is skipped).
+      unsigned long long tgt = 0;
+      auto rf = [&](unsigned long long total) -> unsigned long long {
+        unsigned long long t = (unsigned long long)ceil((double)bu.mass * (double)total);
+        if (t > total) t = total;   // double rounding of f * total
+        tgt = t;
+        return t ? t : 1ull;        // no target: the descent's result goes unused
+      };
+      // After each digit the count lies in [above + 1, above + keys in the
+      // chosen bin]; once that range is at or below lo (at or above hi) the
+      // clamp decides k and the descent stops.
+      int clamped = 0;   // -1: k = lo, +1: k = hi
+      auto ex = [&](uint32_t ab, uint32_t in_bin) -> bool {
+        if (tgt == 0) return false;
+        if ((long long)ab + in_bin <= (long long)lo) clamped = -1;
+        else if ((long long)ab + 1 >= (long long)hi) clamped = 1;
+        return clamped != 0;
+      };
+      uint32_t above, eqm;
+      unsigned long long rem;
+      const uint32_t Tm = descend<true>(key, n, cp, mn, 1ull, sm, fx, &above, &rem, false, &eqm,
+                                        rf, ex);
+      if (clamped != 0) {
+        k = clamped < 0 ? lo : hi;
+      } else if (tgt > 0) {
+        const unsigned long long fv = fx(Tm);   // > 0: its bin holds mass
+        const unsigned long long j = fv ? (rem + fv - 1) / fv : 1ull;
+        k = (int)(above + (uint32_t)j);
+        if (k >= lo && k <= hi) {
+          mass_T = Tm;
+          mass_quota = (uint32_t)j;
+          mass_eq = eqm;
+          mass_done = true;
+        }
+      }
+      k = min(max(k, lo), hi);
+      goto budget_done;
+    }
     unsigned long long tp = 0, pm = 0;
     for_keys(key, n, [&](uint32_t kk) { tp += fx(kk); });
     if (n_prot > 0) {   // real mass of the protected tokens
@@ -874,11 +955,16 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   } else {
     k = lo;
   }
+budget_done:
   k = min(max(k, n_prot), n);
 
   // The k-th key and the tie quota.
   uint32_t T, quota, eq_total = 0;
-  {
+  if (mass_done) {
+    T = mass_T;
+    quota = mass_quota;
+    eq_total = mass_eq;
+  } else {
     uint32_t above;
     unsigned long long rem;
     auto nofx = [](uint32_t) { return 0ull; };

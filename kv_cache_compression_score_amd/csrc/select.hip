@@ -498,14 +498,13 @@ __device__ __forceinline__ uint32_t ties_kept(uint32_t quota, uint32_t before, u
 
 // One digit's histogram over a wave's register-held keys, each lane holding
 // a run of R = 4 * JR consecutive tokens (key 4 j + u of the lane is token
-// tl + 4 j + u, valid below s1; `full`: every key of the wave is valid):
-// keys whose bits from `hi` up equal `prefix` add one to bin (key >> lo) of
-// the bits below `hi`.  A step in which no lane has a matching key costs two
-// VALU instructions per key and a branch (the lower digits match a few keys
-// of a head); a wave whose sampled keys crowd into one bin aggregates its
-// adds instead.
+// tl + 4 j + u, valid below s1; `full`: every key of the wave is valid; the
+// same keys sit in the wave's LDS stretch): keys whose bits from `hi` up
+// equal `prefix` add one to bin (key >> lo) of the bits below `hi`.  A wave
+// whose sampled keys crowd into one bin aggregates its adds.
 __device__ __forceinline__ void count_runs(const uint4 (&ek)[EPI], int tl, int s1, int JR, bool full,
-                                           int hi, int lo, uint32_t prefix, Smem& sm) {
+                                           int hi, int lo, uint32_t prefix, Smem& sm,
+                                           const uint32_t* stretch) {
   const uint32_t bmask = (1u << (hi - lo)) - 1u;
   const bool in0 = tl < s1 && (ek[0].x >> hi) == prefix;
   if (crowded(in0, (int)((ek[0].x >> lo) & bmask))) {
@@ -522,27 +521,27 @@ __device__ __forceinline__ void count_runs(const uint4 (&ek)[EPI], int tl, int s
     acc.flush(sm);
     return;
   }
-  // one step of 4 keys per lane; a full wave's steps take their own copy,
-  // whose masks are plain compares
-  auto step = [&](const uint32_t (&kk)[4], bool m0, bool m1, bool m2, bool m3) {
-    if ((__ballot(m0) | __ballot(m1) | __ballot(m2) | __ballot(m3)) == 0) return;   // uniform
-    if (m0) atomicAdd(&sm.hist[(kk[0] >> lo) & bmask], 1u);
-    if (m1) atomicAdd(&sm.hist[(kk[1] >> lo) & bmask], 1u);
-    if (m2) atomicAdd(&sm.hist[(kk[2] >> lo) & bmask], 1u);
-    if (m3) atomicAdd(&sm.hist[(kk[3] >> lo) & bmask], 1u);
-  };
+  // Otherwise each lane marks its keys that carry the prefix in a bit mask
+  // and adds them one by one (a few per lane: the lower digits match a few
+  // keys of a head), reading each key back from the wave's stretch of LDS
+  // (16-byte chunk c at slot c ^ ((c >> 3) & 7)): one LDS atomic per
+  // matching key of the busiest lane instead of one per four keys.
+  uint32_t mm = 0u;
 #pragma unroll
   for (int j = 0; j < EPI; ++j) {
     if (j >= JR) break;   // uniform
     const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
-    if (full) {
-      step(kk, (kk[0] >> hi) == prefix, (kk[1] >> hi) == prefix, (kk[2] >> hi) == prefix,
-           (kk[3] >> hi) == prefix);
-    } else {
-      const int left = s1 - tl - 4 * j;   // this lane's keys left in the segment
-      step(kk, left > 0 && (kk[0] >> hi) == prefix, left > 1 && (kk[1] >> hi) == prefix,
-           left > 2 && (kk[2] >> hi) == prefix, left > 3 && (kk[3] >> hi) == prefix);
-    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      mm |= ((full || tl + 4 * j + u < s1) && (kk[u] >> hi) == prefix ? 1u : 0u) << (4 * j + u);
+  }
+  const int lane = threadIdx.x & (WAVE - 1);
+  while (mm) {
+    const int bit = __builtin_ctz(mm);
+    mm &= mm - 1u;
+    const int c = lane * JR + (bit >> 2);
+    const uint32_t key = stretch[4 * (c ^ ((c >> 3) & 7)) + (bit & 3)];
+    atomicAdd(&sm.hist[(key >> lo) & bmask], 1u);
   }
 }
 
@@ -1171,12 +1170,12 @@ __global__ __launch_bounds__(NT) void select_hist_kernel(SelectArgs a, const uin
   // when its bits above the digit equal the prefix found so far.
   unsigned long long rem = (unsigned long long)(k - sm.cnt_above);
   uint32_t prefix = sm.bin;   // the top DIGIT bits of the k-th largest key
-  count_runs(ek, tl, s1, JR, full, 32 - DIGIT, 32 - 2 * DIGIT, prefix, sm);
+  count_runs(ek, tl, s1, JR, full, 32 - DIGIT, 32 - 2 * DIGIT, prefix, sm, keys_lds + s0);
   __syncthreads();
   resolve_digit<false>(sm, NBINS, rem);
   rem -= sm.cnt_above;
   prefix = prefix << DIGIT | sm.bin;   // the top 2 * DIGIT bits
-  count_runs(ek, tl, s1, JR, full, 32 - 2 * DIGIT, 0, prefix, sm);
+  count_runs(ek, tl, s1, JR, full, 32 - 2 * DIGIT, 0, prefix, sm, keys_lds + s0);
   __syncthreads();
   resolve_digit<false>(sm, 1 << (32 - 2 * DIGIT), rem);
   rem -= sm.cnt_above;

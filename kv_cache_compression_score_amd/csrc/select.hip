@@ -496,6 +496,37 @@ __device__ __forceinline__ uint32_t ties_kept(uint32_t quota, uint32_t before, u
   return (uint32_t)(avail <= 0 ? 0 : (avail < (int64_t)e ? avail : (int64_t)e));
 }
 
+// Bit b of the result: key b of the lane's run (token tl + b) is valid
+// (below s1, or the whole wave is: `full`) and satisfies pred.  The keys are
+// taken last to first, each doubling the mask and adding its predicate, an
+// add with the compare's carry; full waves skip the bounds.
+template <class P>
+__device__ __forceinline__ uint32_t run_mask(const uint4 (&ek)[EPI], int tl, int s1, int JR,
+                                             bool full, const P& pred) {
+  uint32_t mm = 0u;
+  if (full) {
+#pragma unroll
+    for (int j = EPI - 1; j >= 0; --j) {
+      if (j >= JR) continue;   // uniform
+      mm = mm + mm + (pred(ek[j].w) ? 1u : 0u);
+      mm = mm + mm + (pred(ek[j].z) ? 1u : 0u);
+      mm = mm + mm + (pred(ek[j].y) ? 1u : 0u);
+      mm = mm + mm + (pred(ek[j].x) ? 1u : 0u);
+    }
+  } else {
+    const int left = s1 - tl;   // this lane's keys in the segment
+#pragma unroll
+    for (int j = EPI - 1; j >= 0; --j) {
+      if (j >= JR) continue;   // uniform
+      mm = mm + mm + (4 * j + 3 < left && pred(ek[j].w) ? 1u : 0u);
+      mm = mm + mm + (4 * j + 2 < left && pred(ek[j].z) ? 1u : 0u);
+      mm = mm + mm + (4 * j + 1 < left && pred(ek[j].y) ? 1u : 0u);
+      mm = mm + mm + (4 * j < left && pred(ek[j].x) ? 1u : 0u);
+    }
+  }
+  return mm;
+}
+
 // One digit's histogram over a wave's register-held keys, each lane holding
 // a run of R = 4 * JR consecutive tokens (key 4 j + u of the lane is token
 // tl + 4 j + u, valid below s1; `full`: every key of the wave is valid; the
@@ -526,15 +557,7 @@ __device__ __forceinline__ void count_runs(const uint4 (&ek)[EPI], int tl, int s
   // keys of a head), reading each key back from the wave's stretch of LDS
   // (16-byte chunk c at slot c ^ ((c >> 3) & 7)): one LDS atomic per
   // matching key of the busiest lane instead of one per four keys.
-  uint32_t mm = 0u;
-#pragma unroll
-  for (int j = 0; j < EPI; ++j) {
-    if (j >= JR) break;   // uniform
-    const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      mm |= ((full || tl + 4 * j + u < s1) && (kk[u] >> hi) == prefix ? 1u : 0u) << (4 * j + u);
-  }
+  uint32_t mm = run_mask(ek, tl, s1, JR, full, [&](uint32_t kk) { return (kk >> hi) == prefix; });
   const int lane = threadIdx.x & (WAVE - 1);
   while (mm) {
     const int bit = __builtin_ctz(mm);
@@ -560,22 +583,12 @@ __device__ __forceinline__ void emit_runs(const uint4 (&ek)[EPI], int s0, int tl
                                           int32_t* dst) {
   const int lane = threadIdx.x & (WAVE - 1), wave = wave_index();
   const bool all_ties = quota >= eq_total;   // then the keep rule is key >= T
-  uint32_t keep = 0u, eqm = 0u;
-#pragma unroll
-  for (int j = 0; j < EPI; ++j) {
-    if (j >= JR) break;   // uniform
-    const uint32_t kk[4] = {ek[j].x, ek[j].y, ek[j].z, ek[j].w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int b = 4 * j + u;
-      const bool ok = full || tl + b < s1;
-      if (all_ties) {
-        keep |= (ok && kk[u] >= T ? 1u : 0u) << b;
-      } else {
-        keep |= (ok && kk[u] > T ? 1u : 0u) << b;
-        eqm |= (ok && kk[u] == T ? 1u : 0u) << b;
-      }
-    }
+  uint32_t keep, eqm = 0u;
+  if (all_ties) {
+    keep = run_mask(ek, tl, s1, JR, full, [&](uint32_t kk) { return kk >= T; });
+  } else {
+    keep = run_mask(ek, tl, s1, JR, full, [&](uint32_t kk) { return kk > T; });
+    eqm = run_mask(ek, tl, s1, JR, full, [&](uint32_t kk) { return kk == T; });
   }
   if (!all_ties) {
     const uint32_t ne = (uint32_t)__popc(eqm);

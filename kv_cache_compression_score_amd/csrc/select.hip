@@ -303,9 +303,10 @@ __device__ __forceinline__ void for_keys_all(const Keys<IN_LDS>& key, int n, con
 struct KeepRem {
   __device__ unsigned long long operator()(unsigned long long) const { return 0ull; }
 };
+// save (optional): each count also goes to save[bin] as it is read.
 template <bool MASS, class RF = KeepRem>
 __device__ __forceinline__ void resolve_digit(Smem& sm, int nb, unsigned long long rem,
-                                              RF rf = RF()) {
+                                              RF rf = RF(), uint16_t* save = nullptr) {
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = wave_index();
   const int p0 = 2 * tid;
   uint32_t c0 = 0, c1 = 0;
@@ -314,6 +315,7 @@ __device__ __forceinline__ void resolve_digit(Smem& sm, int nb, unsigned long lo
     const int b0 = nb - 1 - p0, b1 = b0 - 1;
     c0 = sm.hist[b0]; c1 = sm.hist[b1];
     sm.hist[b0] = 0; sm.hist[b1] = 0;
+    if (save) { save[b0] = (uint16_t)c0; save[b1] = (uint16_t)c1; }
     if (MASS) {
       m0 = sm.hmass[b0]; m1 = sm.hmass[b1];
       sm.hmass[b0] = 0; sm.hmass[b1] = 0;
@@ -385,12 +387,16 @@ __device__ __forceinline__ uint32_t descend(const Keys<IN_LDS>& key, int n, int 
                             unsigned long long rem, Smem& sm, const FX& fx,
                             uint32_t* cnt_above_out, unsigned long long* rem_out,
                             bool top_ready = false, uint32_t* eq_out = nullptr, RF first_rf = RF(),
-                            EX ex = EX()) {
-  if (top_ready) cp = 0;   // sm.hist already holds the top DIGIT bits of every key
+                            EX ex = EX(), uint16_t* save_first = nullptr,
+                            bool first_ready = false) {
+  // top_ready: sm.hist already holds the top DIGIT bits of every key;
+  // first_ready: it holds the first digit below the shared prefix (as
+  // save_first keeps it, counts below 2^16) of every key
+  if (top_ready) cp = 0;
   uint32_t pmask = cp <= 0 ? 0u : (cp >= 32 ? ~0u : ~0u << (32 - cp));
   uint32_t prefix = lo_key & pmask, cnt_above = 0;
   int left = cp >= 32 ? 0 : 32 - cp;
-  bool ready = top_ready;
+  bool ready = top_ready || first_ready;
   uint32_t pref_cnt = (uint32_t)n;   // keys matching the current prefix
   bool first = true;
 #pragma unroll 1
@@ -434,11 +440,11 @@ __device__ __forceinline__ uint32_t descend(const Keys<IN_LDS>& key, int n, int 
         resolve_digit<MASS>(sm, nb, rem, [&](unsigned long long total) {
           rem = first_rf(total);
           return rem;
-        });
+        }, save_first);
         plain = false;
       }
     }
-    if (plain) resolve_digit<MASS>(sm, nb, rem);
+    if (plain) resolve_digit<MASS>(sm, nb, rem, KeepRem(), first ? save_first : nullptr);
     first = false;
     ready = false;
     rem -= MASS ? sm.mass_above : (unsigned long long)sm.cnt_above;
@@ -732,6 +738,9 @@ template <bool IN_LDS>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t keys_lds[IN_LDS ? LDS_KEYS : 4];
   __shared__ Smem sm;
+  // the mass descent's first-digit counts, for the count descent that may
+  // follow (counts of at most 65535 keys)
+  __shared__ uint16_t save16[NBINS];
   const int head = blockIdx.x, b = head / a.Hkv;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = wave_index();
   const int n = a.n_head ? min(max(a.n_head[head], 0), a.N_max)
@@ -882,6 +891,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   int lo, hi;
   budget_clamps(bu, n, &lo, &hi);
   int k = 1;
+  bool saved_first = false;   // save16 holds the first digit's counts of every key
   bool mass_done = false;   // the mass descent gave the k-th key and the quota
   uint32_t mass_T = 0, mass_quota = 0, mass_eq = 0;
   if (bu.mode != KV_BUDGET_MASS) {
@@ -917,8 +927,9 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       };
       uint32_t above, eqm;
       unsigned long long rem;
+      saved_first = n < 65536;
       const uint32_t Tm = descend<true>(key, n, cp, mn, 1ull, sm, fx, &above, &rem, false, &eqm,
-                                        rf, ex);
+                                        rf, ex, saved_first ? save16 : nullptr);
       if (clamped != 0) {
         k = clamped < 0 ? lo : hi;
       } else if (tgt > 0) {
@@ -980,8 +991,13 @@ budget_done:
     uint32_t above;
     unsigned long long rem;
     auto nofx = [](uint32_t) { return 0ull; };
+    if (saved_first) {   // the first digit is the mass descent's: its counts come back
+      const int nb1 = 1 << min(DIGIT, 32 - cp);
+      for (int i = tid; i < nb1; i += NT) sm.hist[i] = save16[i];
+      __syncthreads();
+    }
     T = descend<false>(key, n, cp, mn, (unsigned long long)k, sm, nofx, &above, &rem, !mass,
-                       &eq_total);
+                       &eq_total, KeepRem(), NoExit(), nullptr, saved_first);
     quota = (uint32_t)rem;
   }
 

@@ -195,13 +195,16 @@ __device__ __forceinline__ void hist_add(Smem& sm, bool active, int bin, unsigne
 // (see crowded below): the bin of the wave's first key (hb, wave-uniform) is
 // counted in registers, lane by lane, and added once at the end (flush);
 // other bins go through hist_add.  With one bin holding most keys this
-// leaves that bin no LDS atomic and no wave reduction per step.  Every lane
-// calls add at every step and flush once.
+// leaves that bin no LDS atomic and no wave reduction per step.  With MASS a
+// second bin (hb2) is kept in registers too, the first that AGG_MIN lanes of
+// a step share outside hb: a head whose keys split between two bins would
+// otherwise pay a 64-bit wave reduction per step.  Every lane calls add at
+// every step and flush once.
 template <bool MASS>
 struct HistAcc {
-  int hb = -1;
-  uint32_t c = 0;
-  unsigned long long m = 0;
+  int hb = -1, hb2 = -1;
+  uint32_t c = 0, c2 = 0;
+  unsigned long long m = 0, m2 = 0;
   __device__ __forceinline__ void add(Smem& sm, bool active, int bin, unsigned long long mass) {
     if (hb < 0) {
       const uint64_t act = __ballot(active);
@@ -213,15 +216,39 @@ struct HistAcc {
       ++c;
       if (MASS) m += mass;
     }
-    hist_add<MASS>(sm, active && !hot, bin, mass);
+    bool rest = active && !hot;
+    if (MASS) {
+      if (hb2 < 0) {
+        const uint64_t r = __ballot(rest);
+        if (r != 0) {
+          const int b = __builtin_amdgcn_readlane(bin, __builtin_ctzll(r));
+          if (__popcll(__ballot(rest && bin == b)) >= AGG_MIN) hb2 = b;
+        }
+      }
+      const bool hot2 = rest && bin == hb2;
+      if (hot2) {
+        ++c2;
+        m2 += mass;
+      }
+      rest = rest && !hot2;
+    }
+    hist_add<MASS>(sm, rest, bin, mass);
   }
   __device__ __forceinline__ void flush(Smem& sm) {
     if (hb < 0) return;
     const uint32_t cs = last_lane(wave_scan_u32(c, 0u, OpAdd()));
     const unsigned long long ms = MASS ? last_lane(wave_scan_add_u64(m)) : 0ull;
+    uint32_t cs2 = 0;
+    unsigned long long ms2 = 0;
+    if (MASS && hb2 >= 0) {
+      cs2 = last_lane(wave_scan_u32(c2, 0u, OpAdd()));
+      ms2 = last_lane(wave_scan_add_u64(m2));
+    }
     if ((threadIdx.x & (WAVE - 1)) == 0) {
       if (cs) atomicAdd(&sm.hist[hb], cs);
       if (MASS && ms) atomicAdd(&sm.hmass[hb], ms);
+      if (MASS && cs2) atomicAdd(&sm.hist[hb2], cs2);
+      if (MASS && ms2) atomicAdd(&sm.hmass[hb2], ms2);
     }
   }
 };

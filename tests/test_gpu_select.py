@@ -22,6 +22,11 @@ def synth_scores(seed, B, Hkv, N, ctx, kind):
         s = np.where(rng.random((B, Hkv, N)) < 0.9, 0.0, rng.random((B, Hkv, N)))
         s = s.astype(np.float32)
         s[(s == 0) & (rng.random((B, Hkv, N)) < 0.5)] = np.float32(-0.0)
+    elif kind == "twobins":   # 60% and 35% of the keys in two top-digit bins, 5% spread
+        u = rng.random((B, Hkv, N))
+        j = 1 + rng.random((B, Hkv, N)) * 2.0 ** -8      # leaves the top digit alone
+        s = np.where(u < 0.6, 0.5 * j, np.where(u < 0.95, 0.25 * j, rng.random((B, Hkv, N))))
+        s = s.astype(np.float32)
     elif kind == "heavy":     # softmax-like heavy tail over many decades
         s = np.exp(rng.standard_normal((B, Hkv, N)) * 6).astype(np.float32)
     else:                     # plain uniform
@@ -100,7 +105,9 @@ def test_select_threshold(kind, shape):
         compare_sets(idx_g, cnt_g, idx_r, cnt_r)
 
 
-@pytest.mark.parametrize("kind", ["ties", "heavy", "uniform"])
+# twobins: the mass descent's crowded-key sums hold a second bin in registers,
+# and its first digit's counts serve the count descent of a clamped head
+@pytest.mark.parametrize("kind", ["ties", "heavy", "uniform", "twobins"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"B{s[0]}H{s[1]}N{s[2]}")
 def test_select_mass(kind, shape):
     B, Hkv, N, ctx = shape
